@@ -1,0 +1,144 @@
+/*
+ * llmint8 -- the LLM.int8() matrix multiply on AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("LLM.int8(): 8-bit Matrix Multiplication for Transformers at Scale",
+ * abstract): a two-part procedure for the feed-forward and attention projection
+ * products Y = X W.
+ *   1. Vector-wise quantization: one normalization constant per inner-product vector,
+ *      i.e. per row of X (token) and per output column of W.  The constant is the
+ *      vector's absolute maximum s (kept in fp32); a value x is coded as
+ *      q = clamp(round_half_even(x * RN32(127/s)), -127, 127)  (s = 0 gives q = 0).
+ *   2. Mixed-precision decomposition: the feature dimensions of X that hold outliers
+ *      -- every column j with |X[i,j]| > threshold for some row i of this call
+ *      (talk summary "llama3-model-quantization", "Understanding Outliers in
+ *      Transformer Models": outliers sit in specific columns of the input batch) --
+ *      go through a 16-bit matrix multiplication; everything else goes through int8
+ *      with exact int32 accumulation.
+ *   With O the ascending outlier set, Xq the int8 codes of X with the columns in O
+ *   zeroed (row scales s_x taken over the other columns), Wq the int8 codes of W
+ *   (column scales s_w), C = Xq Wq^T (int32) and F = X[:,O] Wq[:,O]^T (16-bit inputs,
+ *   fp32 accumulation; Wq's codes are exact in fp16/bf16), each element of Y is
+ *       y = RN32( RN32( RN32((float)C * r_i) * c_n ) + RN32(c_n * F) ),
+ *       r_i = RN32(s_x[i] / 127),  c_n = RN32(s_w[n] / 127),  Y = round_even_to_T(y),
+ *   i.e. the int32 product dequantized by the outer product of the two scale vectors
+ *   divided by 127^2, plus the outlier product.  (Rounding to nearest: "nuQmm" report
+ *   page, GPTQ statement under "Large-model Quantization".)
+ *
+ * Conventions for every call below.
+ *   - Pointers are DEVICE pointers owned by the caller unless marked HOST.  The library
+ *     allocates no memory and keeps no state between calls; it is re-entrant.
+ *   - `stream` is a hipStream_t (NULL: the default stream).  Calls only enqueue work on
+ *     it and return before it runs, except int8_matmul_stats, which synchronizes it.
+ *   - `dtype` is LLMINT8_F16 or LLMINT8_BF16; X, W and Y share it.
+ *   - Returns LLMINT8_OK (0) or a negative status.  Every argument is validated before
+ *     any GPU work is enqueued; on a validation error nothing is written.  A HIP error
+ *     is returned as LLMINT8_EHIP (the sticky error is consumed); work enqueued before
+ *     it may have run.  No C++ exception crosses this interface.
+ *   - Shapes: M >= 0 rows of X (tokens), K >= 0 features, N >= 0 output columns;
+ *     K must be a multiple of 16 and N a multiple of 8; K <= 133143 so that every
+ *     int32 dot product is exact (127 * 127 * K < 2^31), else LLMINT8_ERANGE.
+ *     Any M (ragged tails included); M, N, K < 2^31.
+ *   - Layouts are row-major.  X: M x K.  W: K x N.  Wq: N x K (K contiguous).  Y: M x N.
+ *     X, W, Wq, Y and the workspace must be 16-byte aligned; w_scale 4-byte aligned.
+ *   - Non-finite inputs, and nonzero vectors whose absmax is below 2^-120 (where
+ *     127/s overflows fp32; bf16 only), are outside the contract.
+ */
+#ifndef LLMINT8_H
+#define LLMINT8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum llmint8_dtype { LLMINT8_F16 = 0, LLMINT8_BF16 = 1 };
+
+enum llmint8_status {
+    LLMINT8_OK = 0,
+    LLMINT8_EINVAL = -1,     /* bad pointer, shape, alignment, dtype, threshold or aliasing */
+    LLMINT8_EWORKSPACE = -2, /* workspace missing, misaligned or smaller than required     */
+    LLMINT8_EHIP = -3,       /* a HIP launch or runtime call failed                        */
+    LLMINT8_ERANGE = -4      /* K too large for exact int32 accumulation                   */
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* llmint8_status_string(int status);
+
+/*
+ * Offline weight conversion ("LLM.int8()" page, abstract: a 16-bit checkpoint is
+ * loaded, converted to Int8 and used immediately; data-free, one pass -- "nuQmm"
+ * report page, GPTQ statement under "The Gptq Algorithm", on round-to-nearest).
+ *   W        in : K x N, dtype, row-major.
+ *   Wq       out: N x K int8, row-major (each output column's codes contiguous).
+ *   w_scale  out: fp32[N], s_w[n] = max_k |W[k,n]|.
+ * K = 0 gives w_scale = 0; N = 0 is a no-op.
+ */
+int int8_quantize_weight(const void* W, int64_t K, int64_t N, int dtype,
+                         int8_t* Wq, float* w_scale, void* stream);
+
+/* Bytes of device workspace int8_matmul needs for these sizes (worst case: every
+ * column an outlier).  int8_matmul_stats needs int8_matmul_workspace_bytes(M, K, 0). */
+size_t int8_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N);
+
+/*
+ * The LLM.int8() product Y = X W (see the top of this file for the exact definition).
+ *   X          in : M x K, dtype.
+ *   Wq, w_scale in: from int8_quantize_weight (N x K int8, fp32[N]).
+ *   threshold  in : outlier threshold tau >= 0 (+INFINITY allowed: no outliers;
+ *                   0: every nonzero column is an outlier, the 16-bit product).
+ *                   NaN or negative: LLMINT8_EINVAL.
+ *   Y          out: M x N, dtype.  Must not overlap X, Wq, w_scale or the workspace.
+ *   workspace  scratch of at least int8_matmul_workspace_bytes(M, K, N) bytes,
+ *              16-byte aligned.  After the call it holds the X pass's products in the
+ *              layout int8_matmul_workspace_layout describes (Xq, s_x, O, n_O, X[:,O]).
+ */
+int int8_matmul(const void* X, int64_t M, int64_t K, int dtype,
+                const int8_t* Wq, const float* w_scale, int64_t N,
+                float threshold, void* Y,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The outlier feature dimensions of X for this threshold ("LLM.int8()" page,
+ * abstract: more than 99.9% of values are multiplied in 8-bit; this reports the rest).
+ *   n_outlier_cols  HOST out: n_O = |O|.
+ *   outlier_cols    DEVICE out, may be NULL, capacity K int32: O in ascending order.
+ * Synchronizes `stream`.  Workspace: int8_matmul_workspace_bytes(M, K, 0) bytes.
+ */
+int int8_matmul_stats(const void* X, int64_t M, int64_t K, int dtype, float threshold,
+                      int32_t* n_outlier_cols, int32_t* outlier_cols,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Where int8_matmul leaves the X pass's products in its workspace (byte offsets from
+ * the workspace start; pitches in elements).  All regions are 256-byte aligned.
+ *   xq        int8  [M][xq_pitch]   Xq; columns in O are 0; columns >= K are 0
+ *   s_x       fp32  [M]             row absmax over the non-outlier columns
+ *   n_outliers int32                n_O
+ *   outliers  int32 [K]             O ascending (first n_O entries valid)
+ *   xo        dtype [M][xo_pitch]   X[:, O] (first n_O columns; zero up to the next
+ *                                   multiple of 32)
+ *   wo        dtype [N][xo_pitch]   Wq[:, O] cast to dtype (same padding)
+ *   scratch   internal (outlier flags)                                              */
+typedef struct {
+    size_t xq, xq_pitch, s_x, n_outliers, outliers, xo, xo_pitch, wo, scratch, total;
+} llmint8_workspace_layout;
+
+int int8_matmul_workspace_layout(int64_t M, int64_t K, int64_t N, llmint8_workspace_layout* out);
+
+/*
+ * Test hook, not part of the product path: the same kernels as int8_matmul with the
+ * epilogue replaced by a store of the raw accumulators, so that the int32 product can
+ * be compared exactly.
+ *   C  out: M x N int32, C = Xq Wq^T.
+ *   F  out: M x N fp32, the 16-bit outlier product (0 where there are no outliers).
+ */
+int int8_matmul_accumulators(const void* X, int64_t M, int64_t K, int dtype,
+                             const int8_t* Wq, int64_t N, float threshold,
+                             int32_t* C, float* F,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LLMINT8_H */

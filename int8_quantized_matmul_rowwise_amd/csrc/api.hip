@@ -1,0 +1,255 @@
+// C-ABI entry points of llmint8 (declared and documented in include/llmint8.h).
+// Validation happens before anything is enqueued; HIP failures map to LLMINT8_EHIP.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/llmint8.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+#define LLMINT8_API extern "C" __attribute__((visibility("default")))
+
+using namespace llmint8;
+
+namespace {
+
+constexpr int64_t kMaxK = 133143;  // 127 * 127 * K < 2^31
+constexpr int64_t kMaxDim = 0x7fffffff;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+// Shape rules shared by every call (see the header).
+int check_shape(int64_t M, int64_t K, int64_t N, int dtype) {
+    if (dtype != LLMINT8_F16 && dtype != LLMINT8_BF16) return LLMINT8_EINVAL;
+    if (M < 0 || K < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return LLMINT8_EINVAL;
+    if (K % 16 != 0 || N % 8 != 0) return LLMINT8_EINVAL;
+    if (K > kMaxK) return LLMINT8_ERANGE;
+    if (ceil_div(M, 256) * ceil_div(N, 256) > kMaxDim) return LLMINT8_ERANGE;
+    return LLMINT8_OK;
+}
+
+int check_threshold(float t) { return (isnan(t) || t < 0.0f) ? LLMINT8_EINVAL : LLMINT8_OK; }
+
+struct Layout {
+    size_t xq, xq_pitch, s_x, n_outliers, outliers, xo, xo_pitch, wo, bitmap, partial, total;
+};
+
+Layout make_layout(int64_t M, int64_t K, int64_t N) {
+    Layout L;
+    const size_t m = (size_t)M, k = (size_t)K, n = (size_t)N;
+    L.xq_pitch = (size_t)round_up(K, 256);
+    L.xo_pitch = (size_t)round_up(K, 32);
+    const size_t kw = (size_t)ceil_div(K, 32);
+    size_t off = 0;
+    L.xq = off;
+    off = align_up(off + m * L.xq_pitch);
+    L.s_x = off;
+    off = align_up(off + 4 * m);
+    L.n_outliers = off;
+    off = align_up(off + 4);
+    L.outliers = off;
+    off = align_up(off + 4 * k);
+    L.xo = off;
+    off = align_up(off + 2 * m * L.xo_pitch);
+    L.wo = off;
+    off = align_up(off + 2 * n * L.xo_pitch);
+    L.bitmap = off;
+    off = align_up(off + 4 * kw);
+    L.partial = off;
+    off = align_up(off + 4 * kw * (size_t)detect_row_blocks(M));
+    L.total = off;
+    return L;
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return LLMINT8_OK;
+    (void)hipGetLastError();
+    return LLMINT8_EHIP;
+}
+
+// Enqueue the X pass (detect, compact, code rows [+ gather W_O]) into the workspace.
+int run_xpass(const void* X, int64_t M, int64_t K, int dtype, float tau, const int8_t* Wq, int64_t N,
+              int8_t* ws, const Layout& L, hipStream_t st) {
+    uint32_t* partial = (uint32_t*)(ws + L.partial);
+    uint32_t* bitmap = (uint32_t*)(ws + L.bitmap);
+    int32_t* O = (int32_t*)(ws + L.outliers);
+    int32_t* nO = (int32_t*)(ws + L.n_outliers);
+    hipError_t e = launch_detect(dtype, X, M, K, tau, partial, st);
+    if (e == hipSuccess) e = launch_compact(M, K, partial, bitmap, O, nO, st);
+    if (e == hipSuccess) {
+        XPassArgs a;
+        a.dt = dtype;
+        a.X = X;
+        a.M = M;
+        a.K = K;
+        a.N = N;
+        a.bitmap = bitmap;
+        a.O = O;
+        a.n_out = nO;
+        a.Xq = ws + L.xq;
+        a.xq_pitch = (int64_t)L.xq_pitch;
+        a.s_x = (float*)(ws + L.s_x);
+        a.XO = ws + L.xo;
+        a.xo_pitch = (int64_t)L.xo_pitch;
+        a.Wq = Wq;
+        a.WO = ws + L.wo;
+        e = launch_quantize_rows(a, st);
+    }
+    return hip_status(e);
+}
+
+int matmul_common(const void* X, int64_t M, int64_t K, int dtype, const int8_t* Wq, const float* w_scale,
+                  int64_t N, float threshold, void* Y, int32_t* C, float* F, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    int rc = check_shape(M, K, N, dtype);
+    if (rc) return rc;
+    if ((rc = check_threshold(threshold))) return rc;
+    const bool acc = Y == nullptr;
+    if (M > 0 && K > 0 && (!X || !aligned(X, 16))) return LLMINT8_EINVAL;
+    if (N > 0 && K > 0 && (!Wq || !aligned(Wq, 16))) return LLMINT8_EINVAL;
+    if (M > 0 && N > 0) {
+        if (acc) {
+            if (!C || !F || !aligned(C, 16) || !aligned(F, 16)) return LLMINT8_EINVAL;
+        } else {
+            if (!Y || !aligned(Y, 16)) return LLMINT8_EINVAL;
+            if (!w_scale || !aligned(w_scale, 4)) return LLMINT8_EINVAL;
+        }
+    }
+    const Layout L = make_layout(M, K, N);
+    if (M > 0 && (!workspace || !aligned(workspace, 16))) return LLMINT8_EWORKSPACE;
+    if (M > 0 && workspace_bytes < L.total) return LLMINT8_EWORKSPACE;
+    if (!acc) {
+        const size_t ybytes = (size_t)M * (size_t)N * 2;
+        if (overlap(Y, ybytes, X, (size_t)M * (size_t)K * 2) || overlap(Y, ybytes, Wq, (size_t)N * (size_t)K) ||
+            overlap(Y, ybytes, w_scale, (size_t)N * 4) || overlap(Y, ybytes, workspace, L.total))
+            return LLMINT8_EINVAL;
+    }
+    if (M == 0) return LLMINT8_OK;
+    hipStream_t st = (hipStream_t)stream;
+    int8_t* ws = (int8_t*)workspace;
+    rc = run_xpass(X, M, K, dtype, threshold, N > 0 ? Wq : nullptr, N, ws, L, st);
+    if (rc) return rc;
+    GemmArgs g;
+    g.dt = dtype;
+    g.Xq = ws + L.xq;
+    g.xq_pitch = (int64_t)L.xq_pitch;
+    g.Wq = Wq;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.s_x = (const float*)(ws + L.s_x);
+    g.s_w = w_scale;
+    g.XO = ws + L.xo;
+    g.WO = ws + L.wo;
+    g.xo_pitch = (int64_t)L.xo_pitch;
+    g.n_out = (const int32_t*)(ws + L.n_outliers);
+    g.Y = Y;
+    g.C_acc = C;
+    g.F_acc = F;
+    return hip_status(launch_gemm(g, st));
+}
+
+}  // namespace
+
+LLMINT8_API const char* llmint8_status_string(int status) {
+    switch (status) {
+        case LLMINT8_OK: return "LLMINT8_OK";
+        case LLMINT8_EINVAL: return "LLMINT8_EINVAL: invalid argument";
+        case LLMINT8_EWORKSPACE: return "LLMINT8_EWORKSPACE: workspace missing, misaligned or too small";
+        case LLMINT8_EHIP: return "LLMINT8_EHIP: HIP runtime or launch failure";
+        case LLMINT8_ERANGE: return "LLMINT8_ERANGE: size outside the exact-int32 range";
+        default: return "LLMINT8: unknown status";
+    }
+}
+
+LLMINT8_API int int8_quantize_weight(const void* W, int64_t K, int64_t N, int dtype, int8_t* Wq, float* w_scale,
+                                     void* stream) {
+    int rc = check_shape(0, K, N, dtype);
+    if (rc) return rc;
+    if (N == 0) return LLMINT8_OK;
+    if (!w_scale || !aligned(w_scale, 4)) return LLMINT8_EINVAL;
+    if (K > 0 && (!W || !Wq || !aligned(W, 16) || !aligned(Wq, 16))) return LLMINT8_EINVAL;
+    if (overlap(W, (size_t)K * N * 2, Wq, (size_t)K * N) || overlap(W, (size_t)K * N * 2, w_scale, (size_t)N * 4) ||
+        overlap(Wq, (size_t)K * N, w_scale, (size_t)N * 4))
+        return LLMINT8_EINVAL;
+    return hip_status(launch_weight(dtype, W, K, N, Wq, w_scale, nullptr, (hipStream_t)stream));
+}
+
+LLMINT8_API size_t int8_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (M < 0 || K < 0 || N < 0) return 0;
+    return make_layout(M, K, N).total;
+}
+
+LLMINT8_API int int8_matmul_workspace_layout(int64_t M, int64_t K, int64_t N, llmint8_workspace_layout* out) {
+    if (!out || M < 0 || K < 0 || N < 0) return LLMINT8_EINVAL;
+    const Layout L = make_layout(M, K, N);
+    out->xq = L.xq;
+    out->xq_pitch = L.xq_pitch;
+    out->s_x = L.s_x;
+    out->n_outliers = L.n_outliers;
+    out->outliers = L.outliers;
+    out->xo = L.xo;
+    out->xo_pitch = L.xo_pitch;
+    out->wo = L.wo;
+    out->scratch = L.bitmap;
+    out->total = L.total;
+    return LLMINT8_OK;
+}
+
+LLMINT8_API int int8_matmul(const void* X, int64_t M, int64_t K, int dtype, const int8_t* Wq,
+                            const float* w_scale, int64_t N, float threshold, void* Y, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    if (!Y && M > 0 && N > 0) return LLMINT8_EINVAL;
+    return matmul_common(X, M, K, dtype, Wq, w_scale, N, threshold, Y, nullptr, nullptr, workspace,
+                         workspace_bytes, stream);
+}
+
+LLMINT8_API int int8_matmul_accumulators(const void* X, int64_t M, int64_t K, int dtype, const int8_t* Wq,
+                                         int64_t N, float threshold, int32_t* C, float* F, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+    if ((!C || !F) && M > 0 && N > 0) return LLMINT8_EINVAL;
+    return matmul_common(X, M, K, dtype, Wq, nullptr, N, threshold, nullptr, C, F, workspace, workspace_bytes,
+                         stream);
+}
+
+LLMINT8_API int int8_matmul_stats(const void* X, int64_t M, int64_t K, int dtype, float threshold,
+                                  int32_t* n_outlier_cols, int32_t* outlier_cols, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    int rc = check_shape(M, K, 0, dtype);
+    if (rc) return rc;
+    if ((rc = check_threshold(threshold))) return rc;
+    if (!n_outlier_cols) return LLMINT8_EINVAL;
+    if (M > 0 && K > 0 && (!X || !aligned(X, 16))) return LLMINT8_EINVAL;
+    if (outlier_cols && !aligned(outlier_cols, 4)) return LLMINT8_EINVAL;
+    const Layout L = make_layout(M, K, 0);
+    if (M > 0 && (!workspace || !aligned(workspace, 16) || workspace_bytes < L.total)) return LLMINT8_EWORKSPACE;
+    if (M == 0 || K == 0) {
+        *n_outlier_cols = 0;
+        return LLMINT8_OK;
+    }
+    hipStream_t st = (hipStream_t)stream;
+    int8_t* ws = (int8_t*)workspace;
+    hipError_t e = launch_detect(dtype, X, M, K, threshold, (uint32_t*)(ws + L.partial), st);
+    if (e == hipSuccess)
+        e = launch_compact(M, K, (const uint32_t*)(ws + L.partial), (uint32_t*)(ws + L.bitmap),
+                           (int32_t*)(ws + L.outliers), (int32_t*)(ws + L.n_outliers), st);
+    int32_t n = 0;
+    if (e == hipSuccess) e = hipMemcpyAsync(&n, ws + L.n_outliers, 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e == hipSuccess && outlier_cols && n > 0) {
+        e = hipMemcpyAsync(outlier_cols, ws + L.outliers, (size_t)n * 4, hipMemcpyDeviceToDevice, st);
+        if (e == hipSuccess) e = hipStreamSynchronize(st);
+    }
+    if (e != hipSuccess) return hip_status(e);
+    *n_outlier_cols = n;
+    return LLMINT8_OK;
+}

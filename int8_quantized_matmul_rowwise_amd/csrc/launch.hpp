@@ -1,0 +1,60 @@
+// Internal launchers of the llmint8 kernels (host side).  Each enqueues on `stream`
+// and returns the launch status; shapes were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace llmint8 {
+
+// ---- weight conversion
+// Column absmax partials over `splits` slices of K, then the final scale + the
+// quantize-transpose into Wq (N x K).
+int64_t weight_splits(int64_t K);
+hipError_t launch_weight(int dt, const void* W, int64_t K, int64_t N, int8_t* Wq, float* w_scale,
+                         float* partial /* weight_splits(K) x N */, hipStream_t stream);
+
+// ---- X pass
+int64_t detect_row_blocks(int64_t M);
+hipError_t launch_detect(int dt, const void* X, int64_t M, int64_t K, float tau, uint32_t* partial,
+                         hipStream_t stream);
+hipError_t launch_compact(int64_t M, int64_t K, const uint32_t* partial, uint32_t* bitmap, int32_t* O,
+                          int32_t* n_out, hipStream_t stream);
+
+struct XPassArgs {
+    int dt;
+    const void* X;
+    int64_t M, K, N;
+    const uint32_t* bitmap;
+    const int32_t* O;
+    const int32_t* n_out;
+    int8_t* Xq;
+    int64_t xq_pitch;
+    float* s_x;
+    void* XO;
+    int64_t xo_pitch;
+    const int8_t* Wq;  // NULL: no W_O gather
+    void* WO;
+};
+hipError_t launch_quantize_rows(const XPassArgs& a, hipStream_t stream);
+
+// ---- products + epilogue
+struct GemmArgs {
+    int dt;
+    const int8_t* Xq;
+    int64_t xq_pitch;
+    const int8_t* Wq;
+    int64_t M, N, K;
+    const float* s_x;
+    const float* s_w;
+    const void* XO;
+    const void* WO;
+    int64_t xo_pitch;
+    const int32_t* n_out;
+    void* Y;          // product path
+    int32_t* C_acc;   // accumulator dump (test hook); Y == NULL then
+    float* F_acc;
+};
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+
+}  // namespace llmint8

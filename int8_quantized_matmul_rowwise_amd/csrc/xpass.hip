@@ -1,0 +1,276 @@
+// The X pass of the LLM.int8() matmul: outlier feature dimensions, row scales, int8
+// codes with the outlier columns zeroed, and the compact 16-bit outlier operands.
+//
+// "LLM.int8(): 8-bit Matrix Multiplication for Transformers at Scale", abstract:
+// vector-wise quantization (one constant per row of X) plus a decomposition that
+// isolates the outlier feature dimensions into a 16-bit product.  The outlier set is
+// a property of the whole batch (talk summary "llama3-model-quantization",
+// "Understanding Outliers in Transformer Models": the outliers sit in specific columns
+// of the input batch), so no row can be coded before every row has been scanned: the
+// pass is two HBM sweeps over X (detect, then code) around a one-workgroup compaction.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace llmint8 {
+
+// ---------------------------------------------------------------------------
+// Detect: bit j of word w of partial[rb] is set iff some row of row-block rb has
+// |X[i, 32w + j]| > tau.  One thread owns 8 consecutive columns (one 16-byte load per
+// row); the four waves of a block split the rows.  No atomics and no pre-zeroed
+// memory: every (row-block, word) slot is written exactly once.
+template <int DT>
+__global__ __launch_bounds__(256) void detect_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                     int64_t rows_per_block, float tau,
+                                                     uint32_t* __restrict__ partial, int64_t Kw) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t chunk = (int64_t)blockIdx.x * 64 + lane;
+    const int64_t nchunks = K / 8;
+    const int64_t r0 = (int64_t)blockIdx.y * rows_per_block;
+    const int64_t r1 = r0 + rows_per_block < M ? r0 + rows_per_block : M;
+    uint32_t mask = 0;
+    if (chunk < nchunks) {
+        const uint16_t* col = X + chunk * 8;
+        int64_t r = r0 + w;
+        for (; r + 12 < r1; r += 16) {  // four rows in flight per thread
+            u32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = *(const u32x4*)(col + (r + 4 * u) * K);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    uint16_t h = (uint16_t)(v[u][j >> 1] >> (16 * (j & 1)));
+                    mask |= (__builtin_fabsf(to_f32<DT>(h)) > tau ? 1u : 0u) << j;
+                }
+        }
+        for (; r < r1; r += 4) {
+            u32x4 v = *(const u32x4*)(col + r * K);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                uint16_t h = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
+                mask |= (__builtin_fabsf(to_f32<DT>(h)) > tau ? 1u : 0u) << j;
+            }
+        }
+    }
+    __shared__ uint32_t sm[4][64];
+    sm[w][lane] = mask;
+    __syncthreads();
+    if (w == 0) {
+        mask = sm[0][lane] | sm[1][lane] | sm[2][lane] | sm[3][lane];
+        uint32_t word = mask << (8 * (lane & 3));
+        word |= __shfl_xor(word, 1, kWave);
+        word |= __shfl_xor(word, 2, kWave);
+        const int64_t wi = chunk >> 2;
+        if ((lane & 3) == 0 && wi < Kw) partial[(int64_t)blockIdx.y * Kw + wi] = word;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Compact (one workgroup of 1024 threads): OR the row-block partials into the
+// bitmap, then list the set bits in ascending column order (block-wide exclusive scan
+// of per-word popcounts), and store n_O.
+__global__ __launch_bounds__(1024) void compact_kernel(const uint32_t* __restrict__ partial, int64_t n_rb, int64_t Kw,
+                                                       uint32_t* __restrict__ bitmap, int32_t* __restrict__ O,
+                                                       int32_t* __restrict__ n_out) {
+    __shared__ int32_t wsum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int32_t base = 0;
+    for (int64_t w0 = 0; w0 < Kw; w0 += 1024) {
+        const int64_t wi = w0 + tid;
+        uint32_t word = 0;
+        if (wi < Kw) {
+            for (int64_t b = 0; b < n_rb; ++b) word |= partial[b * Kw + wi];
+            bitmap[wi] = word;
+        }
+        const int32_t cnt = __popc(word);
+        int32_t incl = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            int32_t t = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += t;
+        }
+        if (lane == 63) wsum[wv] = incl;
+        __syncthreads();
+        int32_t before = 0, total = 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int32_t s = wsum[q];
+            before += q < wv ? s : 0;
+            total += s;
+        }
+        int32_t pos = base + before + incl - cnt;
+        uint32_t wd = word;
+        while (wd) {
+            const int b = __ffs(wd) - 1;
+            O[pos++] = (int32_t)(wi * 32 + b);
+            wd &= wd - 1;
+        }
+        base += total;
+        __syncthreads();  // wsum is reused by the next chunk of words
+    }
+    if (tid == 0) *n_out = base;
+}
+
+// ---------------------------------------------------------------------------
+// Code the rows (blocks 0..M-1, one row each) and gather the outlier operands of W
+// (blocks M.., 64 rows of Wq each).
+//   s_x[i] = max over non-outlier j of |X[i,j]|;  Xq[i,j] = 0 for j in O, else the
+//   vector-wise code;  Xq[i, K..pitch) = 0;  XO[i,t] = X[i,O[t]] for t < n_O and 0 up to
+//   the next multiple of 32.
+//   WO[n,t] = (dtype) Wq[n, O[t]] (exact), same padding.
+// CH: 8-element chunks held per thread (row kept in registers between the max and the
+// coding); CH == 0 is the general form that reads the row twice (second read from L2).
+template <int DT, int CH>
+__global__ __launch_bounds__(256) void quantize_rows_kernel(
+    const uint16_t* __restrict__ X, int64_t M, int64_t K, const uint32_t* __restrict__ bitmap,
+    const int32_t* __restrict__ O, const int32_t* __restrict__ n_out, int8_t* __restrict__ Xq, int64_t xq_pitch,
+    float* __restrict__ s_x, uint16_t* __restrict__ XO, int64_t xo_pitch, const int8_t* __restrict__ Wq,
+    int64_t N, uint16_t* __restrict__ WO) {
+    const int tid = threadIdx.x;
+    const int32_t nO = *n_out;
+    const int32_t P = (nO + 31) & ~31;
+    const int64_t b = blockIdx.x;
+
+    if (b >= M) {
+        const int64_t n0 = (b - M) * 64;
+        for (int64_t idx = tid; idx < 64 * (int64_t)P; idx += 256) {
+            const int64_t r = idx / P, t = idx % P;
+            const int64_t n = n0 + r;
+            if (n < N) {
+                uint16_t v = 0;
+                if (t < nO) v = from_f32<DT>((float)Wq[n * K + O[t]]);
+                WO[n * xo_pitch + t] = v;
+            }
+        }
+        return;
+    }
+
+    const int64_t i = b;
+    const uint16_t* row = X + i * K;
+    const int64_t nch = K / 8;
+    __shared__ float red[4];
+
+    float m = 0.0f;
+    u32x4 v[CH > 0 ? CH : 1];
+    uint32_t om[CH > 0 ? CH : 1];
+    if constexpr (CH > 0) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int64_t ch = tid + (int64_t)c * 256;
+            om[c] = 0xffu;
+            if (ch < nch) {
+                v[c] = *(const u32x4*)(row + ch * 8);
+                om[c] = (bitmap[ch >> 2] >> (8 * (ch & 3))) & 0xffu;
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float a = __builtin_fabsf(to_f32<DT>((uint16_t)(v[c][j >> 1] >> (16 * (j & 1)))));
+                if (!((om[c] >> j) & 1u)) m = fmaxf(m, a);
+            }
+    } else {
+        for (int64_t ch = tid; ch < nch; ch += 256) {
+            const u32x4 x = *(const u32x4*)(row + ch * 8);
+            const uint32_t o = (bitmap[ch >> 2] >> (8 * (ch & 3))) & 0xffu;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float a = __builtin_fabsf(to_f32<DT>((uint16_t)(x[j >> 1] >> (16 * (j & 1)))));
+                if (!((o >> j) & 1u)) m = fmaxf(m, a);
+            }
+        }
+    }
+    m = wave_max(m);
+    if ((tid & 63) == 0) red[tid >> 6] = m;
+    __syncthreads();
+    const float s = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float inv = inv_scale(s);
+
+    auto code8 = [&](const u32x4& x, uint32_t o) -> u32x2 {
+        u32x2 packed = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float f = to_f32<DT>((uint16_t)(x[j >> 1] >> (16 * (j & 1))));
+            const int q = ((o >> j) & 1u) ? 0 : quantize(f, inv);
+            packed[j >> 2] |= ((uint32_t)q & 0xffu) << (8 * (j & 3));
+        }
+        return packed;
+    };
+    int8_t* qrow = Xq + i * xq_pitch;
+    if constexpr (CH > 0) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int64_t ch = tid + (int64_t)c * 256;
+            if (ch < nch) *(u32x2*)(qrow + ch * 8) = code8(v[c], om[c]);
+        }
+    } else {
+        for (int64_t ch = tid; ch < nch; ch += 256) {
+            const u32x4 x = *(const u32x4*)(row + ch * 8);
+            const uint32_t o = (bitmap[ch >> 2] >> (8 * (ch & 3))) & 0xffu;
+            *(u32x2*)(qrow + ch * 8) = code8(x, o);
+        }
+    }
+    for (int64_t ch = nch + tid; ch < xq_pitch / 8; ch += 256) *(u32x2*)(qrow + ch * 8) = u32x2{0u, 0u};
+    if (tid == 0) s_x[i] = s;
+    for (int64_t t = tid; t < P; t += 256) XO[i * xo_pitch + t] = t < nO ? row[O[t]] : (uint16_t)0;
+}
+
+// ---------------------------------------------------------------------------
+
+int64_t detect_row_blocks(int64_t M) {
+    if (M <= 0) return 0;
+    int64_t nrb = ceil_div(M, 64);
+    return nrb > 32 ? 32 : nrb;
+}
+
+hipError_t launch_detect(int dt, const void* X, int64_t M, int64_t K, float tau, uint32_t* partial,
+                         hipStream_t stream) {
+    const int64_t nrb = detect_row_blocks(M);
+    const int64_t Kw = ceil_div(K, 32);
+    if (nrb == 0 || K == 0) return hipSuccess;
+    const int64_t rpb = round_up(ceil_div(M, nrb), 4);
+    dim3 grid((unsigned)ceil_div(K / 8, 64), (unsigned)nrb);
+    if (dt == F16)
+        detect_kernel<F16><<<grid, 256, 0, stream>>>((const uint16_t*)X, M, K, rpb, tau, partial, Kw);
+    else
+        detect_kernel<BF16><<<grid, 256, 0, stream>>>((const uint16_t*)X, M, K, rpb, tau, partial, Kw);
+    return hipGetLastError();
+}
+
+hipError_t launch_compact(int64_t M, int64_t K, const uint32_t* partial, uint32_t* bitmap, int32_t* O,
+                          int32_t* n_out, hipStream_t stream) {
+    const int64_t nrb = detect_row_blocks(M);
+    const int64_t Kw = (M > 0 && K > 0) ? ceil_div(K, 32) : 0;
+    compact_kernel<<<1, 1024, 0, stream>>>(partial, nrb, Kw, bitmap, O, n_out);
+    return hipGetLastError();
+}
+
+template <int DT, int CH>
+static void quantize_rows_dispatch(dim3 grid, hipStream_t stream, const XPassArgs& a) {
+    quantize_rows_kernel<DT, CH><<<grid, 256, 0, stream>>>(
+        (const uint16_t*)a.X, a.M, a.K, a.bitmap, a.O, a.n_out, a.Xq, a.xq_pitch, a.s_x, (uint16_t*)a.XO,
+        a.xo_pitch, a.Wq, a.N, (uint16_t*)a.WO);
+}
+
+template <int DT>
+static void quantize_rows_pick(dim3 grid, hipStream_t stream, const XPassArgs& a) {
+    const int64_t per_thread = ceil_div(a.K / 8, 256);
+    if (per_thread <= 1) quantize_rows_dispatch<DT, 1>(grid, stream, a);
+    else if (per_thread <= 2) quantize_rows_dispatch<DT, 2>(grid, stream, a);
+    else if (per_thread <= 4) quantize_rows_dispatch<DT, 4>(grid, stream, a);
+    else if (per_thread <= 8) quantize_rows_dispatch<DT, 8>(grid, stream, a);
+    else if (per_thread <= 16) quantize_rows_dispatch<DT, 16>(grid, stream, a);
+    else quantize_rows_dispatch<DT, 0>(grid, stream, a);
+}
+
+hipError_t launch_quantize_rows(const XPassArgs& a, hipStream_t stream) {
+    const int64_t nblk = a.M + (a.Wq ? ceil_div(a.N, 64) : 0);
+    if (nblk == 0) return hipSuccess;
+    dim3 grid((unsigned)nblk);
+    if (a.dt == F16) quantize_rows_pick<F16>(grid, stream, a);
+    else quantize_rows_pick<BF16>(grid, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace llmint8

@@ -1,0 +1,108 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every function its header
+declares, sizes its workspace, and rejects bad arguments before any GPU work (these
+calls return before the first HIP call, so they run without a GPU)."""
+import ctypes
+import math
+import re
+
+import pytest
+
+import int8_quantized_matmul_rowwise_amd as L
+
+INF = float("inf")
+A16 = 0x10000  # a fake, 16-byte-aligned device address: never dereferenced by these calls
+
+
+def _declared_functions():
+    src = open(L.HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert set(names) >= {"int8_quantize_weight", "int8_matmul", "int8_matmul_stats",
+                          "int8_matmul_workspace_bytes", "int8_matmul_workspace_layout",
+                          "int8_matmul_accumulators", "llmint8_status_string"}
+    lib = ctypes.CDLL(L.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L._SIGNATURES)
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, 7):
+        assert L.status_string(s).startswith("LLMINT8")
+
+
+def test_workspace_layout_regions_fit_and_align():
+    for (M, K, N) in [(1, 16, 8), (32, 256, 128), (300, 1040, 520), (4096, 12288, 36864), (0, 64, 8), (5, 0, 8)]:
+        lay = L.int8_matmul_workspace_layout(M, K, N)
+        assert lay["total"] == L.int8_matmul_workspace_bytes(M, K, N)
+        assert lay["xq_pitch"] % 256 == 0 and lay["xq_pitch"] >= K
+        assert lay["xo_pitch"] % 32 == 0 and lay["xo_pitch"] >= K
+        regions = sorted([(lay["xq"], M * lay["xq_pitch"]), (lay["s_x"], 4 * M), (lay["n_outliers"], 4),
+                          (lay["outliers"], 4 * K), (lay["xo"], 2 * M * lay["xo_pitch"]),
+                          (lay["wo"], 2 * N * lay["xo_pitch"]), (lay["scratch"], 4 * math.ceil(K / 32))])
+        for (o, n), (o2, _) in zip(regions, regions[1:]):
+            assert o % 256 == 0 and o + n <= o2
+        assert regions[-1][0] + regions[-1][1] <= lay["total"]
+
+
+def _mm(**kw):
+    a = dict(X=A16, M=4, K=64, dt=0, Wq=A16 * 2, s_w=A16 * 3, N=8, tau=6.0, Y=A16 * 4 + 0x100000,
+             ws=A16 * 0x1000, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return L.lib().int8_matmul(a["X"], a["M"], a["K"], a["dt"], a["Wq"], a["s_w"], a["N"], a["tau"], a["Y"],
+                               a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dt=2), L.EINVAL), (dict(M=-1), L.EINVAL), (dict(K=-16), L.EINVAL), (dict(N=-8), L.EINVAL),
+    (dict(K=24), L.EINVAL), (dict(N=12), L.EINVAL), (dict(K=133152), L.ERANGE),
+    (dict(tau=float("nan")), L.EINVAL), (dict(tau=-1.0), L.EINVAL),
+    (dict(X=None), L.EINVAL), (dict(X=A16 + 8), L.EINVAL), (dict(Wq=None), L.EINVAL), (dict(Y=None), L.EINVAL),
+    (dict(Y=A16 + 2), L.EINVAL), (dict(s_w=None), L.EINVAL), (dict(ws=None), L.EWORKSPACE), (dict(wsb=100), L.EWORKSPACE),
+    (dict(Y=A16), L.EINVAL),  # Y overlaps X
+])
+def test_matmul_rejects(kw, code):
+    assert _mm(**kw) == code
+
+
+def test_matmul_empty_batch_is_a_noop():
+    assert _mm(M=0, X=None, ws=None, wsb=0) == L.OK
+
+
+def test_quantize_weight_rejects():
+    q = L.lib().int8_quantize_weight
+    assert q(A16, 64, 8, 3, A16 * 2, A16 * 4, None) == L.EINVAL
+    assert q(A16, 60, 8, 0, A16 * 2, A16 * 4, None) == L.EINVAL
+    assert q(A16, 64, 9, 0, A16 * 2, A16 * 4, None) == L.EINVAL
+    assert q(None, 64, 8, 0, A16 * 2, A16 * 4, None) == L.EINVAL
+    assert q(A16, 64, 8, 0, A16 * 2, None, None) == L.EINVAL
+    assert q(A16, 64, 8, 0, A16 + 64, A16 * 4, None) == L.EINVAL     # Wq overlaps W
+    assert q(A16, 200000, 8, 0, A16 * 2, A16 * 4, None) == L.ERANGE
+    assert q(None, 64, 0, 0, None, None, None) == L.OK                # N = 0: nothing to do
+
+
+def test_stats_rejects():
+    s = L.lib().int8_matmul_stats
+    n = ctypes.c_int32(-5)
+    assert s(A16, 4, 64, 0, 6.0, None, None, A16 * 4, 1 << 20, None) == L.EINVAL
+    assert s(A16, 4, 64, 0, float("nan"), ctypes.byref(n), None, A16 * 4, 1 << 20, None) == L.EINVAL
+    assert s(A16, 4, 64, 0, 6.0, ctypes.byref(n), None, A16 * 4, 10, None) == L.EWORKSPACE
+    assert s(A16, 4, 60, 0, 6.0, ctypes.byref(n), None, A16 * 4, 1 << 20, None) == L.EINVAL
+    assert s(None, 0, 64, 0, 6.0, ctypes.byref(n), None, None, 0, None) == L.OK and n.value == 0
+
+
+def test_accumulators_rejects():
+    a = L.lib().int8_matmul_accumulators
+    assert a(A16, 4, 64, 0, A16 * 2, 8, 6.0, None, A16 * 8, A16 * 16, 1 << 30, None) == L.EINVAL
+    assert a(A16, 4, 64, 1, A16 * 2, 8, -2.0, A16 * 4, A16 * 8, A16 * 16, 1 << 30, None) == L.EINVAL
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    with pytest.raises(TypeError):
+        L.int8_matmul(torch.zeros(4, 64, dtype=torch.float16), torch.zeros(8, 64, dtype=torch.int8),
+                      torch.zeros(8), 6.0)
