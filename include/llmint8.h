@@ -110,6 +110,26 @@ int int8_matmul_stats(const void* X, int64_t M, int64_t K, int dtype, float thre
                       int32_t* n_outlier_cols, int32_t* outlier_cols,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The two stages int8_matmul runs, for callers that reuse one X pass.
+ *   int8_matmul_prepare:  the X pass -- outlier set O and n_O, row scales s_x, int8
+ *                         codes Xq with the outlier columns zeroed, and the compact
+ *                         16-bit outlier operands X[:,O] and Wq[:,O] -- into the
+ *                         workspace (layout: int8_matmul_workspace_layout).  Wq may be
+ *                         NULL when N == 0.
+ *   int8_matmul_products: C = Xq Wq^T (int8, int32 accumulation), F = X[:,O] Wq[:,O]^T
+ *                         (16-bit, fp32 accumulation) and the dequantizing epilogue,
+ *                         from a workspace prepared for the same X, Wq, M, K, N, dtype
+ *                         and threshold on the same stream.
+ * int8_matmul(X, ...) == int8_matmul_prepare(X, ...) then int8_matmul_products(...).
+ * Same conventions and status codes as int8_matmul.
+ */
+int int8_matmul_prepare(const void* X, int64_t M, int64_t K, int dtype, const int8_t* Wq, int64_t N,
+                        float threshold, void* workspace, size_t workspace_bytes, void* stream);
+
+int int8_matmul_products(int64_t M, int64_t K, int dtype, const int8_t* Wq, const float* w_scale, int64_t N,
+                         void* Y, const void* workspace, size_t workspace_bytes, void* stream);
+
 /* Where int8_matmul leaves the X pass's products in its workspace (byte offsets from
  * the workspace start; pitches in elements).  All regions are 256-byte aligned.
  *   xq        int8  [M][xq_pitch]   Xq; columns in O are 0; columns >= K are 0

@@ -53,6 +53,8 @@ _SIGNATURES = {
     "int8_matmul_stats": (_I, [_P, _I64, _I64, _I, _F, _P, _P, _P, _SZ, _P]),
     "int8_matmul_workspace_layout": (_I, [_I64, _I64, _I64, ctypes.POINTER(WorkspaceLayout)]),
     "int8_matmul_accumulators": (_I, [_P, _I64, _I64, _I, _P, _I64, _F, _P, _P, _P, _SZ, _P]),
+    "int8_matmul_prepare": (_I, [_P, _I64, _I64, _I, _P, _I64, _F, _P, _SZ, _P]),
+    "int8_matmul_products": (_I, [_I64, _I64, _I, _P, _P, _I64, _P, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -161,6 +163,36 @@ def int8_matmul(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor, thresh
     return Y
 
 
+def int8_matmul_prepare(X: torch.Tensor, Wq: torch.Tensor, threshold: float = 6.0,
+                        workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Stage 1 of int8_matmul (the X pass) into a workspace, which is returned."""
+    _dev_tensor(X, "X")
+    if X.dtype not in _DT or X.dim() != 2:
+        raise TypeError("X must be a 2-D fp16 or bf16 tensor")
+    M, K = X.shape
+    _dev_tensor(Wq, "Wq", torch.int8)
+    N = Wq.shape[0]
+    ws = _workspace(workspace, int8_matmul_workspace_bytes(M, K, N), X.device)
+    _check(lib().int8_matmul_prepare(_ptr(X), M, K, _DT[X.dtype], _ptr(Wq), N, float(threshold), _ptr(ws),
+                                     ws.numel(), _stream(X, stream)), "int8_matmul_prepare")
+    return ws
+
+
+def int8_matmul_products(M: int, K: int, dtype: torch.dtype, Wq: torch.Tensor, w_scale: torch.Tensor,
+                         workspace: torch.Tensor, Y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Stage 2 of int8_matmul: the products and the epilogue from a prepared workspace."""
+    _dev_tensor(Wq, "Wq", torch.int8)
+    _dev_tensor(w_scale, "w_scale", torch.float32)
+    _dev_tensor(workspace, "workspace")
+    N = Wq.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=dtype, device=Wq.device)
+    _dev_tensor(Y, "Y", dtype)
+    _check(lib().int8_matmul_products(M, K, _DT[dtype], _ptr(Wq), _ptr(w_scale), N, _ptr(Y), _ptr(workspace),
+                                      workspace.numel(), _stream(Wq, stream)), "int8_matmul_products")
+    return Y
+
+
 def int8_matmul_stats(X: torch.Tensor, threshold: float = 6.0, outlier_cols: Optional[torch.Tensor] = None,
                       workspace: Optional[torch.Tensor] = None, stream=None) -> Tuple[int, torch.Tensor]:
     """(n_O, O[:n_O]) -- the outlier feature dimensions of X (synchronizes the stream)."""
@@ -216,7 +248,7 @@ def workspace_views(ws: torch.Tensor, M: int, K: int, N: int, dtype: torch.dtype
 
 
 __all__ = [
-    "int8_quantize_weight", "int8_matmul", "int8_matmul_stats", "int8_matmul_workspace_bytes",
+    "int8_quantize_weight", "int8_matmul", "int8_matmul_stats", "int8_matmul_prepare", "int8_matmul_products", "int8_matmul_workspace_bytes",
     "int8_matmul_workspace_layout", "int8_matmul_accumulators", "workspace_views", "LLMInt8Error", "lib",
     "status_string",
 ]

@@ -107,37 +107,50 @@ int run_xpass(const void* X, int64_t M, int64_t K, int dtype, float tau, const i
     return hip_status(e);
 }
 
-int matmul_common(const void* X, int64_t M, int64_t K, int dtype, const int8_t* Wq, const float* w_scale,
-                  int64_t N, float threshold, void* Y, int32_t* C, float* F, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+// Each stage validates its arguments and, when `enqueue` is set and they are valid,
+// enqueues its kernels.
+int prepare_common(const void* X, int64_t M, int64_t K, int dtype, const int8_t* Wq, int64_t N, float threshold,
+                   void* workspace, size_t workspace_bytes, void* stream, bool enqueue) {
     int rc = check_shape(M, K, N, dtype);
     if (rc) return rc;
     if ((rc = check_threshold(threshold))) return rc;
-    const bool acc = Y == nullptr;
     if (M > 0 && K > 0 && (!X || !aligned(X, 16))) return LLMINT8_EINVAL;
-    if (N > 0 && K > 0 && (!Wq || !aligned(Wq, 16))) return LLMINT8_EINVAL;
+    if (M > 0 && N > 0 && K > 0 && (!Wq || !aligned(Wq, 16))) return LLMINT8_EINVAL;
+    const Layout L = make_layout(M, K, N);
+    if (M > 0 && (!workspace || !aligned(workspace, 16) || workspace_bytes < L.total)) return LLMINT8_EWORKSPACE;
+    if (overlap(workspace, L.total, X, (size_t)M * (size_t)K * 2) ||
+        overlap(workspace, L.total, Wq, (size_t)N * (size_t)K))
+        return LLMINT8_EINVAL;
+    if (M == 0 || !enqueue) return LLMINT8_OK;
+    return run_xpass(X, M, K, dtype, threshold, N > 0 ? Wq : nullptr, N, (int8_t*)workspace, L,
+                     (hipStream_t)stream);
+}
+
+// Products + epilogue (Y != NULL) or the accumulator dump (C, F) from a prepared workspace.
+int products_common(int64_t M, int64_t K, int dtype, const int8_t* Wq, const float* w_scale, int64_t N, void* Y,
+                    int32_t* C, float* F, const void* workspace, size_t workspace_bytes, void* stream,
+                    bool enqueue) {
+    int rc = check_shape(M, K, N, dtype);
+    if (rc) return rc;
+    const bool acc = Y == nullptr;
     if (M > 0 && N > 0) {
+        if (K > 0 && (!Wq || !aligned(Wq, 16))) return LLMINT8_EINVAL;
         if (acc) {
             if (!C || !F || !aligned(C, 16) || !aligned(F, 16)) return LLMINT8_EINVAL;
-        } else {
-            if (!Y || !aligned(Y, 16)) return LLMINT8_EINVAL;
-            if (!w_scale || !aligned(w_scale, 4)) return LLMINT8_EINVAL;
+        } else if (!Y || !aligned(Y, 16) || !w_scale || !aligned(w_scale, 4)) {
+            return LLMINT8_EINVAL;
         }
     }
     const Layout L = make_layout(M, K, N);
-    if (M > 0 && (!workspace || !aligned(workspace, 16))) return LLMINT8_EWORKSPACE;
-    if (M > 0 && workspace_bytes < L.total) return LLMINT8_EWORKSPACE;
+    if (M > 0 && (!workspace || !aligned(workspace, 16) || workspace_bytes < L.total)) return LLMINT8_EWORKSPACE;
     if (!acc) {
-        const size_t ybytes = (size_t)M * (size_t)N * 2;
-        if (overlap(Y, ybytes, X, (size_t)M * (size_t)K * 2) || overlap(Y, ybytes, Wq, (size_t)N * (size_t)K) ||
-            overlap(Y, ybytes, w_scale, (size_t)N * 4) || overlap(Y, ybytes, workspace, L.total))
+        const size_t yb = (size_t)M * (size_t)N * 2;
+        if (overlap(Y, yb, Wq, (size_t)N * (size_t)K) || overlap(Y, yb, w_scale, (size_t)N * 4) ||
+            overlap(Y, yb, workspace, L.total))
             return LLMINT8_EINVAL;
     }
-    if (M == 0) return LLMINT8_OK;
-    hipStream_t st = (hipStream_t)stream;
-    int8_t* ws = (int8_t*)workspace;
-    rc = run_xpass(X, M, K, dtype, threshold, N > 0 ? Wq : nullptr, N, ws, L, st);
-    if (rc) return rc;
+    if (M == 0 || N == 0 || !enqueue) return LLMINT8_OK;
+    const int8_t* ws = (const int8_t*)workspace;
     GemmArgs g;
     g.dt = dtype;
     g.Xq = ws + L.xq;
@@ -155,7 +168,21 @@ int matmul_common(const void* X, int64_t M, int64_t K, int dtype, const int8_t* 
     g.Y = Y;
     g.C_acc = C;
     g.F_acc = F;
-    return hip_status(launch_gemm(g, st));
+    return hip_status(launch_gemm(g, (hipStream_t)stream));
+}
+
+int matmul_common(const void* X, int64_t M, int64_t K, int dtype, const int8_t* Wq, const float* w_scale,
+                  int64_t N, float threshold, void* Y, int32_t* C, float* F, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    // validate both stages before enqueueing either
+    int rc = prepare_common(X, M, K, dtype, Wq, N, threshold, workspace, workspace_bytes, stream, false);
+    if (rc) return rc;
+    rc = products_common(M, K, dtype, Wq, w_scale, N, Y, C, F, workspace, workspace_bytes, stream, false);
+    if (rc) return rc;
+    if (Y && overlap(Y, (size_t)M * (size_t)N * 2, X, (size_t)M * (size_t)K * 2)) return LLMINT8_EINVAL;
+    rc = prepare_common(X, M, K, dtype, Wq, N, threshold, workspace, workspace_bytes, stream, true);
+    if (rc) return rc;
+    return products_common(M, K, dtype, Wq, w_scale, N, Y, C, F, workspace, workspace_bytes, stream, true);
 }
 
 }  // namespace
@@ -252,4 +279,17 @@ LLMINT8_API int int8_matmul_stats(const void* X, int64_t M, int64_t K, int dtype
     if (e != hipSuccess) return hip_status(e);
     *n_outlier_cols = n;
     return LLMINT8_OK;
+}
+
+LLMINT8_API int int8_matmul_prepare(const void* X, int64_t M, int64_t K, int dtype, const int8_t* Wq, int64_t N,
+                                    float threshold, void* workspace, size_t workspace_bytes, void* stream) {
+    return prepare_common(X, M, K, dtype, Wq, N, threshold, workspace, workspace_bytes, stream, true);
+}
+
+LLMINT8_API int int8_matmul_products(int64_t M, int64_t K, int dtype, const int8_t* Wq, const float* w_scale,
+                                     int64_t N, void* Y, const void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+    if (!Y && M > 0 && N > 0) return LLMINT8_EINVAL;
+    return products_common(M, K, dtype, Wq, w_scale, N, Y, nullptr, nullptr, workspace, workspace_bytes, stream,
+                           true);
 }

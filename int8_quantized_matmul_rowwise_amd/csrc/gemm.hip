@@ -1,6 +1,6 @@
 // The products of the LLM.int8() matmul and its dequantizing epilogue, one kernel:
-//   C = Xq Wq^T            int8 x int8 -> int32 on v_mfma_i32_16x16x64_i8 (exact),
-//   F = X[:,O] Wq[:,O]^T   16-bit x 16-bit -> fp32 on v_mfma_f32_16x16x32_{f16,bf16},
+//   C = Xq Wq^T            int8 x int8 -> int32 on v_mfma_i32_32x32x32_i8 (exact),
+//   F = X[:,O] Wq[:,O]^T   16-bit x 16-bit -> fp32 on v_mfma_f32_32x32x16_{f16,bf16},
 //   y = RN((RN(RN((float)C * r_i) * c_n)) + RN(c_n * F)),  r_i = s_x/127, c_n = s_w/127,
 //   Y = y rounded to the 16-bit type.
 // "LLM.int8(): 8-bit Matrix Multiplication for Transformers at Scale", abstract: the
@@ -8,15 +8,23 @@
 // outlier feature dimensions through a 16-bit product, summed into the same output.
 //
 // Tiling (gfx950: 64-wide waves, 160 KB LDS, 512 registers per lane at one wave/SIMD):
-//   block tile 256 x 256, K step 128 bytes, 4 waves in 2 x 2, each wave 128 x 128 =
-//   8 x 8 MFMA tiles of 16 x 16 -> 256 int32 accumulators per lane.
+//   block tile 256 x 256, 4 waves in 2 x 2, each wave 128 x 128 = 4 x 4 MFMA tiles of
+//   32 x 32 -> 256 int32 accumulators per lane (AGPRs).  (On gfx950 the 32x32x32 i8
+//   MFMA sustains the full int8 rate; the 16x16x64 form issues at about half of it.)
 //   Operands go HBM/L2 -> LDS with global_load_lds (16 B per lane, no register
-//   staging), two stages of 64 KB.  LDS rows are 128 B; the 16-byte chunk c of row r
-//   is stored at chunk c ^ (r & 7) ^ ((r >> 3) & 1), so the ds_read_b128 of 16
-//   consecutive rows at one k hit distinct banks.
+//   staging), one 128-byte line per row per K stage (full-line requests).  The LDS
+//   holds 2 A slots and 3 B slots of 32 KB: at the start of stage k the loads of A[k+1]
+//   and B[k+2] are issued, so the weight lines -- the ones that miss L2 -- get two
+//   stages to arrive.  Waits are counted (vmcnt) and the workgroup barrier is a bare
+//   s_barrier, so a barrier never drains the loads still in flight.  Each stage is
+//   four 32-deep MFMA sub-steps; the operands of the next sub-step are read from LDS
+//   into a second register set while the 16 MFMAs of the current one run.  The
+//   16-byte chunk c of LDS row r sits at chunk c ^ (r & 7) ^ ((r >> 3) & 1), so the
+//   ds_read_b128 of 16 consecutive rows at one k hit distinct banks (for both 8- and
+//   16-lane service groups).
 //   Tiles are assigned so that the workgroups the dispatcher places on one XCD (ids
-//   congruent mod 8) take a contiguous run of tiles in grouped order (4 row-tiles per
-//   group): concurrently running tiles on an XCD share A and B panels in its L2.
+//   congruent mod 8) take a contiguous run of tiles in grouped order (8 row-tiles per
+//   group): the 32 tiles running together on an XCD share A and B panels in its L2.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -24,17 +32,35 @@ namespace llmint8 {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 128;
-constexpr int kStageBytes = (BM + BN) * BK;  // 64 KB
-constexpr int kStages = 2;
-constexpr int kGroupM = 4;
+constexpr int NJ = 4;                                    // 32-column MFMA tiles per wave along N
+constexpr int BM = 256, BN = 64 * NJ;
+constexpr int BK = 128;                                  // bytes of K per stage: one line per row
+constexpr int kTileBytes = BM * BK;                      // one operand's stage: 32 KB
+constexpr int kChunks = BK / 16;                         // 16-byte chunks per row segment
+constexpr int kRowsPerLoad = 64 / kChunks;               // rows covered by one 64-lane load
+constexpr int kLoadsA = BM / kRowsPerLoad / 4;           // per wave, per stage (8)
+constexpr int kLoadsB = BN / kRowsPerLoad / 4;           // per wave, per stage (8)
+constexpr int kSlotsA = 2, kSlotsB = 3;                  // 5 x 32 KB: the whole 160 KB of LDS
+constexpr int kSlotBytesB = BN * BK;
+constexpr int kSubSteps = BK / 32;                       // 32-deep MFMA steps per stage
+constexpr int kGroupM = 8;                               // row tiles per group of the tile order
 constexpr int kXcds = 8;
+static_assert(kSlotsA * kTileBytes + kSlotsB * kSlotBytesB <= 160 * 1024, "LDS");
+static_assert(kLoadsA == 8 && kLoadsB == 8, "the waits below count 8 loads per operand and wave");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ __forceinline__ void load_lds16(const void* g, int8_t* lds_base) {
     __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_base, 16, 0, 0);
 }
+
+// Chunk swizzle: the 16-byte chunk c of LDS row r is stored at chunk c ^ swz(r), so that
+// the ds_read_b128 of 16 consecutive rows at one chunk touch distinct banks.
+__host__ __device__ constexpr int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Wait until at most N of this wave's direct-to-LDS loads are in flight and its LDS
+// reads are done, then the workgroup barrier (no fence: later loads stay in flight).
+#define LLMINT8_WAIT_BARRIER(N) asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
 struct Params {
     const int8_t* Xq;
@@ -54,16 +80,16 @@ struct Params {
 };
 
 template <int DT>
-__device__ __forceinline__ v4f mfma16(const u32x4& a, const u32x4& b, const v4f& c) {
+__device__ __forceinline__ v16f mfma16(const u32x4& a, const u32x4& b, const v16f& c) {
     if constexpr (DT == F16)
-        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
     else
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
 template <int DT, bool ACC_OUT>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
-    __shared__ __attribute__((aligned(1024))) int8_t smem[kStages * kStageBytes];
+    __shared__ __attribute__((aligned(1024))) int8_t smem[kSlotsA * kTileBytes + kSlotsB * kSlotBytesB];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
 
@@ -81,111 +107,158 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
     // ---- loader: wave w fills LDS slots [64*(8w+j), +64) of each operand, j = 0..7:
-    // rows r = 64w + 8j + lane/8, physical chunk lane%8 -> logical chunk c.
-    const int lrow = 64 * w + (lane >> 3);
-    const int c_even = (lane & 7) ^ (lane >> 3);      // j even: (r>>3)&1 == 0
-    const int c_odd = c_even ^ 1;                     // j odd
-    const int nk = (int)ceil_div(p.K, BK);
-
-    auto issue_stage = [&](int kt, int stage) {
-        int8_t* As = smem + stage * kStageBytes;
-        int8_t* Bs = As + BM * BK;
-        const int64_t kb = (int64_t)kt * BK;
+    // row r = 8*(8w + j) + lane/8 (one 128-byte line per row), physical chunk lane%8,
+    // logical chunk c_ld(j) = (lane%8) ^ swz(r).
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    uint32_t a_off[kLoadsA], b_off[kLoadsB];
+    int cb_ld[kLoadsB];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int r = lrow + 8 * j;
-            const int c = (j & 1) ? c_odd : c_even;
-            int64_t m = m0 + r;
-            m = m < p.M ? m : p.M - 1;
-            load_lds16(p.Xq + m * p.xq_pitch + kb + c * 16, As + (8 * w + j) * 1024);
-            int64_t n = n0 + r;
-            n = n < p.N ? n : p.N - 1;
-            int64_t k = kb + c * 16;
-            k = k < p.K ? k : 0;  // past K the A side is zero; any in-bounds bytes will do
-            load_lds16(p.Wq + n * p.K + k, Bs + (8 * w + j) * 1024);
+    for (int j = 0; j < kLoadsA; ++j) {
+        const int r = kRowsPerLoad * (kLoadsA * wu + j) + lane / kChunks;
+        const int c = (lane % kChunks) ^ swz(r);
+        const int64_t m = m0 + r < p.M ? m0 + r : p.M - 1;
+        a_off[j] = (uint32_t)((m - m0) * p.xq_pitch + c * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < kLoadsB; ++j) {
+        const int r = kRowsPerLoad * (kLoadsB * wu + j) + lane / kChunks;
+        cb_ld[j] = (lane % kChunks) ^ swz(r);
+        const int64_t n = n0 + r < p.N ? n0 + r : p.N - 1;
+        b_off[j] = (uint32_t)((n - n0) * p.K + cb_ld[j] * 16);
+    }
+    const int8_t* a_tile = p.Xq + m0 * p.xq_pitch;
+    const int8_t* b_tile = p.Wq + n0 * p.K;
+    const int nk = (int)ceil_div(p.K, BK);
+    const bool k_tail = (p.K % BK) != 0;
+
+    auto slot_a = [&](int kt) { return smem + (kt % kSlotsA) * kTileBytes; };
+    auto slot_b = [&](int kt) { return smem + kSlotsA * kTileBytes + (kt % kSlotsB) * kSlotBytesB; };
+    auto stage_k = [](int kt) { return kt * BK; };
+    auto issue_a = [&](int kt) {
+        int8_t* As = slot_a(kt);
+        const int kb = stage_k(kt);
+#pragma unroll
+        for (int j = 0; j < kLoadsA; ++j) load_lds16(a_tile + kb + a_off[j], As + (kLoadsA * wu + j) * 1024);
+    };
+    auto issue_b = [&](int kt) {
+        int8_t* Bs = slot_b(kt);
+        const int kb = stage_k(kt);
+        if (!k_tail || kb + BK <= p.K) {
+#pragma unroll
+            for (int j = 0; j < kLoadsB; ++j) load_lds16(b_tile + kb + b_off[j], Bs + (kLoadsB * wu + j) * 1024);
+        } else {
+            // the partial K stage: chunks past K read the row start instead (their A side is zero)
+#pragma unroll
+            for (int j = 0; j < kLoadsB; ++j) {
+                const int kk = kb + cb_ld[j] * 16;
+                load_lds16(b_tile + b_off[j] - cb_ld[j] * 16 + (kk < p.K ? kk : 0), Bs + (kLoadsB * wu + j) * 1024);
+            }
         }
     };
 
-    // ---- per-lane LDS read offsets for the MFMA operands (row within the wave's
-    // 128-row panel: 16*bi + lane%16; k chunk 4*ks + lane/16)
-    const int s = (lane & 7) ^ ((lane >> 3) & 1);
-    const int q = lane >> 4;
-    const int rd0 = (lane & 15) * BK + ((q ^ s) << 4);
-    const int rd1 = (lane & 15) * BK + (((q + 4) ^ s) << 4);
+    // ---- MFMA operand reads (32x32x32: lane holds row lane%32, 16 k at 16*(lane/32)):
+    // fragment i of sub-step u reads row 32*i + lane%32 of the wave's 128-row panel,
+    // logical chunk 2u + lane/32.
+    const int rl = lane & 31, h = lane >> 5;
+    int rd[kSubSteps];
+#pragma unroll
+    for (int u = 0; u < kSubSteps; ++u) rd[u] = rl * BK + (((2 * u + h) ^ swz(rl)) << 4);
+    auto read_frags = [&](int kt, int u, v4i (&fa)[4], v4i (&fb)[NJ]) {
+        const int8_t* As = slot_a(kt) + wm * 128 * BK + rd[u];
+        const int8_t* Bs = slot_b(kt) + wn * (32 * NJ) * BK + rd[u];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) fa[i] = *(const v4i*)(As + i * 32 * BK);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) fb[j] = *(const v4i*)(Bs + j * 32 * BK);
+    };
 
-    v4i acc[8][8];
+    v16i acc[4][NJ];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = v4i{0, 0, 0, 0};
+        for (int j = 0; j < NJ; ++j) acc[i][j] = v16i{};
 
-    if (nk > 0) issue_stage(0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (kt + 1 < nk) issue_stage(kt + 1, (kt + 1) & 1);
-        const int8_t* As = smem + (kt & 1) * kStageBytes + wm * 128 * BK;
-        const int8_t* Bs = smem + (kt & 1) * kStageBytes + BM * BK + wn * 128 * BK;
+    auto mfma_all = [&](const v4i (&fa)[4], const v4i (&fb)[NJ]) {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const int rd = ks ? rd1 : rd0;
-            v4i a[8], b[8];
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) a[i] = *(const v4i*)(As + rd + i * 16 * BK);
+            for (int j = 0; j < NJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    };
+
+    if (nk > 0) {
+        v4i fa[2][4], fb[2][NJ];  // operand sets of the current / next sub-step
+        // prologue: A[0], B[0], B[1] in flight; wait for the first two groups
+        issue_a(0);
+        issue_b(0);
+        if (nk > 1) {
+            issue_b(1);
+            LLMINT8_WAIT_BARRIER(8);
+        } else {
+            LLMINT8_WAIT_BARRIER(0);
+        }
+        read_frags(0, 0, fa[0], fb[0]);
+        for (int kt = 0; kt < nk; ++kt) {
+            // every wave passed the last barrier after reading the slots of stage kt-1:
+            // refill them with A[kt+1] and B[kt+2]
+            const bool more_a = kt + 1 < nk, more_b = kt + 2 < nk;
+            if (more_a) issue_a(kt + 1);
+            if (more_b) issue_b(kt + 2);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) b[j] = *(const v4i*)(Bs + rd + j * 16 * BK);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+            for (int u = 0; u < kSubSteps; ++u) {
+                const int cur = u & 1, nxt = cur ^ 1;
+                if (u + 1 < kSubSteps) {
+                    read_frags(kt, u + 1, fa[nxt], fb[nxt]);
+                } else if (more_a) {
+                    // A[kt+1] and B[kt+1] must have landed; B[kt+2] may stay in flight
+                    if (more_b) LLMINT8_WAIT_BARRIER(8);
+                    else LLMINT8_WAIT_BARRIER(0);
+                    read_frags(kt + 1, 0, fa[nxt], fb[nxt]);
+                }
+                mfma_all(fa[cur], fb[cur]);
+            }
         }
     }
 
-    // ---- 16-bit outlier product and epilogue, one 16-row slice at a time
+    // ---- 16-bit outlier product and epilogue, one 32-row slice at a time
     const int32_t nO = *p.n_out;
-    const int nchunk = (nO + 31) >> 5;
-    const int64_t wm0 = m0 + wm * 128, wn0 = n0 + wn * 128;
+    const int nsub = (nO + 15) >> 4;  // 16-deep MFMA steps over the padded outlier columns
+    const int64_t wm0 = m0 + wm * 128, wn0 = n0 + wn * (32 * NJ);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        v4f F[8];
+    for (int i = 0; i < 4; ++i) {
+        // lane holds column lane%32 and rows 8*(e/4) + 4*(lane/32) + e%4 (e = 0..15) of each 32x32 tile
+        const int64_t row0 = wm0 + 32 * i + 4 * h;
+        float r[16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) F[j] = v4f{0.f, 0.f, 0.f, 0.f};
-        for (int ch = 0; ch < nchunk; ++ch) {
-            int64_t am = wm0 + 16 * i + (lane & 15);
-            am = am < p.M ? am : p.M - 1;
-            const u32x4 a = *(const u32x4*)(p.XO + am * p.xo_pitch + ch * 32 + q * 8);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                int64_t bn = wn0 + 16 * j + (lane & 15);
-                bn = bn < p.N ? bn : p.N - 1;
-                const u32x4 b = *(const u32x4*)(p.WO + bn * p.xo_pitch + ch * 32 + q * 8);
-                F[j] = mfma16<DT>(a, b, F[j]);
-            }
+        for (int e = 0; e < 16; ++e) {
+            const int64_t m = row0 + 8 * (e >> 2) + (e & 3);
+            r[e] = m < p.M ? p.s_x[m] / 127.0f : 0.0f;
         }
-        // lane holds rows 16i + 4q + e (e = 0..3) and column lane%16 of each 16x16 tile
-        float r[4];
-        int64_t mrow[4];
+        int64_t am = wm0 + 32 * i + rl;
+        am = am < p.M ? am : p.M - 1;
+        const uint16_t* xo = p.XO + am * p.xo_pitch + h * 8;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            mrow[e] = wm0 + 16 * i + 4 * q + e;
-            r[e] = mrow[e] < p.M ? p.s_x[mrow[e]] / 127.0f : 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t n = wn0 + 16 * j + (lane & 15);
+        for (int j = 0; j < NJ; ++j) {
+            const int64_t n = wn0 + 32 * j + rl;
+            const int64_t bn = n < p.N ? n : p.N - 1;
+            const uint16_t* wo = p.WO + bn * p.xo_pitch + h * 8;
+            v16f F = v16f{};
+            for (int ch = 0; ch < nsub; ++ch)
+                F = mfma16<DT>(*(const u32x4*)(xo + ch * 16), *(const u32x4*)(wo + ch * 16), F);
             if (n >= p.N) continue;
             const float c = p.s_w[n] / 127.0f;
+            const int64_t lane_off = row0 * p.N + n;  // element (row0, n); row e adds a uniform multiple of N
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (mrow[e] >= p.M) continue;
+            for (int e = 0; e < 16; ++e) {
+                if (row0 + 8 * (e >> 2) + (e & 3) >= p.M) continue;
+                const int64_t off = lane_off + (int64_t)(8 * (e >> 2) + (e & 3)) * p.N;
                 if constexpr (ACC_OUT) {
-                    p.C_acc[mrow[e] * p.N + n] = acc[i][j][e];
-                    p.F_acc[mrow[e] * p.N + n] = F[j][e];
+                    p.C_acc[off] = acc[i][j][e];
+                    p.F_acc[off] = F[e];
                 } else {
                     const float yi = __fmul_rn(__fmul_rn((float)acc[i][j][e], r[e]), c);
-                    const float y = __fadd_rn(yi, __fmul_rn(c, F[j][e]));
-                    p.Y[mrow[e] * p.N + n] = from_f32<DT>(y);
+                    const float y = __fadd_rn(yi, __fmul_rn(c, F[e]));
+                    p.Y[off] = from_f32<DT>(y);
                 }
             }
         }

@@ -170,3 +170,17 @@ def test_full_size_workload_sampled(name):
     st = parity.run_case(x, w, wl.tau, rows=rows)
     assert st["n_outliers"] >= len(cols)
     print(f"[stats] {name}: {st}", flush=True)
+
+
+def test_two_stage_calls_equal_the_one_call():
+    _banner("prepare + products == int8_matmul")
+    x, w = _case(130, 512, 264, "bf16", n_out=3, seed=9)
+    Xd = x.cuda()
+    Wq, s_w = lm.int8_quantize_weight(w.cuda())
+    Y1 = lm.int8_matmul(Xd, Wq, s_w, 6.0)
+    ws = lm.int8_matmul_prepare(Xd, Wq, 6.0)
+    Y2 = lm.int8_matmul_products(130, 512, torch.bfloat16, Wq, s_w, ws)
+    Y3 = lm.int8_matmul_products(130, 512, torch.bfloat16, Wq, s_w, ws)  # the workspace is reusable
+    torch.cuda.synchronize()
+    assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+    assert torch.equal(Y1.view(torch.int16), Y3.view(torch.int16))
