@@ -138,7 +138,9 @@ int int8_matmul_products(int64_t M, int64_t K, int dtype, const int8_t* Wq, cons
  *   outliers  int32 [K]             O ascending (first n_O entries valid)
  *   xo        dtype [M][xo_pitch]   X[:, O] (first n_O columns; zero up to the next
  *                                   multiple of 32)
- *   wo        dtype [N][xo_pitch]   Wq[:, O] cast to dtype (same padding)
+ *   wo        dtype [N][xo_pitch]   Wq[:, O] cast to dtype (same padding); written only by
+ *                                   the tiled path (M > 64 or K > 32768) -- the small-batch
+ *                                   product kernel gathers these values itself
  *   scratch   internal (outlier flags)                                              */
 typedef struct {
     size_t xq, xq_pitch, s_x, n_outliers, outliers, xo, xo_pitch, wo, scratch, total;

@@ -83,12 +83,22 @@ int run_xpass(const void* X, int64_t M, int64_t K, int dtype, float tau, const i
     uint32_t* bitmap = (uint32_t*)(ws + L.bitmap);
     int32_t* O = (int32_t*)(ws + L.outliers);
     int32_t* nO = (int32_t*)(ws + L.n_outliers);
+    XPassArgs a;
+    a.dt = dtype;
+    a.X = X;
+    a.tau = tau;
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.Xq = ws + L.xq;
+    a.xq_pitch = (int64_t)L.xq_pitch;
+    a.s_x = (float*)(ws + L.s_x);
+    a.XO = ws + L.xo;
+    a.xo_pitch = (int64_t)L.xo_pitch;
+    if (small_batch(M, K)) return hip_status(launch_xpass_small(a, O, nO, bitmap, st));
     hipError_t e = launch_detect(dtype, X, M, K, tau, partial, st);
     if (e == hipSuccess) e = launch_compact(M, K, partial, bitmap, O, nO, st);
     if (e == hipSuccess) {
-        XPassArgs a;
-        a.dt = dtype;
-        a.X = X;
         a.M = M;
         a.K = K;
         a.N = N;
@@ -165,9 +175,11 @@ int products_common(int64_t M, int64_t K, int dtype, const int8_t* Wq, const flo
     g.WO = ws + L.wo;
     g.xo_pitch = (int64_t)L.xo_pitch;
     g.n_out = (const int32_t*)(ws + L.n_outliers);
+    g.O = (const int32_t*)(ws + L.outliers);
     g.Y = Y;
     g.C_acc = C;
     g.F_acc = F;
+    if (small_batch(M, K)) return hip_status(launch_gemm_small(g, (hipStream_t)stream));
     return hip_status(launch_gemm(g, (hipStream_t)stream));
 }
 

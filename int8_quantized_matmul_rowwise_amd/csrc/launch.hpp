@@ -21,9 +21,15 @@ hipError_t launch_detect(int dt, const void* X, int64_t M, int64_t K, float tau,
 hipError_t launch_compact(int64_t M, int64_t K, const uint32_t* partial, uint32_t* bitmap, int32_t* O,
                           int32_t* n_out, hipStream_t stream);
 
+// Small-batch path (two-launch X pass, split-N product kernel) for M <= kSmallM, K <= kSmallK.
+constexpr int64_t kSmallM = 64;
+constexpr int64_t kSmallK = 32768;
+inline bool small_batch(int64_t M, int64_t K) { return M <= kSmallM && K <= kSmallK; }
+
 struct XPassArgs {
     int dt;
     const void* X;
+    float tau;
     int64_t M, K, N;
     const uint32_t* bitmap;
     const int32_t* O;
@@ -37,6 +43,7 @@ struct XPassArgs {
     void* WO;
 };
 hipError_t launch_quantize_rows(const XPassArgs& a, hipStream_t stream);
+hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, uint32_t* bitmap, hipStream_t stream);
 
 // ---- products + epilogue
 struct GemmArgs {
@@ -51,10 +58,12 @@ struct GemmArgs {
     const void* WO;
     int64_t xo_pitch;
     const int32_t* n_out;
+    const int32_t* O;  // outlier columns (the small-batch kernel gathers Wq[:,O] itself)
     void* Y;          // product path
     int32_t* C_acc;   // accumulator dump (test hook); Y == NULL then
     float* F_acc;
 };
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_small(const GemmArgs& a, hipStream_t stream);
 
 }  // namespace llmint8

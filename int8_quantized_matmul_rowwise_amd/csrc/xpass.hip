@@ -274,3 +274,164 @@ hipError_t launch_quantize_rows(const XPassArgs& a, hipStream_t stream) {
 }
 
 }  // namespace llmint8
+
+// ---------------------------------------------------------------------------
+// The X pass for a small batch (M <= kSmallM rows, K <= kSmallK) in two launches:
+//   detect_direct: one thread per 8-column chunk scans all M rows and writes its bits of
+//     the bitmap directly (no row blocks, hence no partials and no compaction launch);
+//   code_rows_small: one workgroup per row holds the row in registers (K/8/256 <= 16
+//     chunks per thread), takes the max over the non-outlier columns, codes the row, and
+//     gathers X[i,O] by walking the bitmap with a block-wide scan of its popcounts (the
+//     rank of column j in O); workgroup 0 also writes O and n_O.
+namespace llmint8 {
+
+constexpr int kHold = 16;  // 16-byte chunks per thread held in registers (256 threads: K <= 32768)
+
+template <int DT>
+__global__ __launch_bounds__(256) void detect_direct_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                            float tau, uint32_t* __restrict__ bitmap) {
+    const int lane = threadIdx.x & 63;
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 8-column chunk
+    const int64_t nch = K / 8;
+    uint32_t mask = 0;
+    if (c < nch) {
+        const uint16_t* col = X + c * 8;
+        int64_t r = 0;
+        for (; r + 8 <= M; r += 8) {
+            u32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = *(const u32x4*)(col + (r + u) * K);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    mask |= (__builtin_fabsf(to_f32<DT>((uint16_t)(v[u][j >> 1] >> (16 * (j & 1))))) > tau ? 1u : 0u) << j;
+        }
+        for (; r < M; ++r) {
+            const u32x4 v = *(const u32x4*)(col + r * K);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                mask |= (__builtin_fabsf(to_f32<DT>((uint16_t)(v[j >> 1] >> (16 * (j & 1))))) > tau ? 1u : 0u) << j;
+        }
+    }
+    uint32_t word = mask << (8 * (lane & 3));
+    word |= __shfl_xor(word, 1, kWave);
+    word |= __shfl_xor(word, 2, kWave);
+    if ((lane & 3) == 0 && c < nch) bitmap[c >> 2] = word;  // K % 16 == 0: a word's chunks exist together
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void code_rows_small_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                              const uint32_t* __restrict__ bitmap,
+                                                              int32_t* __restrict__ O, int32_t* __restrict__ n_out,
+                                                              int8_t* __restrict__ Xq, int64_t xq_pitch,
+                                                              float* __restrict__ s_x, uint16_t* __restrict__ XO,
+                                                              int64_t xo_pitch) {
+    __shared__ uint32_t bits[kSmallK / 32];
+    __shared__ float red[4];
+    __shared__ int32_t wsum[4];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int64_t i = blockIdx.x;
+    const int64_t nch = K / 8, Kw = ceil_div(K, 32);
+    const uint16_t* row = X + i * K;
+
+    u32x4 v[kHold];
+#pragma unroll
+    for (int h = 0; h < kHold; ++h) {
+        const int64_t c = tid + 256 * h;
+        v[h] = c < nch ? *(const u32x4*)(row + c * 8) : u32x4{0u, 0u, 0u, 0u};
+    }
+    for (int64_t w = tid; w < Kw; w += 256) bits[w] = bitmap[w];
+    __syncthreads();
+
+    float m = 0.0f;
+#pragma unroll
+    for (int h = 0; h < kHold; ++h) {
+        const int64_t c = tid + 256 * h;
+        if (c >= nch) continue;
+        const uint32_t o = (bits[c >> 2] >> (8 * (c & 3))) & 0xffu;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float a = __builtin_fabsf(to_f32<DT>((uint16_t)(v[h][j >> 1] >> (16 * (j & 1)))));
+            if (!((o >> j) & 1u)) m = fmaxf(m, a);
+        }
+    }
+    m = wave_max(m);
+    if (lane == 0) red[wv] = m;
+    __syncthreads();
+    const float s = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float inv = inv_scale(s);
+    int8_t* qrow = Xq + i * xq_pitch;
+#pragma unroll
+    for (int h = 0; h < kHold; ++h) {
+        const int64_t c = tid + 256 * h;
+        if (c >= nch) continue;
+        const uint32_t o = (bits[c >> 2] >> (8 * (c & 3))) & 0xffu;
+        u32x2 packed = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float f = to_f32<DT>((uint16_t)(v[h][j >> 1] >> (16 * (j & 1))));
+            const int qv = ((o >> j) & 1u) ? 0 : quantize(f, inv);
+            packed[j >> 2] |= ((uint32_t)qv & 0xffu) << (8 * (j & 3));
+        }
+        *(u32x2*)(qrow + c * 8) = packed;
+    }
+    for (int64_t c = nch + tid; c < xq_pitch / 8; c += 256) *(u32x2*)(qrow + c * 8) = u32x2{0u, 0u};
+    if (tid == 0) s_x[i] = s;
+
+    // outlier gather: thread tid walks words [tid*wpt, (tid+1)*wpt); its first rank is the
+    // exclusive prefix of the popcounts before them
+    const int64_t wpt = ceil_div(Kw, 256);
+    int32_t cnt = 0;
+    for (int64_t w = tid * wpt; w < (tid + 1) * wpt && w < Kw; ++w) cnt += __popc(bits[w]);
+    int32_t incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t t = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += t;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int32_t pos = incl - cnt, total = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        pos += q < wv ? wsum[q] : 0;
+        total += wsum[q];
+    }
+    uint16_t* xo = XO + i * xo_pitch;
+    for (int64_t w = tid * wpt; w < (tid + 1) * wpt && w < Kw; ++w) {
+        uint32_t wd = bits[w];
+        while (wd) {
+            const int b = __ffs(wd) - 1;
+            const int64_t j = w * 32 + b;
+            xo[pos] = row[j];
+            if (i == 0) O[pos] = (int32_t)j;
+            ++pos;
+            wd &= wd - 1;
+        }
+    }
+    const int32_t P = (total + 31) & ~31;
+    for (int64_t t = total + tid; t < P; t += 256) xo[t] = 0;
+    if (i == 0 && tid == 0) *n_out = total;
+}
+
+hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, uint32_t* bitmap, hipStream_t stream) {
+    const unsigned g1 = (unsigned)ceil_div(a.K / 8, 256);
+    if (a.K > 0) {
+        if (a.dt == F16) detect_direct_kernel<F16><<<g1, 256, 0, stream>>>((const uint16_t*)a.X, a.M, a.K, a.tau, bitmap);
+        else detect_direct_kernel<BF16><<<g1, 256, 0, stream>>>((const uint16_t*)a.X, a.M, a.K, a.tau, bitmap);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (a.dt == F16)
+        code_rows_small_kernel<F16><<<(unsigned)a.M, 256, 0, stream>>>((const uint16_t*)a.X, a.M, a.K, bitmap, O, n_out,
+                                                                        a.Xq, a.xq_pitch, a.s_x, (uint16_t*)a.XO,
+                                                                        a.xo_pitch);
+    else
+        code_rows_small_kernel<BF16><<<(unsigned)a.M, 256, 0, stream>>>((const uint16_t*)a.X, a.M, a.K, bitmap, O,
+                                                                         n_out, a.Xq, a.xq_pitch, a.s_x,
+                                                                         (uint16_t*)a.XO, a.xo_pitch);
+    return hipGetLastError();
+}
+
+}  // namespace llmint8

@@ -44,6 +44,7 @@ def test_ragged_medium(dt):
 
 
 @pytest.mark.parametrize("M,K,N,dt", [(1, 16, 8, "fp16"), (1, 4096, 264, "bf16"), (16, 8192, 512, "bf16"),
+                                      (64, 1040, 264, "fp16"), (65, 1040, 264, "bf16"), (33, 32784, 24, "fp16"),
                                       (257, 272, 264, "fp16"), (513, 128, 8, "bf16"), (7, 32, 1032, "fp16")])
 def test_edge_shapes(M, K, N, dt):
     _banner(f"edge {M}x{K}x{N} {dt}")
@@ -63,10 +64,11 @@ def test_threshold_exactly_tau_is_not_an_outlier(dt):
 
 
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
-def test_tau_zero_every_column_is_an_outlier(dt):
+@pytest.mark.parametrize("M", [40, 130])  # small-batch path and tiled path
+def test_tau_zero_every_column_is_an_outlier(dt, M):
     # the degenerate 16-bit path: n_O = K (nine 32-wide chunks), C = 0, s_x = 0
-    _banner(f"tau=0 {dt}")
-    x, w = _case(40, 272, 72, dt, n_out=0, seed=4)
+    _banner(f"tau=0 {dt} M={M}")
+    x, w = _case(M, 272, 72, dt, n_out=0, seed=4)
     st = parity.run_case(x, w, 0.0)
     assert st["n_outliers"] == 272
 
@@ -90,12 +92,13 @@ def test_zero_rows_and_zero_weight_columns():
 
 
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
-def test_lattice_closed_form_exact_on_gpu(dt):
+@pytest.mark.parametrize("M", [13, 70])  # small-batch path and tiled path
+def test_lattice_closed_form_exact_on_gpu(dt, M):
     # power-of-two lattice: every step is exact, so Y must equal RN_T(exact) bitwise,
     # outlier part included (its sums are exact integers in any order)
-    _banner(f"lattice {dt}")
+    _banner(f"lattice {dt} M={M}")
     for seed in range(4):
-        xl, wl_, tau, exact, cols = _lattice_case(dt, seed, M=70, K=320, N=136, out_cols=(3, 20, 41, 300))
+        xl, wl_, tau, exact, cols = _lattice_case(dt, seed, M=M, K=320, N=136, out_cols=(3, 20, 41, 300))
         X = workloads.from_bits(bits_of(xl, dt), dt)
         W = workloads.from_bits(bits_of(wl_, dt), dt)
         Wq, s_w = lm.int8_quantize_weight(W.cuda())
