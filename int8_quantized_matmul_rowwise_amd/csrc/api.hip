@@ -112,7 +112,7 @@ int run_xpass(const void* X, int64_t M, int64_t K, int dtype, float tau, const i
         a.xo_pitch = (int64_t)L.xo_pitch;
         a.Wq = Wq;
         a.WO = ws + L.wo;
-        e = launch_quantize_rows(a, st);
+        e = launch_code_rows(a, bitmap, O, nO, st);
     }
     return hip_status(e);
 }

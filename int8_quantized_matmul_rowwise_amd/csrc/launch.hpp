@@ -42,7 +42,8 @@ struct XPassArgs {
     const int8_t* Wq;  // NULL: no W_O gather
     void* WO;
 };
-hipError_t launch_quantize_rows(const XPassArgs& a, hipStream_t stream);
+hipError_t launch_code_rows(const XPassArgs& a, const uint32_t* bitmap, int32_t* O, int32_t* n_out,
+                            hipStream_t stream);
 hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, uint32_t* bitmap, hipStream_t stream);
 
 // ---- products + epilogue

@@ -31,12 +31,12 @@ __global__ __launch_bounds__(256) void detect_kernel(const uint16_t* __restrict_
     if (chunk < nchunks) {
         const uint16_t* col = X + chunk * 8;
         int64_t r = r0 + w;
-        for (; r + 12 < r1; r += 16) {  // four rows in flight per thread
-            u32x4 v[4];
+        for (; r + 28 < r1; r += 32) {  // eight rows in flight per thread
+            u32x4 v[8];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = *(const u32x4*)(col + (r + 4 * u) * K);
+            for (int u = 0; u < 8; ++u) v[u] = *(const u32x4*)(col + (r + 4 * u) * K);
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
+            for (int u = 0; u < 8; ++u)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     uint16_t h = (uint16_t)(v[u][j >> 1] >> (16 * (j & 1)));
@@ -66,27 +66,44 @@ __global__ __launch_bounds__(256) void detect_kernel(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Compact (one workgroup of 1024 threads): OR the row-block partials into the
-// bitmap, then list the set bits in ascending column order (block-wide exclusive scan
-// of per-word popcounts), and store n_O.
+// Compact (one workgroup of 1024 threads): OR the row-block partials into an LDS bitmap
+// (coalesced, independent loads; LDS atomics), store the bitmap, then list the set bits in
+// ascending column order (block-wide exclusive scan of per-word popcounts), and store n_O.
+constexpr int64_t kMaxKw = (133143 + 31) / 32 + 1;
+
 __global__ __launch_bounds__(1024) void compact_kernel(const uint32_t* __restrict__ partial, int64_t n_rb, int64_t Kw,
                                                        uint32_t* __restrict__ bitmap, int32_t* __restrict__ O,
                                                        int32_t* __restrict__ n_out) {
+    __shared__ uint32_t bits[kMaxKw];
     __shared__ int32_t wsum[16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    for (int64_t w = tid; w < Kw; w += 1024) bits[w] = 0;
+    __syncthreads();
+    const int64_t total_entries = n_rb * Kw;
+    for (int64_t e0 = tid; e0 < total_entries; e0 += 8 * 1024) {
+        uint32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t e = e0 + (int64_t)u * 1024;
+            v[u] = e < total_entries ? partial[e] : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t e = e0 + (int64_t)u * 1024;
+            if (v[u]) atomicOr(&bits[e % Kw], v[u]);
+        }
+    }
+    __syncthreads();
     int32_t base = 0;
     for (int64_t w0 = 0; w0 < Kw; w0 += 1024) {
         const int64_t wi = w0 + tid;
-        uint32_t word = 0;
-        if (wi < Kw) {
-            for (int64_t b = 0; b < n_rb; ++b) word |= partial[b * Kw + wi];
-            bitmap[wi] = word;
-        }
+        const uint32_t word = wi < Kw ? bits[wi] : 0u;
+        if (wi < Kw) bitmap[wi] = word;
         const int32_t cnt = __popc(word);
         int32_t incl = cnt;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
-            int32_t t = __shfl_up(incl, off, kWave);
+            const int32_t t = __shfl_up(incl, off, kWave);
             if (lane >= off) incl += t;
         }
         if (lane == 63) wsum[wv] = incl;
@@ -94,9 +111,9 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint32_t* __restric
         int32_t before = 0, total = 0;
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
-            const int32_t s = wsum[q];
-            before += q < wv ? s : 0;
-            total += s;
+            const int32_t sq = wsum[q];
+            before += q < wv ? sq : 0;
+            total += sq;
         }
         int32_t pos = base + before + incl - cnt;
         uint32_t wd = word;
@@ -109,111 +126,6 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint32_t* __restric
         __syncthreads();  // wsum is reused by the next chunk of words
     }
     if (tid == 0) *n_out = base;
-}
-
-// ---------------------------------------------------------------------------
-// Code the rows (blocks 0..M-1, one row each) and gather the outlier operands of W
-// (blocks M.., 64 rows of Wq each).
-//   s_x[i] = max over non-outlier j of |X[i,j]|;  Xq[i,j] = 0 for j in O, else the
-//   vector-wise code;  Xq[i, K..pitch) = 0;  XO[i,t] = X[i,O[t]] for t < n_O and 0 up to
-//   the next multiple of 32.
-//   WO[n,t] = (dtype) Wq[n, O[t]] (exact), same padding.
-// CH: 8-element chunks held per thread (row kept in registers between the max and the
-// coding); CH == 0 is the general form that reads the row twice (second read from L2).
-template <int DT, int CH>
-__global__ __launch_bounds__(256) void quantize_rows_kernel(
-    const uint16_t* __restrict__ X, int64_t M, int64_t K, const uint32_t* __restrict__ bitmap,
-    const int32_t* __restrict__ O, const int32_t* __restrict__ n_out, int8_t* __restrict__ Xq, int64_t xq_pitch,
-    float* __restrict__ s_x, uint16_t* __restrict__ XO, int64_t xo_pitch, const int8_t* __restrict__ Wq,
-    int64_t N, uint16_t* __restrict__ WO) {
-    const int tid = threadIdx.x;
-    const int32_t nO = *n_out;
-    const int32_t P = (nO + 31) & ~31;
-    const int64_t b = blockIdx.x;
-
-    if (b >= M) {
-        const int64_t n0 = (b - M) * 64;
-        for (int64_t idx = tid; idx < 64 * (int64_t)P; idx += 256) {
-            const int64_t r = idx / P, t = idx % P;
-            const int64_t n = n0 + r;
-            if (n < N) {
-                uint16_t v = 0;
-                if (t < nO) v = from_f32<DT>((float)Wq[n * K + O[t]]);
-                WO[n * xo_pitch + t] = v;
-            }
-        }
-        return;
-    }
-
-    const int64_t i = b;
-    const uint16_t* row = X + i * K;
-    const int64_t nch = K / 8;
-    __shared__ float red[4];
-
-    float m = 0.0f;
-    u32x4 v[CH > 0 ? CH : 1];
-    uint32_t om[CH > 0 ? CH : 1];
-    if constexpr (CH > 0) {
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int64_t ch = tid + (int64_t)c * 256;
-            om[c] = 0xffu;
-            if (ch < nch) {
-                v[c] = *(const u32x4*)(row + ch * 8);
-                om[c] = (bitmap[ch >> 2] >> (8 * (ch & 3))) & 0xffu;
-            }
-        }
-#pragma unroll
-        for (int c = 0; c < CH; ++c)
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float a = __builtin_fabsf(to_f32<DT>((uint16_t)(v[c][j >> 1] >> (16 * (j & 1)))));
-                if (!((om[c] >> j) & 1u)) m = fmaxf(m, a);
-            }
-    } else {
-        for (int64_t ch = tid; ch < nch; ch += 256) {
-            const u32x4 x = *(const u32x4*)(row + ch * 8);
-            const uint32_t o = (bitmap[ch >> 2] >> (8 * (ch & 3))) & 0xffu;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float a = __builtin_fabsf(to_f32<DT>((uint16_t)(x[j >> 1] >> (16 * (j & 1)))));
-                if (!((o >> j) & 1u)) m = fmaxf(m, a);
-            }
-        }
-    }
-    m = wave_max(m);
-    if ((tid & 63) == 0) red[tid >> 6] = m;
-    __syncthreads();
-    const float s = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float inv = inv_scale(s);
-
-    auto code8 = [&](const u32x4& x, uint32_t o) -> u32x2 {
-        u32x2 packed = {0u, 0u};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float f = to_f32<DT>((uint16_t)(x[j >> 1] >> (16 * (j & 1))));
-            const int q = ((o >> j) & 1u) ? 0 : quantize(f, inv);
-            packed[j >> 2] |= ((uint32_t)q & 0xffu) << (8 * (j & 3));
-        }
-        return packed;
-    };
-    int8_t* qrow = Xq + i * xq_pitch;
-    if constexpr (CH > 0) {
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-            const int64_t ch = tid + (int64_t)c * 256;
-            if (ch < nch) *(u32x2*)(qrow + ch * 8) = code8(v[c], om[c]);
-        }
-    } else {
-        for (int64_t ch = tid; ch < nch; ch += 256) {
-            const u32x4 x = *(const u32x4*)(row + ch * 8);
-            const uint32_t o = (bitmap[ch >> 2] >> (8 * (ch & 3))) & 0xffu;
-            *(u32x2*)(qrow + ch * 8) = code8(x, o);
-        }
-    }
-    for (int64_t ch = nch + tid; ch < xq_pitch / 8; ch += 256) *(u32x2*)(qrow + ch * 8) = u32x2{0u, 0u};
-    if (tid == 0) s_x[i] = s;
-    for (int64_t t = tid; t < P; t += 256) XO[i * xo_pitch + t] = t < nO ? row[O[t]] : (uint16_t)0;
 }
 
 // ---------------------------------------------------------------------------
@@ -246,43 +158,14 @@ hipError_t launch_compact(int64_t M, int64_t K, const uint32_t* partial, uint32_
     return hipGetLastError();
 }
 
-template <int DT, int CH>
-static void quantize_rows_dispatch(dim3 grid, hipStream_t stream, const XPassArgs& a) {
-    quantize_rows_kernel<DT, CH><<<grid, 256, 0, stream>>>(
-        (const uint16_t*)a.X, a.M, a.K, a.bitmap, a.O, a.n_out, a.Xq, a.xq_pitch, a.s_x, (uint16_t*)a.XO,
-        a.xo_pitch, a.Wq, a.N, (uint16_t*)a.WO);
-}
-
-template <int DT>
-static void quantize_rows_pick(dim3 grid, hipStream_t stream, const XPassArgs& a) {
-    const int64_t per_thread = ceil_div(a.K / 8, 256);
-    if (per_thread <= 1) quantize_rows_dispatch<DT, 1>(grid, stream, a);
-    else if (per_thread <= 2) quantize_rows_dispatch<DT, 2>(grid, stream, a);
-    else if (per_thread <= 4) quantize_rows_dispatch<DT, 4>(grid, stream, a);
-    else if (per_thread <= 8) quantize_rows_dispatch<DT, 8>(grid, stream, a);
-    else if (per_thread <= 16) quantize_rows_dispatch<DT, 16>(grid, stream, a);
-    else quantize_rows_dispatch<DT, 0>(grid, stream, a);
-}
-
-hipError_t launch_quantize_rows(const XPassArgs& a, hipStream_t stream) {
-    const int64_t nblk = a.M + (a.Wq ? ceil_div(a.N, 64) : 0);
-    if (nblk == 0) return hipSuccess;
-    dim3 grid((unsigned)nblk);
-    if (a.dt == F16) quantize_rows_pick<F16>(grid, stream, a);
-    else quantize_rows_pick<BF16>(grid, stream, a);
-    return hipGetLastError();
-}
-
 }  // namespace llmint8
 
 // ---------------------------------------------------------------------------
-// The X pass for a small batch (M <= kSmallM rows, K <= kSmallK) in two launches:
-//   detect_direct: one thread per 8-column chunk scans all M rows and writes its bits of
-//     the bitmap directly (no row blocks, hence no partials and no compaction launch);
-//   code_rows_small: one workgroup per row holds the row in registers (K/8/256 <= 16
-//     chunks per thread), takes the max over the non-outlier columns, codes the row, and
-//     gathers X[i,O] by walking the bitmap with a block-wide scan of its popcounts (the
-//     rank of column j in O); workgroup 0 also writes O and n_O.
+// Row coding (both paths) and the small-batch detection.  A small batch (M <= kSmallM
+// rows, K <= kSmallK) takes two launches: detect_direct -- one thread per 8-column chunk
+// scans all M rows and writes its bits of the bitmap directly (no row blocks, hence no
+// partials and no compaction launch) -- then code_rows, whose workgroup 0 also writes O
+// and n_O.  The tiled path runs detect (row-block partials), compact, then code_rows.
 namespace llmint8 {
 
 constexpr int kHold = 16;  // 16-byte chunks per thread held in registers (256 threads: K <= 32768)
@@ -320,41 +203,80 @@ __global__ __launch_bounds__(256) void detect_direct_kernel(const uint16_t* __re
     if ((lane & 3) == 0 && c < nch) bitmap[c >> 2] = word;  // K % 16 == 0: a word's chunks exist together
 }
 
-template <int DT>
-__global__ __launch_bounds__(256) void code_rows_small_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
-                                                              const uint32_t* __restrict__ bitmap,
-                                                              int32_t* __restrict__ O, int32_t* __restrict__ n_out,
-                                                              int8_t* __restrict__ Xq, int64_t xq_pitch,
-                                                              float* __restrict__ s_x, uint16_t* __restrict__ XO,
-                                                              int64_t xo_pitch) {
-    __shared__ uint32_t bits[kSmallK / 32];
+// Code the rows: workgroup i < M takes row i.  s_x[i] = max over the non-outlier columns
+// of |X[i,j]|; Xq[i,j] = 0 for j in O, else the vector-wise code; Xq[i, K..pitch) = 0;
+// XO[i,t] = X[i, O[t]] for t < n_O, 0 up to the next multiple of 32 (the rank t of column j
+// comes from a block-wide scan of the bitmap's popcounts).  HOLD: the row stays in
+// registers between the max and the coding (K <= 32768), else it is read twice.
+// Workgroups M.. gather WO[n,t] = (dtype) Wq[n, O[t]] (exact; same padding), 64 rows of Wq
+// each, from the O written by the compaction.  WRITE_O: workgroup 0 writes O and n_O (the
+// small-batch path has no compaction launch).
+template <int DT, bool HOLD, bool WRITE_O>
+__global__ __launch_bounds__(256) void code_rows_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                        const uint32_t* __restrict__ bitmap, int32_t* __restrict__ O,
+                                                        int32_t* __restrict__ n_out, int8_t* __restrict__ Xq,
+                                                        int64_t xq_pitch, float* __restrict__ s_x,
+                                                        uint16_t* __restrict__ XO, int64_t xo_pitch,
+                                                        const int8_t* __restrict__ Wq, int64_t N,
+                                                        uint16_t* __restrict__ WO) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if ((int64_t)blockIdx.x >= M) {
+        const int32_t nO = *n_out;
+        const int32_t P = (nO + 31) & ~31;
+        const int64_t n0 = ((int64_t)blockIdx.x - M) * 64;
+        for (int64_t idx = tid; idx < 64 * (int64_t)P; idx += 256) {
+            const int64_t r = idx / P, t = idx % P;
+            const int64_t n = n0 + r;
+            if (n < N) WO[n * xo_pitch + t] = t < nO ? from_f32<DT>((float)Wq[n * K + O[t]]) : (uint16_t)0;
+        }
+        return;
+    }
+    __shared__ uint32_t bits[kMaxKw];
     __shared__ float red[4];
     __shared__ int32_t wsum[4];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int64_t i = blockIdx.x;
     const int64_t nch = K / 8, Kw = ceil_div(K, 32);
     const uint16_t* row = X + i * K;
-
-    u32x4 v[kHold];
+    constexpr int H = HOLD ? kHold : 1;
+    u32x4 v[H];
+    if constexpr (HOLD) {
 #pragma unroll
-    for (int h = 0; h < kHold; ++h) {
-        const int64_t c = tid + 256 * h;
-        v[h] = c < nch ? *(const u32x4*)(row + c * 8) : u32x4{0u, 0u, 0u, 0u};
+        for (int h = 0; h < kHold; ++h) {
+            const int64_t c = tid + 256 * h;
+            v[h] = c < nch ? *(const u32x4*)(row + c * 8) : u32x4{0u, 0u, 0u, 0u};
+        }
     }
     for (int64_t w = tid; w < Kw; w += 256) bits[w] = bitmap[w];
     __syncthreads();
-
-    float m = 0.0f;
-#pragma unroll
-    for (int h = 0; h < kHold; ++h) {
-        const int64_t c = tid + 256 * h;
-        if (c >= nch) continue;
-        const uint32_t o = (bits[c >> 2] >> (8 * (c & 3))) & 0xffu;
+    auto obits = [&](int64_t c) { return (bits[c >> 2] >> (8 * (c & 3))) & 0xffu; };
+    auto absmax8 = [&](const u32x4& x, uint32_t o, float m) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float a = __builtin_fabsf(to_f32<DT>((uint16_t)(v[h][j >> 1] >> (16 * (j & 1)))));
+            const float a = __builtin_fabsf(to_f32<DT>((uint16_t)(x[j >> 1] >> (16 * (j & 1)))));
             if (!((o >> j) & 1u)) m = fmaxf(m, a);
         }
+        return m;
+    };
+    auto code8 = [&](const u32x4& x, uint32_t o, float inv) -> u32x2 {
+        u32x2 packed = {0u, 0u};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float f = to_f32<DT>((uint16_t)(x[j >> 1] >> (16 * (j & 1))));
+            const int qv = ((o >> j) & 1u) ? 0 : quantize(f, inv);
+            packed[j >> 2] |= ((uint32_t)qv & 0xffu) << (8 * (j & 3));
+        }
+        return packed;
+    };
+
+    float m = 0.0f;
+    if constexpr (HOLD) {
+#pragma unroll
+        for (int h = 0; h < kHold; ++h) {
+            const int64_t c = tid + 256 * h;
+            if (c < nch) m = absmax8(v[h], obits(c), m);
+        }
+    } else {
+        for (int64_t c = tid; c < nch; c += 256) m = absmax8(*(const u32x4*)(row + c * 8), obits(c), m);
     }
     m = wave_max(m);
     if (lane == 0) red[wv] = m;
@@ -362,19 +284,14 @@ __global__ __launch_bounds__(256) void code_rows_small_kernel(const uint16_t* __
     const float s = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float inv = inv_scale(s);
     int8_t* qrow = Xq + i * xq_pitch;
+    if constexpr (HOLD) {
 #pragma unroll
-    for (int h = 0; h < kHold; ++h) {
-        const int64_t c = tid + 256 * h;
-        if (c >= nch) continue;
-        const uint32_t o = (bits[c >> 2] >> (8 * (c & 3))) & 0xffu;
-        u32x2 packed = {0u, 0u};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float f = to_f32<DT>((uint16_t)(v[h][j >> 1] >> (16 * (j & 1))));
-            const int qv = ((o >> j) & 1u) ? 0 : quantize(f, inv);
-            packed[j >> 2] |= ((uint32_t)qv & 0xffu) << (8 * (j & 3));
+        for (int h = 0; h < kHold; ++h) {
+            const int64_t c = tid + 256 * h;
+            if (c < nch) *(u32x2*)(qrow + c * 8) = code8(v[h], obits(c), inv);
         }
-        *(u32x2*)(qrow + c * 8) = packed;
+    } else {
+        for (int64_t c = tid; c < nch; c += 256) *(u32x2*)(qrow + c * 8) = code8(*(const u32x4*)(row + c * 8), obits(c), inv);
     }
     for (int64_t c = nch + tid; c < xq_pitch / 8; c += 256) *(u32x2*)(qrow + c * 8) = u32x2{0u, 0u};
     if (tid == 0) s_x[i] = s;
@@ -405,32 +322,50 @@ __global__ __launch_bounds__(256) void code_rows_small_kernel(const uint16_t* __
             const int b = __ffs(wd) - 1;
             const int64_t j = w * 32 + b;
             xo[pos] = row[j];
-            if (i == 0) O[pos] = (int32_t)j;
+            if (WRITE_O && i == 0) O[pos] = (int32_t)j;
             ++pos;
             wd &= wd - 1;
         }
     }
     const int32_t P = (total + 31) & ~31;
     for (int64_t t = total + tid; t < P; t += 256) xo[t] = 0;
-    if (i == 0 && tid == 0) *n_out = total;
+    if (WRITE_O && i == 0 && tid == 0) *n_out = total;
 }
 
+template <int DT, bool WRITE_O>
+static void code_rows_launch(unsigned grid, const XPassArgs& a, const uint32_t* bitmap, int32_t* O, int32_t* n_out,
+                             hipStream_t stream) {
+    if (a.K <= kSmallK)
+        code_rows_kernel<DT, true, WRITE_O><<<grid, 256, 0, stream>>>(
+            (const uint16_t*)a.X, a.M, a.K, bitmap, O, n_out, a.Xq, a.xq_pitch, a.s_x, (uint16_t*)a.XO, a.xo_pitch,
+            a.Wq, a.N, (uint16_t*)a.WO);
+    else
+        code_rows_kernel<DT, false, WRITE_O><<<grid, 256, 0, stream>>>(
+            (const uint16_t*)a.X, a.M, a.K, bitmap, O, n_out, a.Xq, a.xq_pitch, a.s_x, (uint16_t*)a.XO, a.xo_pitch,
+            a.Wq, a.N, (uint16_t*)a.WO);
+}
+
+// Big path: after detect + compact (which wrote the bitmap, O and n_O).
+hipError_t launch_code_rows(const XPassArgs& a, const uint32_t* bitmap, int32_t* O, int32_t* n_out,
+                            hipStream_t stream) {
+    const int64_t nblk = a.M + (a.Wq ? ceil_div(a.N, 64) : 0);
+    if (nblk == 0) return hipSuccess;
+    if (a.dt == F16) code_rows_launch<F16, false>((unsigned)nblk, a, bitmap, O, n_out, stream);
+    else code_rows_launch<BF16, false>((unsigned)nblk, a, bitmap, O, n_out, stream);
+    return hipGetLastError();
+}
+
+// Small-batch path: direct detect, then the row coding also writes O and n_O.
 hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, uint32_t* bitmap, hipStream_t stream) {
-    const unsigned g1 = (unsigned)ceil_div(a.K / 8, 256);
     if (a.K > 0) {
+        const unsigned g1 = (unsigned)ceil_div(a.K / 8, 256);
         if (a.dt == F16) detect_direct_kernel<F16><<<g1, 256, 0, stream>>>((const uint16_t*)a.X, a.M, a.K, a.tau, bitmap);
         else detect_direct_kernel<BF16><<<g1, 256, 0, stream>>>((const uint16_t*)a.X, a.M, a.K, a.tau, bitmap);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (a.dt == F16)
-        code_rows_small_kernel<F16><<<(unsigned)a.M, 256, 0, stream>>>((const uint16_t*)a.X, a.M, a.K, bitmap, O, n_out,
-                                                                        a.Xq, a.xq_pitch, a.s_x, (uint16_t*)a.XO,
-                                                                        a.xo_pitch);
-    else
-        code_rows_small_kernel<BF16><<<(unsigned)a.M, 256, 0, stream>>>((const uint16_t*)a.X, a.M, a.K, bitmap, O,
-                                                                         n_out, a.Xq, a.xq_pitch, a.s_x,
-                                                                         (uint16_t*)a.XO, a.xo_pitch);
+    if (a.dt == F16) code_rows_launch<F16, true>((unsigned)a.M, a, bitmap, O, n_out, stream);
+    else code_rows_launch<BF16, true>((unsigned)a.M, a, bitmap, O, n_out, stream);
     return hipGetLastError();
 }
 
