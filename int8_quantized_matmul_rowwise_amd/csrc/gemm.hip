@@ -13,18 +13,22 @@
 //   MFMA sustains the full int8 rate; the 16x16x64 form issues at about half of it.)
 //   Operands go HBM/L2 -> LDS with global_load_lds (16 B per lane, no register
 //   staging), one 128-byte line per row per K stage (full-line requests).  The LDS
-//   holds 2 A slots and 3 B slots of 32 KB: at the start of stage k the loads of A[k+1]
-//   and B[k+2] are issued, so the weight lines -- the ones that miss L2 -- get two
-//   stages to arrive.  Waits are counted (vmcnt) and the workgroup barrier is a bare
-//   s_barrier, so a barrier never drains the loads still in flight.  Each stage is
-//   four 32-deep MFMA sub-steps; the operands of the next sub-step are read from LDS
-//   into a second register set while the 16 MFMAs of the current one run.  The
+//   holds 2 A slots and 3 B slots of 32 KB: during stage k the loads of A[k+1] and
+//   B[k+2] are issued, so the weight lines get two stages to arrive.  Waits are counted
+//   (vmcnt) and the workgroup barrier is a bare s_barrier, so a barrier never drains the
+//   loads still in flight.  Each stage is four 32-deep MFMA sub-steps; the operands of
+//   the next sub-step are read from LDS into a second register set while the 16 MFMAs
+//   of the current one run.  The instruction order inside a sub-step (global loads and
+//   LDS reads front-loaded between the MFMAs) is pinned with scheduling-group hints, and
+//   each sub-step begins with an LDS wait that costs nothing.  The
 //   16-byte chunk c of LDS row r sits at chunk c ^ (r & 7) ^ ((r >> 3) & 1), so the
 //   ds_read_b128 of 16 consecutive rows at one k hit distinct banks (for both 8- and
 //   16-lane service groups).
 //   Tiles are assigned so that the workgroups the dispatcher places on one XCD (ids
 //   congruent mod 8) take a contiguous run of tiles in grouped order (8 row-tiles per
 //   group): the 32 tiles running together on an XCD share A and B panels in its L2.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -58,9 +62,14 @@ __device__ __forceinline__ void load_lds16(const void* g, int8_t* lds_base) {
 // the ds_read_b128 of 16 consecutive rows at one chunk touch distinct banks.
 __host__ __device__ constexpr int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
-// Wait until at most N of this wave's direct-to-LDS loads are in flight and its LDS
-// reads are done, then the workgroup barrier (no fence: later loads stay in flight).
-#define LLMINT8_WAIT_BARRIER(N) asm volatile("s_waitcnt vmcnt(" #N ") lgkmcnt(0)\n\ts_barrier" ::: "memory")
+// Wait until this wave's LDS reads are done (a builtin, so the compiler knows) and at most
+// N of its direct-to-LDS loads are in flight, then the workgroup barrier (no fence: later
+// loads stay in flight).  0xC07F: s_waitcnt lgkmcnt(0) with vmcnt and expcnt unconstrained.
+#define LLMINT8_WAIT_BARRIER(N)                                  \
+    do {                                                         \
+        __builtin_amdgcn_s_waitcnt(0xC07F);                      \
+        asm volatile("s_waitcnt vmcnt(" #N ")\n\ts_barrier" ::: "memory"); \
+    } while (0)
 
 struct Params {
     const int8_t* Xq;
@@ -129,36 +138,30 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
     const int8_t* a_tile = p.Xq + m0 * p.xq_pitch;
     const int8_t* b_tile = p.Wq + n0 * p.K;
     const int nk = (int)ceil_div(p.K, BK);
-    const bool k_tail = (p.K % BK) != 0;
 
     auto slot_a = [&](int kt) { return smem + (kt % kSlotsA) * kTileBytes; };
     auto slot_b = [&](int kt) { return smem + kSlotsA * kTileBytes + (kt % kSlotsB) * kSlotBytesB; };
-    auto stage_k = [](int kt) { return kt * BK; };
     auto issue_a = [&](int kt) {
         int8_t* As = slot_a(kt);
-        const int kb = stage_k(kt);
+        const int kb = kt * BK;
 #pragma unroll
         for (int j = 0; j < kLoadsA; ++j) load_lds16(a_tile + kb + a_off[j], As + (kLoadsA * wu + j) * 1024);
     };
+    // Chunks past K (a partial last stage) read the row start instead: their A side is zero.
+    // Written branch-free so that a stage of the main loop is one scheduling region.
     auto issue_b = [&](int kt) {
         int8_t* Bs = slot_b(kt);
-        const int kb = stage_k(kt);
-        if (!k_tail || kb + BK <= p.K) {
+        const int kb = kt * BK;
 #pragma unroll
-            for (int j = 0; j < kLoadsB; ++j) load_lds16(b_tile + kb + b_off[j], Bs + (kLoadsB * wu + j) * 1024);
-        } else {
-            // the partial K stage: chunks past K read the row start instead (their A side is zero)
-#pragma unroll
-            for (int j = 0; j < kLoadsB; ++j) {
-                const int kk = kb + cb_ld[j] * 16;
-                load_lds16(b_tile + b_off[j] - cb_ld[j] * 16 + (kk < p.K ? kk : 0), Bs + (kLoadsB * wu + j) * 1024);
-            }
+        for (int j = 0; j < kLoadsB; ++j) {
+            const int kk = kb + cb_ld[j] * 16;
+            load_lds16(b_tile + b_off[j] - cb_ld[j] * 16 + (kk < p.K ? kk : 0), Bs + (kLoadsB * wu + j) * 1024);
         }
     };
 
     // ---- MFMA operand reads (32x32x32: lane holds row lane%32, 16 k at 16*(lane/32)):
     // fragment i of sub-step u reads row 32*i + lane%32 of the wave's 128-row panel,
-    // logical chunk 2u + lane/32.
+    // logical chunk 2u + lane/32.  Read in the order the MFMAs consume them.
     const int rl = lane & 31, h = lane >> 5;
     int rd[kSubSteps];
 #pragma unroll
@@ -166,10 +169,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
     auto read_frags = [&](int kt, int u, v4i (&fa)[4], v4i (&fb)[NJ]) {
         const int8_t* As = slot_a(kt) + wm * 128 * BK + rd[u];
         const int8_t* Bs = slot_b(kt) + wn * (32 * NJ) * BK + rd[u];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) fa[i] = *(const v4i*)(As + i * 32 * BK);
+        fa[0] = *(const v4i*)As;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) fb[j] = *(const v4i*)(Bs + j * 32 * BK);
+#pragma unroll
+        for (int i = 1; i < 4; ++i) fa[i] = *(const v4i*)(As + i * 32 * BK);
     };
 
     v16i acc[4][NJ];
@@ -178,17 +182,66 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = v16i{};
 
-    auto mfma_all = [&](const v4i (&fa)[4], const v4i (&fb)[NJ]) {
+    auto mfma_rows = [&](const v4i (&fa)[4], const v4i (&fb)[NJ], int i0, int i1) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = i0; i < i1; ++i)
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
     };
 
+    // One K stage.  Sub-steps 0..2 run their 16 MFMAs while the LDS reads of the next
+    // sub-step (and, in 0 and 1, the global loads of A[kt+1] and B[kt+2], into the slots
+    // stage kt-1 freed) are interleaved, front-loaded so they have most of the sub-step to
+    // land.  Sub-step 3 runs 4 MFMAs, waits for A[kt+1] and B[kt+1] and meets the other
+    // waves at the barrier, then reads stage kt+1's first operands under its other 12.
+    // Each sub-step is fenced (sched_barrier) so that the interleave stays inside it.
+    // STEADY: B[kt+2] exists (every stage but the last two).
+    v4i fa[2][4], fb[2][NJ];  // operand sets of the current / next sub-step
+    auto stage = [&](int kt, auto steady_tag) {
+        constexpr bool STEADY = decltype(steady_tag)::value;
+        const bool next = STEADY || kt + 1 < nk;
+#pragma unroll
+        for (int u = 0; u < kSubSteps - 1; ++u) {
+            const int cur = u & 1, nxt = cur ^ 1;
+            const bool loads = STEADY && u < 2;
+            // this sub-step's operands were read a sub-step ago: a free wait that keeps the
+            // compiler's own waits (it counts the direct-to-LDS loads as LDS traffic) out
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            if (u == 0 && next) issue_a(kt + 1);
+            if (u == 1 && STEADY) issue_b(kt + 2);
+            read_frags(kt, u + 1, fa[nxt], fb[nxt]);
+            mfma_rows(fa[cur], fb[cur], 0, 4);
+            if (loads) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mfma_rows(fa[1], fb[1], 0, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (STEADY) LLMINT8_WAIT_BARRIER(8);  // B[kt+2] may stay in flight
+        else LLMINT8_WAIT_BARRIER(0);
+        if (next) read_frags(kt + 1, 0, fa[0], fb[0]);
+        mfma_rows(fa[1], fb[1], 1, 4);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
     if (nk > 0) {
-        v4i fa[2][4], fb[2][NJ];  // operand sets of the current / next sub-step
-        // prologue: A[0], B[0], B[1] in flight; wait for the first two groups
+        // prologue: A[0], B[0] (and B[1]) in flight; wait for the first two groups
         issue_a(0);
         issue_b(0);
         if (nk > 1) {
@@ -198,26 +251,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
             LLMINT8_WAIT_BARRIER(0);
         }
         read_frags(0, 0, fa[0], fb[0]);
-        for (int kt = 0; kt < nk; ++kt) {
-            // every wave passed the last barrier after reading the slots of stage kt-1:
-            // refill them with A[kt+1] and B[kt+2]
-            const bool more_a = kt + 1 < nk, more_b = kt + 2 < nk;
-            if (more_a) issue_a(kt + 1);
-            if (more_b) issue_b(kt + 2);
-#pragma unroll
-            for (int u = 0; u < kSubSteps; ++u) {
-                const int cur = u & 1, nxt = cur ^ 1;
-                if (u + 1 < kSubSteps) {
-                    read_frags(kt, u + 1, fa[nxt], fb[nxt]);
-                } else if (more_a) {
-                    // A[kt+1] and B[kt+1] must have landed; B[kt+2] may stay in flight
-                    if (more_b) LLMINT8_WAIT_BARRIER(8);
-                    else LLMINT8_WAIT_BARRIER(0);
-                    read_frags(kt + 1, 0, fa[nxt], fb[nxt]);
-                }
-                mfma_all(fa[cur], fb[cur]);
-            }
-        }
+        int kt = 0;
+        for (; kt + 2 < nk; ++kt) stage(kt, std::true_type{});
+        for (; kt < nk; ++kt) stage(kt, std::false_type{});
     }
 
     // ---- 16-bit outlier product and epilogue, one 32-row slice at a time
