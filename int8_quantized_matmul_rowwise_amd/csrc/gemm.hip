@@ -13,8 +13,10 @@
 //   MFMA sustains the full int8 rate; the 16x16x64 form issues at about half of it.)
 //   Operands go HBM/L2 -> LDS with global_load_lds (16 B per lane, no register
 //   staging), one 128-byte line per row per K stage (full-line requests).  The LDS
-//   holds 2 A slots and 3 B slots of 32 KB: during stage k the loads of A[k+1] and
-//   B[k+2] are issued, so the weight lines get two stages to arrive.  Waits are counted
+//   holds 3 A slots and 2 B slots of 32 KB: during stage k the loads of B[k+1] and
+//   A[k+2] are issued.  (The 32 tiles running together on one XCD span 8 row panels and 4
+//   column panels, so the activation lines miss that XCD's L2 twice as often as the
+//   weight lines: they get the longer lead.)  Waits are counted
 //   (vmcnt) and the workgroup barrier is a bare s_barrier, so a barrier never drains the
 //   loads still in flight.  Each stage is four 32-deep MFMA sub-steps; the operands of
 //   the next sub-step are read from LDS into a second register set while the 16 MFMAs
@@ -44,13 +46,23 @@ constexpr int kChunks = BK / 16;                         // 16-byte chunks per r
 constexpr int kRowsPerLoad = 64 / kChunks;               // rows covered by one 64-lane load
 constexpr int kLoadsA = BM / kRowsPerLoad / 4;           // per wave, per stage (8)
 constexpr int kLoadsB = BN / kRowsPerLoad / 4;           // per wave, per stage (8)
-constexpr int kSlotsA = 2, kSlotsB = 3;                  // 5 x 32 KB: the whole 160 KB of LDS
+constexpr bool kLeadA = true;                            // which operand is loaded two stages ahead
+constexpr int kSlotsA = kLeadA ? 3 : 2;                  // 5 x 32 KB: the whole 160 KB of LDS
+constexpr int kSlotsB = kLeadA ? 2 : 3;
 constexpr int kSlotBytesB = BN * BK;
 constexpr int kSubSteps = BK / 32;                       // 32-deep MFMA steps per stage
-constexpr int kGroupM = 8;                               // row tiles per group of the tile order
+constexpr int kGroupM = 8;
+// epilogue staging (reuses the operand slots): the tile's row and column factors, then per
+// wave its 128 x 128 outputs, rows padded to 272 bytes (16-byte aligned, half-waves on
+// different banks)
+constexpr int kScaleBytes = 2 * 256 * 4;
+constexpr int kYPitch = 136;  // 16-bit elements
+constexpr int kYStageBytes = 128 * kYPitch * 2;                               // row tiles per group of the tile order
 constexpr int kXcds = 8;
 static_assert(kSlotsA * kTileBytes + kSlotsB * kSlotBytesB <= 160 * 1024, "LDS");
 static_assert(kLoadsA == 8 && kLoadsB == 8, "the waits below count 8 loads per operand and wave");
+static_assert(kScaleBytes + 4 * kYStageBytes <= kSlotsA * kTileBytes + kSlotsB * kSlotBytesB, "epilogue LDS");
+static_assert(BM == 256 && BN == 256, "the factor tables take one row and one column per thread");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -191,12 +203,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
     };
 
     // One K stage.  Sub-steps 0..2 run their 16 MFMAs while the LDS reads of the next
-    // sub-step (and, in 0 and 1, the global loads of A[kt+1] and B[kt+2], into the slots
-    // stage kt-1 freed) are interleaved, front-loaded so they have most of the sub-step to
-    // land.  Sub-step 3 runs 4 MFMAs, waits for A[kt+1] and B[kt+1] and meets the other
-    // waves at the barrier, then reads stage kt+1's first operands under its other 12.
-    // Each sub-step is fenced (sched_barrier) so that the interleave stays inside it.
-    // STEADY: B[kt+2] exists (every stage but the last two).
+    // sub-step (and, in 0 and 1, the global loads of stage kt+1 of the short-lead operand
+    // and stage kt+2 of the long-lead one, into the slots stage kt-1 freed) are
+    // interleaved, front-loaded so they have most of the sub-step to land.  Sub-step 3 runs
+    // 4 MFMAs, waits for stage kt+1 and meets the other waves at the barrier, then reads
+    // stage kt+1's first operands under its other 12.  Each sub-step is fenced
+    // (sched_barrier) so that the interleave stays inside it.
+    // STEADY: stage kt+2 exists (every stage but the last two).
     v4i fa[2][4], fb[2][NJ];  // operand sets of the current / next sub-step
     auto stage = [&](int kt, auto steady_tag) {
         constexpr bool STEADY = decltype(steady_tag)::value;
@@ -208,8 +221,14 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
             // this sub-step's operands were read a sub-step ago: a free wait that keeps the
             // compiler's own waits (it counts the direct-to-LDS loads as LDS traffic) out
             __builtin_amdgcn_s_waitcnt(0xC07F);
-            if (u == 0 && next) issue_a(kt + 1);
-            if (u == 1 && STEADY) issue_b(kt + 2);
+            if (u == 0 && next) {
+                if (kLeadA) issue_b(kt + 1);
+                else issue_a(kt + 1);
+            }
+            if (u == 1 && STEADY) {
+                if (kLeadA) issue_a(kt + 2);
+                else issue_b(kt + 2);
+            }
             read_frags(kt, u + 1, fa[nxt], fb[nxt]);
             mfma_rows(fa[cur], fb[cur], 0, 4);
             if (loads) {
@@ -231,7 +250,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
         }
         mfma_rows(fa[1], fb[1], 0, 1);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (STEADY) LLMINT8_WAIT_BARRIER(8);  // B[kt+2] may stay in flight
+        if constexpr (STEADY) LLMINT8_WAIT_BARRIER(8);  // the stage kt+2 loads may stay in flight
         else LLMINT8_WAIT_BARRIER(0);
         if (next) read_frags(kt + 1, 0, fa[0], fb[0]);
         mfma_rows(fa[1], fb[1], 1, 4);
@@ -245,7 +264,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
         issue_a(0);
         issue_b(0);
         if (nk > 1) {
-            issue_b(1);
+            if (kLeadA) issue_a(1);
+            else issue_b(1);
             LLMINT8_WAIT_BARRIER(8);
         } else {
             LLMINT8_WAIT_BARRIER(0);
@@ -257,46 +277,86 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
     }
 
     // ---- 16-bit outlier product and epilogue, one 32-row slice at a time
+    // (lane holds column lane%32 and rows 8*(e/4) + 4*(lane/32) + e%4, e = 0..15, of each
+    // 32 x 32 tile)
     const int32_t nO = *p.n_out;
     const int nsub = (nO + 15) >> 4;  // 16-deep MFMA steps over the padded outlier columns
     const int64_t wm0 = m0 + wm * 128, wn0 = n0 + wn * (32 * NJ);
+    auto outlier_product = [&](const uint16_t* xo, int64_t n) {
+        const int64_t bn = n < p.N ? n : p.N - 1;
+        const uint16_t* wo = p.WO + bn * p.xo_pitch + h * 8;
+        v16f F = v16f{};
+        for (int ch = 0; ch < nsub; ++ch)
+            F = mfma16<DT>(*(const u32x4*)(xo + ch * 16), *(const u32x4*)(wo + ch * 16), F);
+        return F;
+    };
+    if constexpr (ACC_OUT) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        // lane holds column lane%32 and rows 8*(e/4) + 4*(lane/32) + e%4 (e = 0..15) of each 32x32 tile
-        const int64_t row0 = wm0 + 32 * i + 4 * h;
-        float r[16];
+        for (int i = 0; i < 4; ++i) {
+            const int64_t row0 = wm0 + 32 * i + 4 * h;
+            int64_t am = wm0 + 32 * i + rl;
+            am = am < p.M ? am : p.M - 1;
+            const uint16_t* xo = p.XO + am * p.xo_pitch + h * 8;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int64_t m = row0 + 8 * (e >> 2) + (e & 3);
-            r[e] = m < p.M ? p.s_x[m] / 127.0f : 0.0f;
-        }
-        int64_t am = wm0 + 32 * i + rl;
-        am = am < p.M ? am : p.M - 1;
-        const uint16_t* xo = p.XO + am * p.xo_pitch + h * 8;
+            for (int j = 0; j < NJ; ++j) {
+                const int64_t n = wn0 + 32 * j + rl;
+                const v16f F = outlier_product(xo, n);
+                if (n >= p.N) continue;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int64_t n = wn0 + 32 * j + rl;
-            const int64_t bn = n < p.N ? n : p.N - 1;
-            const uint16_t* wo = p.WO + bn * p.xo_pitch + h * 8;
-            v16f F = v16f{};
-            for (int ch = 0; ch < nsub; ++ch)
-                F = mfma16<DT>(*(const u32x4*)(xo + ch * 16), *(const u32x4*)(wo + ch * 16), F);
-            if (n >= p.N) continue;
-            const float c = p.s_w[n] / 127.0f;
-            const int64_t lane_off = row0 * p.N + n;  // element (row0, n); row e adds a uniform multiple of N
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                if (row0 + 8 * (e >> 2) + (e & 3) >= p.M) continue;
-                const int64_t off = lane_off + (int64_t)(8 * (e >> 2) + (e & 3)) * p.N;
-                if constexpr (ACC_OUT) {
-                    p.C_acc[off] = acc[i][j][e];
-                    p.F_acc[off] = F[e];
-                } else {
-                    const float yi = __fmul_rn(__fmul_rn((float)acc[i][j][e], r[e]), c);
-                    const float y = __fadd_rn(yi, __fmul_rn(c, F[e]));
-                    p.Y[off] = from_f32<DT>(y);
+                for (int e = 0; e < 16; ++e) {
+                    const int64_t m = row0 + 8 * (e >> 2) + (e & 3);
+                    if (m >= p.M) continue;
+                    p.C_acc[m * p.N + n] = acc[i][j][e];
+                    p.F_acc[m * p.N + n] = F[e];
                 }
             }
+        }
+    } else {
+        // The operand slots are free once every wave is past its last reads and no load is in
+        // flight: the LDS then holds the tile's dequantization factors and, per wave, its
+        // 128 x 128 outputs, which leave as 16-byte row segments (full lines).
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        float* rsc = (float*)smem;  // r_i = s_x[i]/127 of the tile's rows
+        float* csc = rsc + BM;      // c_n = s_w[n]/127 of its columns
+        {
+            const int64_t m = m0 + tid, n = n0 + tid;
+            rsc[tid] = m < p.M ? p.s_x[m] / 127.0f : 0.0f;
+            csc[tid] = n < p.N ? p.s_w[n] / 127.0f : 0.0f;
+        }
+        __syncthreads();
+        uint16_t* ys = (uint16_t*)(smem + kScaleBytes + w * kYStageBytes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rb = wm * 128 + 32 * i + 4 * h;  // tile row of e = 0
+            float r[16];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const v4f t = *(const v4f*)(rsc + rb + 8 * a);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) r[4 * a + b] = t[b];
+            }
+            int64_t am = wm0 + 32 * i + rl;
+            am = am < p.M ? am : p.M - 1;
+            const uint16_t* xo = p.XO + am * p.xo_pitch + h * 8;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const v16f F = outlier_product(xo, wn0 + 32 * j + rl);
+                const float c = csc[wn * (32 * NJ) + 32 * j + rl];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float yi = __fmul_rn(__fmul_rn((float)acc[i][j][e], r[e]), c);
+                    const float y = __fadd_rn(yi, __fmul_rn(c, F[e]));
+                    ys[(32 * i + 8 * (e >> 2) + 4 * h + (e & 3)) * kYPitch + 32 * j + rl] = from_f32<DT>(y);
+                }
+            }
+        }
+        // read back the wave's own rows (one wave's LDS accesses complete in order)
+#pragma unroll 4
+        for (int it = 0; it < 32; ++it) {
+            const int row = it * 4 + (lane >> 4), ch = lane & 15;
+            const u32x4 v = *(const u32x4*)(ys + row * kYPitch + ch * 8);
+            const int64_t m = wm0 + row, n = wn0 + ch * 8;
+            if (m < p.M && n < p.N) *(u32x4*)(p.Y + m * p.N + n) = v;
         }
     }
 }
