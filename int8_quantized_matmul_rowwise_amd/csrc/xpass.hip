@@ -168,7 +168,6 @@ hipError_t launch_compact(int64_t M, int64_t K, const uint32_t* partial, uint32_
 // and n_O.  The tiled path runs detect (row-block partials), compact, then code_rows.
 namespace llmint8 {
 
-constexpr int kHold = 16;  // 16-byte chunks per thread held in registers (256 threads: K <= 32768)
 
 template <int DT>
 __global__ __launch_bounds__(256) void detect_direct_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
@@ -203,101 +202,127 @@ __global__ __launch_bounds__(256) void detect_direct_kernel(const uint16_t* __re
     if ((lane & 3) == 0 && c < nch) bitmap[c >> 2] = word;  // K % 16 == 0: a word's chunks exist together
 }
 
-// Code the rows: workgroup i < M takes row i.  s_x[i] = max over the non-outlier columns
-// of |X[i,j]|; Xq[i,j] = 0 for j in O, else the vector-wise code; Xq[i, K..pitch) = 0;
-// XO[i,t] = X[i, O[t]] for t < n_O, 0 up to the next multiple of 32 (the rank t of column j
-// comes from a block-wide scan of the bitmap's popcounts).  HOLD: the row stays in
-// registers between the max and the coding (K <= 32768), else it is read twice.
-// Workgroups M.. gather WO[n,t] = (dtype) Wq[n, O[t]] (exact; same padding), 64 rows of Wq
-// each, from the O written by the compaction.  WRITE_O: workgroup 0 writes O and n_O (the
-// small-batch path has no compaction launch).
-template <int DT, bool HOLD, bool WRITE_O>
+// ---- per-chunk arithmetic of the row coding (a chunk: 8 consecutive 16-bit elements in
+// four dwords; o: its 8 outlier bits; any: some lane of the wave has o != 0, wave-uniform)
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// 0xffff over the halves of dword d (elements 2d, 2d+1) whose outlier bits are set
+__device__ __forceinline__ uint32_t outlier_halves(uint32_t o, int d) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_sbfe((int)o, 2 * d, 1);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_sbfe((int)o, 2 * d + 1, 1);
+    return (lo & 0xffffu) | (hi & 0xffff0000u);
+}
+
+// 0xff over the bytes whose bit is set in the low 4 bits of b (no carries: the four
+// shifted copies of b do not overlap)
+__device__ __forceinline__ uint32_t byte_mask4(uint32_t b) { return ((b * 0x00204081u) & 0x01010101u) * 0xffu; }
+
+// Running max of the magnitudes of the non-outlier elements.  For finite fp16 and bf16
+// values the order of |x| is the unsigned order of the pattern without its sign bit, so the
+// max is taken on those 15-bit integers, two per instruction.
+__device__ __forceinline__ u16x2 absmax_bits(u16x2 acc, const u32x4& x, uint32_t o, bool any) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        uint32_t a = x[d] & 0x7fff7fffu;
+        if (any) a &= ~outlier_halves(o, d);
+        acc = __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2, a));
+    }
+    return acc;
+}
+
+// Codes of a chunk, byte j of dword d for element 4d + j: clamp(rne(RN32(x * inv)), -127,
+// 127), 0 in outlier columns.  Rounding to an integer by adding 1.5 * 2^23: the sum lies
+// in [2^23, 2^24), where the float spacing is 1, so the add rounds to nearest even and the
+// integer sits in the low mantissa bits (its low byte is the two's-complement code).
+template <int DT>
+__device__ __forceinline__ u32x2 code_chunk(const u32x4& x, uint32_t o, float inv, bool any) {
+    uint32_t t[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float f = to_f32<DT>((uint16_t)(x[j >> 1] >> (16 * (j & 1))));
+        float v = __fmul_rn(f, inv);
+        v = fminf(fmaxf(v, -127.0f), 127.0f);
+        t[j] = __builtin_bit_cast(uint32_t, __fadd_rn(v, 12582912.0f));
+    }
+    u32x2 q;
+    q[0] = __builtin_amdgcn_perm(t[1], t[0], 0x0c0c0400u) | __builtin_amdgcn_perm(t[3], t[2], 0x04000c0cu);
+    q[1] = __builtin_amdgcn_perm(t[5], t[4], 0x0c0c0400u) | __builtin_amdgcn_perm(t[7], t[6], 0x04000c0cu);
+    if (any) {
+        q[0] &= ~byte_mask4(o & 0xfu);
+        q[1] &= ~byte_mask4(o >> 4);
+    }
+    return q;
+}
+
+// Code the rows.  The first n_wo workgroups gather WO[n,t] = (dtype) Wq[n, O[t]] (exact;
+// zero up to the next multiple of 32), 64 rows of Wq each, from the O written by the
+// compaction; they come first so that their scattered loads overlap the row work instead
+// of trailing it.  The other `groups` workgroups each take rows g, g + groups, ...: for
+// row i, s_x[i] = max over the non-outlier columns of |X[i,j]|; Xq[i,j] = 0 for j in O,
+// else the vector-wise code; Xq[i, K..pitch) = 0; XO[i,t] = X[i, O[t]] for t < n_O, 0 up
+// to the next multiple of 32.  Set-up once per workgroup: the bitmap in LDS and, per
+// word, the number of outlier columns before it (a block-wide scan of popcounts), which
+// gives the rank t of every outlier column.  HOLD > 0: a row stays in registers (HOLD
+// 16-byte chunks per thread, K <= 2048 * HOLD) between its max and its coding, else each
+// row is read twice.  (A second register set, to load the next row while one is coded,
+// costs more in occupancy than it gains.)  WRITE_O: the workgroup of row 0 writes O and
+// n_O (the small-batch path has no compaction launch).
+template <int DT, int HOLD, bool WRITE_O>
 __global__ __launch_bounds__(256) void code_rows_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                         const uint32_t* __restrict__ bitmap, int32_t* __restrict__ O,
                                                         int32_t* __restrict__ n_out, int8_t* __restrict__ Xq,
                                                         int64_t xq_pitch, float* __restrict__ s_x,
                                                         uint16_t* __restrict__ XO, int64_t xo_pitch,
                                                         const int8_t* __restrict__ Wq, int64_t N,
-                                                        uint16_t* __restrict__ WO) {
+                                                        uint16_t* __restrict__ WO, int64_t n_wo, int64_t groups) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    if ((int64_t)blockIdx.x >= M) {
+    if ((int64_t)blockIdx.x < n_wo) {
+        // thread: column t0 + tid%32 of W_O, rows tid/32 + 8k; one O load, 8 independent Wq loads
         const int32_t nO = *n_out;
         const int32_t P = (nO + 31) & ~31;
-        const int64_t n0 = ((int64_t)blockIdx.x - M) * 64;
-        for (int64_t idx = tid; idx < 64 * (int64_t)P; idx += 256) {
-            const int64_t r = idx / P, t = idx % P;
-            const int64_t n = n0 + r;
-            if (n < N) WO[n * xo_pitch + t] = t < nO ? from_f32<DT>((float)Wq[n * K + O[t]]) : (uint16_t)0;
+        const int64_t n0 = (int64_t)blockIdx.x * 64;
+        const int rr = tid >> 5;
+        for (int32_t t0 = 0; t0 < P; t0 += 32) {
+            const int32_t t = t0 + (tid & 31);
+            const int64_t col = t < nO ? O[t] : -1;
+            uint16_t v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int64_t n = n0 + rr + 8 * k;
+                v[k] = (col >= 0 && n < N) ? from_f32<DT>((float)Wq[n * K + col]) : (uint16_t)0;
+            }
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int64_t n = n0 + rr + 8 * k;
+                if (n < N) WO[n * xo_pitch + t] = v[k];
+            }
         }
         return;
     }
-    __shared__ uint32_t bits[kMaxKw];
-    __shared__ float red[4];
+    // dynamic LDS, sized to K: the bitmap, then the outlier count before each word
+    extern __shared__ uint32_t dyn_lds[];
+    __shared__ float red[2][4];
     __shared__ int32_t wsum[4];
-    const int64_t i = blockIdx.x;
+    const int64_t g = (int64_t)blockIdx.x - n_wo;
     const int64_t nch = K / 8, Kw = ceil_div(K, 32);
-    const uint16_t* row = X + i * K;
-    constexpr int H = HOLD ? kHold : 1;
-    u32x4 v[H];
-    if constexpr (HOLD) {
+    uint32_t* bits = dyn_lds;
+    int32_t* wrank = (int32_t*)(dyn_lds + Kw);
+    constexpr int H = HOLD > 0 ? HOLD : 1;
+    u32x4 va[H];
+    auto load_row = [&](u32x4(&v)[H], int64_t i) {
+        const uint16_t* row = X + i * K;
 #pragma unroll
-        for (int h = 0; h < kHold; ++h) {
+        for (int h = 0; h < H; ++h) {
             const int64_t c = tid + 256 * h;
             v[h] = c < nch ? *(const u32x4*)(row + c * 8) : u32x4{0u, 0u, 0u, 0u};
         }
-    }
+    };
+    if constexpr (HOLD > 0) load_row(va, g);  // in flight during the set-up
+
     for (int64_t w = tid; w < Kw; w += 256) bits[w] = bitmap[w];
     __syncthreads();
-    auto obits = [&](int64_t c) { return (bits[c >> 2] >> (8 * (c & 3))) & 0xffu; };
-    auto absmax8 = [&](const u32x4& x, uint32_t o, float m) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float a = __builtin_fabsf(to_f32<DT>((uint16_t)(x[j >> 1] >> (16 * (j & 1)))));
-            if (!((o >> j) & 1u)) m = fmaxf(m, a);
-        }
-        return m;
-    };
-    auto code8 = [&](const u32x4& x, uint32_t o, float inv) -> u32x2 {
-        u32x2 packed = {0u, 0u};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float f = to_f32<DT>((uint16_t)(x[j >> 1] >> (16 * (j & 1))));
-            const int qv = ((o >> j) & 1u) ? 0 : quantize(f, inv);
-            packed[j >> 2] |= ((uint32_t)qv & 0xffu) << (8 * (j & 3));
-        }
-        return packed;
-    };
-
-    float m = 0.0f;
-    if constexpr (HOLD) {
-#pragma unroll
-        for (int h = 0; h < kHold; ++h) {
-            const int64_t c = tid + 256 * h;
-            if (c < nch) m = absmax8(v[h], obits(c), m);
-        }
-    } else {
-        for (int64_t c = tid; c < nch; c += 256) m = absmax8(*(const u32x4*)(row + c * 8), obits(c), m);
-    }
-    m = wave_max(m);
-    if (lane == 0) red[wv] = m;
-    __syncthreads();
-    const float s = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float inv = inv_scale(s);
-    int8_t* qrow = Xq + i * xq_pitch;
-    if constexpr (HOLD) {
-#pragma unroll
-        for (int h = 0; h < kHold; ++h) {
-            const int64_t c = tid + 256 * h;
-            if (c < nch) *(u32x2*)(qrow + c * 8) = code8(v[h], obits(c), inv);
-        }
-    } else {
-        for (int64_t c = tid; c < nch; c += 256) *(u32x2*)(qrow + c * 8) = code8(*(const u32x4*)(row + c * 8), obits(c), inv);
-    }
-    for (int64_t c = nch + tid; c < xq_pitch / 8; c += 256) *(u32x2*)(qrow + c * 8) = u32x2{0u, 0u};
-    if (tid == 0) s_x[i] = s;
-
-    // outlier gather: thread tid walks words [tid*wpt, (tid+1)*wpt); its first rank is the
-    // exclusive prefix of the popcounts before them
+    // thread tid takes words [tid*wpt, (tid+1)*wpt); its first rank is the exclusive prefix
+    // of the popcounts before them
     const int64_t wpt = ceil_div(Kw, 256);
     int32_t cnt = 0;
     for (int64_t w = tid * wpt; w < (tid + 1) * wpt && w < Kw; ++w) cnt += __popc(bits[w]);
@@ -315,44 +340,120 @@ __global__ __launch_bounds__(256) void code_rows_kernel(const uint16_t* __restri
         pos += q < wv ? wsum[q] : 0;
         total += wsum[q];
     }
-    uint16_t* xo = XO + i * xo_pitch;
     for (int64_t w = tid * wpt; w < (tid + 1) * wpt && w < Kw; ++w) {
-        uint32_t wd = bits[w];
-        while (wd) {
-            const int b = __ffs(wd) - 1;
-            const int64_t j = w * 32 + b;
-            xo[pos] = row[j];
-            if (WRITE_O && i == 0) O[pos] = (int32_t)j;
-            ++pos;
-            wd &= wd - 1;
-        }
+        wrank[w] = pos;
+        pos += __popc(bits[w]);
     }
+    __syncthreads();
     const int32_t P = (total + 31) & ~31;
-    for (int64_t t = total + tid; t < P; t += 256) xo[t] = 0;
-    if (WRITE_O && i == 0 && tid == 0) *n_out = total;
+
+    auto obits = [&](int64_t c) { return (bits[c >> 2] >> (8 * (c & 3))) & 0xffu; };
+    auto wave_any = [](uint32_t o) { return __builtin_amdgcn_ballot_w64(o != 0u) != 0; };
+
+    // one row: its max, its codes, its outlier values (from the chunk in hand, at their
+    // ranks), its padding.  par: which slot of red this row uses (a slot is written again
+    // only two rows later, after a barrier every wave has passed, so one barrier per row).
+    auto process = [&](const u32x4(&v)[H], int64_t i, int par) {
+        const uint16_t* row = X + i * K;
+        u16x2 mb = {0, 0};
+        if constexpr (HOLD > 0) {
+#pragma unroll
+            for (int h = 0; h < HOLD; ++h) {
+                const int64_t c = tid + 256 * h;
+                const uint32_t o = c < nch ? obits(c) : 0u;  // chunks past the row hold zeros
+                mb = absmax_bits(mb, v[h], o, wave_any(o));
+            }
+        } else {
+            for (int64_t c = tid; c < nch; c += 256) {
+                const uint32_t o = obits(c);
+                mb = absmax_bits(mb, *(const u32x4*)(row + c * 8), o, wave_any(o));
+            }
+        }
+        float m = to_f32<DT>(mb[0] > mb[1] ? mb[0] : mb[1]);
+        m = wave_max(m);
+        if (lane == 0) red[par][wv] = m;
+        __syncthreads();
+        const float s = fmaxf(fmaxf(red[par][0], red[par][1]), fmaxf(red[par][2], red[par][3]));
+        const float inv = inv_scale(s);
+        int8_t* qrow = Xq + i * xq_pitch;
+        uint16_t* xo = XO + i * xo_pitch;
+        auto code_store = [&](const u32x4& x, int64_t c) {
+            const uint32_t o = obits(c);
+            const bool any = wave_any(o);
+            *(u32x2*)(qrow + c * 8) = code_chunk<DT>(x, o, inv, any);
+            if (any && o) {
+                int32_t r = wrank[c >> 2] + __popc(bits[c >> 2] & ((1u << (8 * (c & 3))) - 1u));
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    if ((o >> j) & 1u) {
+                        xo[r] = (uint16_t)(x[j >> 1] >> (16 * (j & 1)));
+                        if (WRITE_O && i == 0) O[r] = (int32_t)(8 * c + j);
+                        ++r;
+                    }
+                }
+            }
+        };
+        if constexpr (HOLD > 0) {
+#pragma unroll
+            for (int h = 0; h < HOLD; ++h) {
+                const int64_t c = tid + 256 * h;
+                if (c < nch) code_store(v[h], c);
+            }
+        } else {
+            for (int64_t c = tid; c < nch; c += 256) code_store(*(const u32x4*)(row + c * 8), c);
+        }
+        for (int64_t c = nch + tid; c < xq_pitch / 8; c += 256) *(u32x2*)(qrow + c * 8) = u32x2{0u, 0u};
+        for (int64_t t = total + tid; t < P; t += 256) xo[t] = 0;
+        if (tid == 0) s_x[i] = s;
+    };
+
+    int par = 0;
+    for (int64_t i = g; i < M; i += groups, par ^= 1) {
+        if (HOLD > 0 && i != g) load_row(va, i);
+        process(va, i, par);
+    }
+    if (WRITE_O && g == 0 && tid == 0) *n_out = total;
 }
 
+template <int DT, int HOLD, bool WRITE_O>
+static hipError_t code_rows_launch1(const XPassArgs& a, const uint32_t* bitmap, int32_t* O, int32_t* n_out,
+                                    int64_t n_wo, hipStream_t stream) {
+    // persistent row workgroups: as many as fit on the device at once (at most M)
+    const size_t lds = (size_t)ceil_div(a.K, 32) * 8;
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, code_rows_kernel<DT, HOLD, WRITE_O>, 256, lds);
+    if (e != hipSuccess) return e;
+    int64_t groups = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    groups = groups < a.M ? groups : a.M;
+    const unsigned grid = (unsigned)(n_wo + groups);
+    if (grid == 0) return hipSuccess;
+    code_rows_kernel<DT, HOLD, WRITE_O><<<grid, 256, lds, stream>>>(
+        (const uint16_t*)a.X, a.M, a.K, bitmap, O, n_out, a.Xq, a.xq_pitch, a.s_x, (uint16_t*)a.XO, a.xo_pitch, a.Wq,
+        a.N, (uint16_t*)a.WO, n_wo, groups);
+    return hipGetLastError();
+}
+
+// The register hold is sized to the row (16-byte chunks per thread of 256): fewer
+// registers per thread leave room for more workgroups per CU.
 template <int DT, bool WRITE_O>
-static void code_rows_launch(unsigned grid, const XPassArgs& a, const uint32_t* bitmap, int32_t* O, int32_t* n_out,
-                             hipStream_t stream) {
-    if (a.K <= kSmallK)
-        code_rows_kernel<DT, true, WRITE_O><<<grid, 256, 0, stream>>>(
-            (const uint16_t*)a.X, a.M, a.K, bitmap, O, n_out, a.Xq, a.xq_pitch, a.s_x, (uint16_t*)a.XO, a.xo_pitch,
-            a.Wq, a.N, (uint16_t*)a.WO);
-    else
-        code_rows_kernel<DT, false, WRITE_O><<<grid, 256, 0, stream>>>(
-            (const uint16_t*)a.X, a.M, a.K, bitmap, O, n_out, a.Xq, a.xq_pitch, a.s_x, (uint16_t*)a.XO, a.xo_pitch,
-            a.Wq, a.N, (uint16_t*)a.WO);
+static hipError_t code_rows_launch(const XPassArgs& a, const uint32_t* bitmap, int32_t* O, int32_t* n_out,
+                                   int64_t n_wo, hipStream_t stream) {
+    if (a.K <= 2048 * 4) return code_rows_launch1<DT, 4, WRITE_O>(a, bitmap, O, n_out, n_wo, stream);
+    if (a.K <= 2048 * 8) return code_rows_launch1<DT, 8, WRITE_O>(a, bitmap, O, n_out, n_wo, stream);
+    if (a.K <= 2048 * 16) return code_rows_launch1<DT, 16, WRITE_O>(a, bitmap, O, n_out, n_wo, stream);
+    return code_rows_launch1<DT, 0, WRITE_O>(a, bitmap, O, n_out, n_wo, stream);
 }
 
 // Big path: after detect + compact (which wrote the bitmap, O and n_O).
 hipError_t launch_code_rows(const XPassArgs& a, const uint32_t* bitmap, int32_t* O, int32_t* n_out,
                             hipStream_t stream) {
-    const int64_t nblk = a.M + (a.Wq ? ceil_div(a.N, 64) : 0);
-    if (nblk == 0) return hipSuccess;
-    if (a.dt == F16) code_rows_launch<F16, false>((unsigned)nblk, a, bitmap, O, n_out, stream);
-    else code_rows_launch<BF16, false>((unsigned)nblk, a, bitmap, O, n_out, stream);
-    return hipGetLastError();
+    const int64_t n_wo = a.Wq ? ceil_div(a.N, 64) : 0;
+    if (a.M + n_wo == 0) return hipSuccess;
+    if (a.dt == F16) return code_rows_launch<F16, false>(a, bitmap, O, n_out, n_wo, stream);
+    return code_rows_launch<BF16, false>(a, bitmap, O, n_out, n_wo, stream);
 }
 
 // Small-batch path: direct detect, then the row coding also writes O and n_O.
@@ -364,9 +465,8 @@ hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, ui
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (a.dt == F16) code_rows_launch<F16, true>((unsigned)a.M, a, bitmap, O, n_out, stream);
-    else code_rows_launch<BF16, true>((unsigned)a.M, a, bitmap, O, n_out, stream);
-    return hipGetLastError();
+    if (a.dt == F16) return code_rows_launch<F16, true>(a, bitmap, O, n_out, 0, stream);
+    return code_rows_launch<BF16, true>(a, bitmap, O, n_out, 0, stream);
 }
 
 }  // namespace llmint8

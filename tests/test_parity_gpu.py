@@ -187,3 +187,92 @@ def test_two_stage_calls_equal_the_one_call():
     torch.cuda.synchronize()
     assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
     assert torch.equal(Y1.view(torch.int16), Y3.view(torch.int16))
+
+
+# ---- exhaustive quantizer sweeps on the GPU: every finite 16-bit value under ~40 scales
+
+def _finite_patterns(dt):
+    p = np.arange(65536, dtype=np.uint32)
+    exp_mask = 0x7C00 if dt == "fp16" else 0x7F80
+    return p[(p & exp_mask) != exp_mask].astype(np.uint16)
+
+
+def _sweep_scales(dt):
+    """About 40 magnitudes (as 15-bit patterns): evenly spread over the finite range, plus the
+    smallest allowed scale, powers of two and the largest finite value.  For bf16 the
+    scales stay at or above 2^-120, below which 127/s leaves fp32 (outside the contract)."""
+    top = 0x7BFF if dt == "fp16" else 0x7F7F
+    low = 0x0001 if dt == "fp16" else 0x0380
+    base = np.linspace(low, top, 32).astype(np.int64)
+    pow2 = (np.array([0x3C00, 0x4400, 0x5800, 0x0400], np.int64) if dt == "fp16"
+            else np.array([0x3F80, 0x4300, 0x4780, 0x0400], np.int64))
+    extra = np.array([low, top, low + 1, top - 1], np.int64)
+    return np.unique(np.concatenate([base, pow2, extra]))[:40]
+
+
+def _sweep_rows(dt, width=None):
+    """Rows whose absmax is each scale s, holding every finite value of magnitude <= s
+    (both signs).  width: split each scale's values over rows of at most `width` columns,
+    each row carrying s itself.  Returns 16-bit patterns, zero padded, K a multiple of 16."""
+    pats = _finite_patterns(dt)
+    mag = (pats & 0x7FFF).astype(np.int64)
+    rows = []
+    for s in _sweep_scales(dt):
+        vals = pats[mag <= s]
+        if width is None:
+            rows.append(vals)
+        else:
+            for k in range(0, vals.size, width - 1):
+                rows.append(np.concatenate([[np.uint16(s)], vals[k:k + width - 1]]))
+    K = int(-(-max(r.size for r in rows) // 16) * 16)
+    X = np.zeros((len(rows), K), np.uint16)
+    for i, r in enumerate(rows):
+        X[i, :r.size] = r
+    return X
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+@pytest.mark.parametrize("layout", ["two_reads", "hold16", "hold8", "hold4", "small_batch"])
+def test_row_quantizer_exhaustive_sweep(dt, layout):
+    """X side: s_x and every code bitwise against the oracle, tau = inf (no outliers),
+    through each row-coding configuration: rows longer than the register hold (read
+    twice), rows held in registers at each hold size (K <= 32768, 16384, 8192; M > 64),
+    and the small-batch launch (M <= 64)."""
+    width = {"two_reads": None, "hold16": 32768, "hold8": 16384, "hold4": 8192, "small_batch": 32768}[layout]
+    Xb = _sweep_rows(dt, width)
+    if layout == "small_batch":
+        Xb = Xb[:64]
+    elif Xb.shape[0] <= 64:
+        Xb = np.concatenate([Xb, Xb[::-1]])  # past the small-batch switch
+    M, K = Xb.shape
+    _banner(f"row quantizer sweep {dt} {layout}: {M} x {K}")
+    X = workloads.from_bits(Xb, dt).cuda()
+    Wq = torch.zeros((8, K), dtype=torch.int8, device="cuda")
+    ws = lm.int8_matmul_prepare(X, Wq, float("inf"))
+    torch.cuda.synchronize()
+    v = lm.workspace_views(ws, M, K, 8, X.dtype)
+    O = oracle.outlier_columns(Xb, dt, float("inf"))
+    assert O.size == 0 and v["n_outliers"] == 0
+    Xq_o, s_x_o, _ = oracle.quantize_rows(Xb, dt, O)
+    assert np.array_equal(v["s_x"].cpu().numpy().view(np.uint32), s_x_o.view(np.uint32)), "s_x differs"
+    xq = v["Xq"].cpu().numpy()
+    bad = np.argwhere(xq != Xq_o)
+    assert bad.size == 0, f"Xq differs at {bad[:5].tolist()} (of {len(bad)})"
+    # every nonzero row maps its absmax to +-127
+    assert np.all(np.abs(xq.astype(np.int32)).max(axis=1) == 127)
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+def test_weight_quantizer_exhaustive_sweep(dt):
+    """W side: the same value sets as the columns of W (K x N), Wq and s_w bitwise."""
+    Wb = np.ascontiguousarray(_sweep_rows(dt).T)
+    K, N = Wb.shape
+    N8 = -(-N // 8) * 8
+    Wb = np.concatenate([Wb, np.zeros((K, N8 - N), np.uint16)], axis=1)
+    _banner(f"weight quantizer sweep {dt}: {K} x {N8}")
+    Wq, s_w = lm.int8_quantize_weight(workloads.from_bits(Wb, dt).cuda())
+    torch.cuda.synchronize()
+    Wq_o, s_w_o = oracle.quantize_weight(Wb, dt)
+    assert np.array_equal(s_w.cpu().numpy().view(np.uint32), s_w_o.view(np.uint32)), "s_w differs"
+    bad = np.argwhere(Wq.cpu().numpy() != Wq_o)
+    assert bad.size == 0, f"Wq differs at {bad[:5].tolist()} (of {len(bad)})"
