@@ -3,10 +3,12 @@
 // MFMA, fp32 F = X[:,O] Wq[:,O]^T on 16-bit MFMA, the same epilogue op sequence), laid
 // out for an HBM-bound product: the weight is read once, so every workgroup streams its
 // own 16 rows of Wq (16 output columns) straight from HBM into registers -- no LDS
-// staging, nothing to reuse -- and the four waves of a workgroup split K, each with 16 K
-// steps of loads in flight.  Two 64-deep steps of a wave cover one 128-byte line of each
-// Wq row.  Partial int32 sums are combined exactly through LDS.  Each workgroup gathers
-// the 16-bit outlier operands Wq[n, O[t]] of its own columns.
+// staging, nothing to reuse -- and the four waves of a workgroup split K, each keeping
+// two batches of K steps in flight (the next batch is loaded before the current one's
+// MFMAs).  Two 64-deep steps of a wave cover one 128-byte line of each Wq row.  Partial
+// int32 sums are combined exactly through LDS.  Each workgroup gathers the 16-bit outlier
+// operands Wq[n, O[t]] of its own columns, at kernel start so that the scattered loads
+// overlap the weight stream.
 // "LLM.int8(): 8-bit Matrix Multiplication for Transformers at Scale", abstract.
 #include "common.hpp"
 #include "launch.hpp"
@@ -17,7 +19,6 @@ namespace {
 
 constexpr int kCols = 16;   // output columns per workgroup
 constexpr int kWaves = 4;   // waves per workgroup, splitting K
-constexpr int kPairs = 8;   // pairs of 64-deep K steps in flight per wave
 
 struct SmallParams {
     const int8_t* Xq;
@@ -43,9 +44,13 @@ __device__ __forceinline__ v4f mfma16x16(const u32x4& a, const u32x4& b, const v
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
-// MG: groups of 16 rows of X (ceil(M/16)).
+// MG: groups of 16 rows of X (ceil(M/16)).  Batches of PAIRS step pairs per wave, two
+// register sets: the next batch's loads are issued before the current batch's MFMAs, so
+// the weight stream never waits for the arithmetic.
 template <int DT, int MG, bool ACC_OUT>
 __global__ __launch_bounds__(256) void gemm_small_kernel(SmallParams p) {
+    constexpr int PAIRS = MG == 1 ? 4 : (MG == 2 ? 2 : 1);
+    constexpr int U = 2 * PAIRS;  // 64-deep steps per batch
     __shared__ v4i red[kWaves][MG][64];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int li = lane & 15, q = lane >> 4;  // 16x16x64 operands: row/column li, 16 k at 16*q
@@ -60,25 +65,60 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(SmallParams p) {
     }
     const int64_t nsteps = ceil_div(p.K, 64);
 
+    // The outlier operands of the epilogue (first 32 outlier columns), gathered now so that
+    // their scattered loads overlap the weight stream: Wq[n, O[t]] for t = 8q + e, and the
+    // row's X[:,O] chunk.
+    const int32_t nO = *p.n_out;
+    uint32_t wo0[4] = {0u, 0u, 0u, 0u};
+    u32x4 xo0 = {0u, 0u, 0u, 0u};
+    if (w < MG && nO > 0) {
+        const int64_t am = w * 16 + li < p.M ? w * 16 + li : p.M - 1;
+        xo0 = *(const u32x4*)(p.XO + am * p.xo_pitch + q * 8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = q * 8 + e;
+            const uint16_t hv = t < nO ? from_f32<DT>((float)brow[p.O[t]]) : (uint16_t)0;
+            wo0[e >> 1] |= (uint32_t)hv << (16 * (e & 1));
+        }
+    }
+
     v4i acc[MG];
 #pragma unroll
     for (int g = 0; g < MG; ++g) acc[g] = v4i{0, 0, 0, 0};
-    // wave w takes step pairs w, w+4, w+8, ...; a batch holds kPairs pairs
-    for (int64_t p0 = w; 2 * p0 < nsteps; p0 += kWaves * kPairs) {
-        v4i b[2 * kPairs], a[2 * kPairs][MG];
+    // wave w takes step pairs w, w+4, w+8, ...; batch j of the wave holds pairs
+    // w + kWaves * (PAIRS * j + i), i < PAIRS
+    const int64_t stride = (int64_t)kWaves * PAIRS;
+    auto load = [&](int64_t p0, v4i (&b)[U], v4i (&a)[U][MG]) {
 #pragma unroll
-        for (int u = 0; u < 2 * kPairs; ++u) {
-            const int64_t s = 2 * (p0 + (int64_t)kWaves * (u >> 1)) + (u & 1);
-            const int64_t k = s * 64 + q * 16;
-            const bool in = s < nsteps;
+        for (int u = 0; u < U; ++u) {
+            const int64_t st = 2 * (p0 + (int64_t)kWaves * (u >> 1)) + (u & 1);
+            const int64_t k = st * 64 + q * 16;
+            const bool in = st < nsteps;
             b[u] = (in && k < p.K) ? *(const v4i*)(brow + k) : v4i{0, 0, 0, 0};
 #pragma unroll
             for (int g = 0; g < MG; ++g) a[u][g] = in ? *(const v4i*)(arow[g] + k) : v4i{0, 0, 0, 0};
         }
+    };
+    auto compute = [&](const v4i (&b)[U], const v4i (&a)[U][MG]) {
 #pragma unroll
-        for (int u = 0; u < 2 * kPairs; ++u)
+        for (int u = 0; u < U; ++u)
 #pragma unroll
             for (int g = 0; g < MG; ++g) acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][g], b[u], acc[g], 0, 0, 0);
+    };
+    {
+        v4i b0[U], a0[U][MG], b1[U], a1[U][MG];
+        int64_t p0 = w;
+        if (2 * p0 < nsteps) load(p0, b0, a0);
+        while (2 * p0 < nsteps) {
+            const int64_t p1 = p0 + stride;
+            if (2 * p1 < nsteps) load(p1, b1, a1);
+            compute(b0, a0);
+            if (2 * p1 >= nsteps) break;
+            const int64_t p2 = p1 + stride;
+            if (2 * p2 < nsteps) load(p2, b0, a0);
+            compute(b1, a1);
+            p0 = p2;
+        }
     }
 #pragma unroll
     for (int g = 0; g < MG; ++g) red[w][g][lane] = acc[g];
@@ -88,12 +128,12 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(SmallParams p) {
     // ---- wave g: rows 16g.., exact sum of the four partials, outlier product, epilogue
     const int g = w;
     const v4i c = red[0][g][lane] + red[1][g][lane] + red[2][g][lane] + red[3][g][lane];
-    const int32_t nO = *p.n_out;
     v4f F = v4f{0.f, 0.f, 0.f, 0.f};
+    if (nO > 0) F = mfma16x16<DT>(xo0, u32x4{wo0[0], wo0[1], wo0[2], wo0[3]}, F);
     {
         const int64_t am = g * 16 + li < p.M ? g * 16 + li : p.M - 1;
         const uint16_t* xo = p.XO + am * p.xo_pitch + q * 8;
-        for (int t0 = 0; t0 < nO; t0 += 32) {
+        for (int t0 = 32; t0 < nO; t0 += 32) {
             const u32x4 av = *(const u32x4*)(xo + t0);  // zero-padded to a multiple of 32
             u32x4 bv = {0u, 0u, 0u, 0u};
 #pragma unroll
