@@ -60,6 +60,8 @@ def _load():
             "orc_int_gemm": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P]),
             "orc_outlier_gemm": (None, [_P, _I64, ctypes.c_int, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P]),
             "orc_dequant": (None, [_P, _P, _P, _P, _I64, _I64, ctypes.c_int, _P, _P]),
+            "orc_block_quantize": (None, [_P, _I64, _I64, _P, _P]),
+            "orc_block_dequantize": (None, [_P, _P, _I64, _I64, _P]),
         }
         _SIGS.update(sig)
         for name, (res, args) in sig.items():
@@ -228,3 +230,25 @@ def matmul(X: np.ndarray, dt: str, Wq: np.ndarray, s_w: np.ndarray, tau: float, 
     F, F64, A = outlier_gemm(XO, O, dt, Wq, r)
     y, Y = dequant(C, F, s_x[r], s_w, dt)
     return dict(O=O, Xq=Xq, s_x=s_x, XO=XO, rows=r, C=C, F=F, F64=F64, A=A, y=y, Y=Y)
+
+
+def block_quantize(x: np.ndarray, block: int):
+    """Block-wise absmax int8 code of a flat fp32 array -> (q int8[n], absmax fp32[ceil(n/block)])."""
+    x = _c(np.ravel(x), np.float32)
+    n = x.size
+    nb = -(-n // block) if n else 0
+    q = np.zeros(n, np.int8)
+    absmax = np.zeros(nb, np.float32)
+    if n:
+        _load().orc_block_quantize(_p(x), n, block, _p(q), _p(absmax))
+    return q, absmax
+
+
+def block_dequantize(q: np.ndarray, absmax: np.ndarray, block: int) -> np.ndarray:
+    """Decode of block_quantize: x' = RN32(q * RN32(absmax / 127)) per block."""
+    q = _c(np.ravel(q), np.int8)
+    absmax = _c(absmax, np.float32)
+    x = np.zeros(q.size, np.float32)
+    if q.size:
+        _load().orc_block_dequantize(_p(q), _p(absmax), q.size, block, _p(x))
+    return x

@@ -246,3 +246,33 @@ void orc_dequant(const int32_t* C, const float* F, const float* s_x_rows, const 
         }
     }
 }
+
+/* ------------------------------------------------------- block-wise codec */
+
+void orc_block_quantize(const float* x, int64_t n, int64_t block, int8_t* q, float* absmax) {
+    int64_t nb = (n + block - 1) / block;
+    int nt = nthreads();
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t b = 0; b < nb; ++b) {
+        int64_t lo = b * block, hi = lo + block < n ? lo + block : n;
+        float s = 0.0f;
+        for (int64_t i = lo; i < hi; ++i) {
+            float a = fabsf(x[i]);
+            if (a > s) s = a;
+        }
+        absmax[b] = s;
+        float inv = orc_inv_scale(s);
+        for (int64_t i = lo; i < hi; ++i) q[i] = orc_quantize(x[i], inv);
+    }
+}
+
+void orc_block_dequantize(const int8_t* q, const float* absmax, int64_t n, int64_t block, float* x) {
+    int64_t nb = (n + block - 1) / block;
+    int nt = nthreads();
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t b = 0; b < nb; ++b) {
+        int64_t lo = b * block, hi = lo + block < n ? lo + block : n;
+        float step = absmax[b] / 127.0f;
+        for (int64_t i = lo; i < hi; ++i) x[i] = (float)q[i] * step;
+    }
+}

@@ -85,6 +85,16 @@ void orc_outlier_gemm(const uint16_t* XO, int64_t nO, int dt, const int8_t* Wq, 
 void orc_dequant(const int32_t* C, const float* F, const float* s_x_rows, const float* s_w,
                  int64_t nrows, int64_t N, int dt, float* y, uint16_t* Y);
 
+/* Block-wise absmax int8 codec of a flat fp32 tensor ("llama3-model-quantization" talk
+ * summary, Key Points, 8-bit optimizers: the state is cut into blocks, each block is
+ * normalised by its own maximum and stored as 8-bit values; the linear code is read, the
+ * same quantizer as above).  Block b = elements [b*block, min((b+1)*block, n)):
+ *   absmax[b] = max |x| over the block,
+ *   q = clamp(rne(RN32(x * RN32(127 / absmax[b]))), -127, 127)   (absmax 0: q = 0),
+ *   decode: x' = RN32((float)q * RN32(absmax[b] / 127)). */
+void orc_block_quantize(const float* x, int64_t n, int64_t block, int8_t* q, float* absmax);
+void orc_block_dequantize(const int8_t* q, const float* absmax, int64_t n, int64_t block, float* x);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,7 @@ import oracle
 from tests import test_oracle_formats as tf
 from tests import test_oracle_pipeline as tp
 from tests import test_oracle_quantizer as tq
+from tests import test_oracle_codec as tc
 
 MUTANTS = {
     "ties_away_from_zero": ("float v = rintf(x * inv);", "float v = roundf(x * inv);"),
@@ -27,6 +28,11 @@ MUTANTS = {
     "weight_transposed": ("Wq[n * K + k] = orc_quantize(orc_to_f32(W[k * N + n], dt), inv[n - nb]);",
                           "Wq[n * K + k] = orc_quantize(orc_to_f32(W[(k * N + n) % (K * N)], dt), inv[(n * 7) % (ne - nb)]);"),
     "int_gemm_transposed": ("const int8_t* w = Wq + n * K;", "const int8_t* w = Wq + ((n + 1) % N) * K;"),
+    "codec_block_end_off_by_one": ("int64_t lo = b * block, hi = lo + block < n ? lo + block : n;\n        float s = 0.0f;",
+                                   "int64_t lo = b * block, hi = lo + block - 1 < n ? lo + block - 1 : n;\n        float s = 0.0f;"),
+    "codec_scale_first_element": ("            if (a > s) s = a;\n        }\n        absmax[b] = s;",
+                                  "            if (a > s && i == lo) s = a;\n        }\n        absmax[b] = s;"),
+    "codec_decode_128": ("float step = absmax[b] / 127.0f;", "float step = absmax[b] / 128.0f;"),
 }
 
 PINS = [
@@ -40,6 +46,9 @@ PINS = [
     tp.test_int_gemm_against_numpy_int64,
     tp.test_epilogue_closed_form_on_lattice,
     tp.test_outlier_gemm_exact_on_integers_and_close_to_float64,
+    lambda: tc.test_codec_lattice_round_trip_is_exact(64),
+    lambda: tc.test_codec_blocks_use_the_scalar_quantizer(64),
+    lambda: tc.test_codec_error_bound_and_range(256),
 ]
 
 
