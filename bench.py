@@ -272,6 +272,71 @@ def trace_summary(trace_dir: str, bench_json: str, wl, cmd: str) -> int:
     return 0
 
 
+def codec_bench(args) -> int:
+    """The block-wise absmax int8 codec on a 2^28-element fp32 optimizer state (blocks of
+    2048): quantize and dequantize timed back to back (HIP events on the current stream),
+    algorithmic bytes 4n + n + 4 n/block (quantize) and n + 4n + 4 n/block (dequantize)."""
+    import numpy as np
+    import torch
+
+    import int8_quantized_matmul_rowwise_amd as lm
+    import oracle
+    import workloads
+
+    wl = workloads.CODEC_WORKLOAD
+    n, block = wl["n"], wl["block"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"codec workload {wl['name']}: n = {n}, block {block}")
+    x = workloads.make_state(n, seed=0)
+    xd = x.to(dev)
+    q, a = lm.int8_blockwise_quantize(xd, block)
+    xr = lm.int8_blockwise_dequantize(q, a, block)
+    for _ in range(args.warmup):
+        lm.int8_blockwise_quantize(xd, block, q=q, absmax=a)
+        lm.int8_blockwise_dequantize(q, a, block, x=xr)
+    ms_q = time_loop(lambda: lm.int8_blockwise_quantize(xd, block, q=q, absmax=a), args.steps, torch)
+    ms_d = time_loop(lambda: lm.int8_blockwise_dequantize(q, a, block, x=xr), args.steps, torch)
+    nb = -(-n // block)
+    bq = 5.0 * n + 4.0 * nb
+    gbs_q = bq / (ms_q * 1e-3) / 1e9
+    gbs_d = bq / (ms_d * 1e-3) / 1e9
+    log(f"quantize {ms_q * 1e3:.1f} us = {gbs_q:.0f} GB/s; dequantize {ms_d * 1e3:.1f} us = {gbs_d:.0f} GB/s")
+    # the oracle on a bounded sample (2^24 elements), on all host threads
+    cores = oracle.set_threads(min(int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count()), os.cpu_count()))
+    xs = x[: 1 << 24].numpy()
+    t0 = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < args.cpu_seconds / 2 or reps == 0:
+        qs, as_ = oracle.block_quantize(xs, block)
+        oracle.block_dequantize(qs, as_, block)
+        reps += 1
+    t_cpu = (time.perf_counter() - t0) / reps
+    line = {
+        "metric": "GB/s of the block-wise absmax int8 codec (quantize + dequantize of an fp32 tensor)",
+        "value": 2 * bq / ((ms_q + ms_d) * 1e-3) / 1e9,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_q + ms_d,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl["name"], "n": n, "block": block},
+        "roofline": {"bound": "hbm", "achieved": gbs_q, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs_q / HBM_PEAK_GBS, "traffic": None, "kernel": "block_quantize_kernel",
+                     "kernel_ms": ms_q, "dequantize_ms": ms_d, "dequantize_gbs": gbs_d},
+        "cpu_baseline": {"value": 2 * (5.0 * xs.size + 4.0 * (-(-xs.size // block))) / t_cpu / 1e9, "unit": "GB/s",
+                         "cores": cores, "kind": "oracle",
+                         "sample": f"quantize + dequantize of the first 2^24 elements, {reps} times"},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 # ---------------------------------------------------------------------------------------
 
 def main() -> int:
@@ -288,6 +353,8 @@ def main() -> int:
                     help="before the steps, run a plain copy-shaped kernel over this many MiB (counter calibration)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarize two rocprofv3 counter runs into the stored traffic record and exit")
+    ap.add_argument("--codec", action="store_true",
+                    help="benchmark the block-wise int8 codec instead (its own JSON line)")
     ap.add_argument("--trace-summary", nargs=3, metavar=("TRACE_DIR", "BENCH_OUT", "COMMAND"),
                     help="summarize a rocprofv3 --kernel-trace --stats run of this script and exit")
     args = ap.parse_args()
@@ -303,6 +370,9 @@ def main() -> int:
         print(f"bench.py: one GPU only; --gpus {args.gpus} is not supported (the library has no multi-GPU "
               f"path: each GPU would run the same kernels on its own column shard)", file=sys.stderr)
         return 2
+
+    if args.codec:
+        return codec_bench(args)
 
     import torch
 

@@ -160,6 +160,27 @@ int int8_matmul_accumulators(const void* X, int64_t M, int64_t K, int dtype,
                              int32_t* C, float* F,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Block-wise absmax int8 codec of a flat fp32 tensor ("llama3-model-quantization" talk
+ * summary, Key Points, 8-bit optimizers: the optimizer state is cut into blocks, each
+ * block is normalised by its own maximum and kept as 8-bit values; the linear code is
+ * read, with the quantizer of the matmul above).  Block b holds elements
+ * [b*block, min((b+1)*block, n)) (the last block may be short):
+ *   absmax[b] = max |x| over the block (fp32),
+ *   q[i] = clamp(round_half_even(RN32(x[i] * RN32(127 / absmax[b]))), -127, 127)
+ *          (absmax 0: q = 0),
+ *   decode x'[i] = RN32((float)q[i] * RN32(absmax[b] / 127)).
+ *   x       : n fp32 values (device), 16-byte aligned.
+ *   q       : n int8 codes (device), 4-byte aligned.
+ *   absmax  : ceil(n / block) fp32 (device), 4-byte aligned.
+ *   block   : a power of two in [64, 4096], else LLMINT8_EINVAL.
+ * n = 0 is a no-op.  Inputs and outputs must not overlap (LLMINT8_EINVAL).  Non-finite
+ * values are outside the contract.
+ */
+int int8_blockwise_quantize(const float* x, int64_t n, int64_t block, int8_t* q, float* absmax, void* stream);
+int int8_blockwise_dequantize(const int8_t* q, const float* absmax, int64_t n, int64_t block, float* x,
+                              void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -55,6 +55,8 @@ _SIGNATURES = {
     "int8_matmul_accumulators": (_I, [_P, _I64, _I64, _I, _P, _I64, _F, _P, _P, _P, _SZ, _P]),
     "int8_matmul_prepare": (_I, [_P, _I64, _I64, _I, _P, _I64, _F, _P, _SZ, _P]),
     "int8_matmul_products": (_I, [_I64, _I64, _I, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "int8_blockwise_quantize": (_I, [_P, _I64, _I64, _P, _P, _P]),
+    "int8_blockwise_dequantize": (_I, [_P, _P, _I64, _I64, _P, _P]),
 }
 
 _lib = None
@@ -247,8 +249,45 @@ def workspace_views(ws: torch.Tensor, M: int, K: int, N: int, dtype: torch.dtype
     }
 
 
+def int8_blockwise_quantize(x: torch.Tensor, block: int = 2048, q: Optional[torch.Tensor] = None,
+                            absmax: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Block-wise absmax int8 code of an fp32 tensor, taken flat: (q int8 of x's shape,
+    absmax fp32[ceil(numel / block)])."""
+    _dev_tensor(x, "x", torch.float32)
+    n = x.numel()
+    nb = -(-n // block) if block > 0 else 0
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.int8, device=x.device)
+    if absmax is None:
+        absmax = torch.empty(nb, dtype=torch.float32, device=x.device)
+    _dev_tensor(q, "q", torch.int8)
+    _dev_tensor(absmax, "absmax", torch.float32)
+    if q.numel() != n or absmax.numel() != nb:
+        raise ValueError("q must hold numel(x) codes and absmax ceil(numel / block) scales")
+    _check(lib().int8_blockwise_quantize(_ptr(x), n, int(block), _ptr(q), _ptr(absmax), _stream(x, stream)),
+           "int8_blockwise_quantize")
+    return q, absmax
+
+
+def int8_blockwise_dequantize(q: torch.Tensor, absmax: torch.Tensor, block: int = 2048,
+                              x: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode of int8_blockwise_quantize: fp32 of q's shape."""
+    _dev_tensor(q, "q", torch.int8)
+    _dev_tensor(absmax, "absmax", torch.float32)
+    n = q.numel()
+    if x is None:
+        x = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    _dev_tensor(x, "x", torch.float32)
+    if x.numel() != n or absmax.numel() != (-(-n // block) if block > 0 else 0):
+        raise ValueError("x must hold numel(q) values and absmax ceil(numel / block) scales")
+    _check(lib().int8_blockwise_dequantize(_ptr(q), _ptr(absmax), n, int(block), _ptr(x), _stream(q, stream)),
+           "int8_blockwise_dequantize")
+    return x
+
+
 __all__ = [
     "int8_quantize_weight", "int8_matmul", "int8_matmul_stats", "int8_matmul_prepare", "int8_matmul_products", "int8_matmul_workspace_bytes",
     "int8_matmul_workspace_layout", "int8_matmul_accumulators", "workspace_views", "LLMInt8Error", "lib",
+    "int8_blockwise_quantize", "int8_blockwise_dequantize",
     "status_string",
 ]

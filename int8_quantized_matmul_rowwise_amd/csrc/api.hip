@@ -305,3 +305,28 @@ LLMINT8_API int int8_matmul_products(int64_t M, int64_t K, int dtype, const int8
     return products_common(M, K, dtype, Wq, w_scale, N, Y, nullptr, nullptr, workspace, workspace_bytes, stream,
                            true);
 }
+
+// ---- block-wise absmax int8 codec
+
+LLMINT8_API int int8_blockwise_quantize(const float* x, int64_t n, int64_t block, int8_t* q, float* absmax,
+                                        void* stream) {
+    if (n < 0 || !codec_block_ok(block)) return LLMINT8_EINVAL;
+    if (n == 0) return LLMINT8_OK;
+    const int64_t nb = ceil_div(n, block);
+    if (!x || !q || !absmax || !aligned(x, 16) || !aligned(q, 4) || !aligned(absmax, 4)) return LLMINT8_EINVAL;
+    if (overlap(x, (size_t)n * 4, q, (size_t)n) || overlap(x, (size_t)n * 4, absmax, (size_t)nb * 4) ||
+        overlap(q, (size_t)n, absmax, (size_t)nb * 4))
+        return LLMINT8_EINVAL;
+    return hip_status(launch_block_quantize(x, n, block, q, absmax, (hipStream_t)stream));
+}
+
+LLMINT8_API int int8_blockwise_dequantize(const int8_t* q, const float* absmax, int64_t n, int64_t block, float* x,
+                                          void* stream) {
+    if (n < 0 || !codec_block_ok(block)) return LLMINT8_EINVAL;
+    if (n == 0) return LLMINT8_OK;
+    const int64_t nb = ceil_div(n, block);
+    if (!x || !q || !absmax || !aligned(x, 16) || !aligned(q, 4) || !aligned(absmax, 4)) return LLMINT8_EINVAL;
+    if (overlap(x, (size_t)n * 4, q, (size_t)n) || overlap(x, (size_t)n * 4, absmax, (size_t)nb * 4))
+        return LLMINT8_EINVAL;
+    return hip_status(launch_block_dequantize(q, absmax, n, block, x, (hipStream_t)stream));
+}

@@ -67,4 +67,11 @@ struct GemmArgs {
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_small(const GemmArgs& a, hipStream_t stream);
 
+// ---- block-wise absmax int8 codec of a flat fp32 tensor
+bool codec_block_ok(int64_t block);  // a power of two in [64, 4096]
+hipError_t launch_block_quantize(const float* x, int64_t n, int64_t block, int8_t* q, float* absmax,
+                                 hipStream_t stream);
+hipError_t launch_block_dequantize(const int8_t* q, const float* absmax, int64_t n, int64_t block, float* x,
+                                   hipStream_t stream);
+
 }  // namespace llmint8

@@ -106,3 +106,23 @@ def test_binding_fails_loudly_without_gpu_tensors():
     with pytest.raises(TypeError):
         L.int8_matmul(torch.zeros(4, 64, dtype=torch.float16), torch.zeros(8, 64, dtype=torch.int8),
                       torch.zeros(8), 6.0)
+
+
+def test_blockwise_codec_rejects():
+    qz, dq = L.lib().int8_blockwise_quantize, L.lib().int8_blockwise_dequantize
+    X, Q, S = A16, A16 * 64, A16 * 128  # disjoint fake device buffers for n = 4096
+    for block in (0, 32, 96, 100, 8192, -64):
+        assert qz(X, 4096, block, Q, S, None) == L.EINVAL
+        assert dq(Q, S, 4096, block, X, None) == L.EINVAL
+    assert qz(X, -1, 2048, Q, S, None) == L.EINVAL
+    assert qz(None, 4096, 2048, Q, S, None) == L.EINVAL
+    assert qz(X, 4096, 2048, None, S, None) == L.EINVAL
+    assert qz(X, 4096, 2048, Q, None, None) == L.EINVAL
+    assert qz(X + 8, 4096, 2048, Q, S, None) == L.EINVAL        # x not 16-byte aligned
+    assert qz(X, 4096, 2048, Q + 2, S, None) == L.EINVAL        # q not 4-byte aligned
+    assert qz(X, 4096, 2048, X + 64, S, None) == L.EINVAL       # q overlaps x
+    assert qz(X, 4096, 2048, Q, Q + 1024, None) == L.EINVAL     # absmax overlaps q
+    assert dq(Q, S, 4096, 2048, Q - 64, None) == L.EINVAL       # x overlaps q
+    assert dq(Q, S, 4096, 2048, X + 4, None) == L.EINVAL        # x not 16-byte aligned
+    assert qz(None, 0, 2048, None, None, None) == L.OK           # empty: nothing to do
+    assert dq(None, None, 0, 64, None, None) == L.OK

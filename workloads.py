@@ -126,3 +126,22 @@ def bits(t: torch.Tensor) -> np.ndarray:
 def from_bits(b: np.ndarray, dtype: str) -> torch.Tensor:
     """Inverse of bits(): a CPU tensor of the given 16-bit dtype over the same patterns."""
     return torch.from_numpy(np.ascontiguousarray(b).view(np.int16)).view(DTYPES[dtype])
+
+
+# ---- inputs of the block-wise codec: a flat fp32 optimizer-state-like tensor
+
+CODEC_WORKLOAD = {"name": "adam_state", "n": 1 << 28, "block": 2048,
+                  "description": "a 2^28-element fp32 optimizer state (1 GiB), blocks of 2048"}
+
+
+def make_state(n: int, seed: int = 0, sigma: float = 1e-3, tail: float = 1e-3) -> torch.Tensor:
+    """fp32 values ~ N(0, sigma) with a thin tail (a fraction `tail`) of entries of magnitude
+    U(0.01, 0.5) and random sign: the spread of an Adam moment, whose rare large entries are
+    what block-wise scaling is for.  Seeded torch CPU generator (tensor id 7)."""
+    g = _gen(seed, 90, 7)
+    x = torch.randn(n, generator=g, dtype=torch.float32) * sigma
+    k = torch.rand(n, generator=g) < tail
+    nk = int(k.sum())
+    sign = torch.where(torch.rand(nk, generator=g) < 0.5, -1.0, 1.0)
+    x[k] = sign * (0.01 + 0.49 * torch.rand(nk, generator=g))
+    return x
