@@ -60,6 +60,9 @@ def _load():
             "orc_int_gemm": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _I64, _P]),
             "orc_outlier_gemm": (None, [_P, _I64, ctypes.c_int, _P, _I64, _I64, _P, _P, _I64, _P, _P, _P]),
             "orc_dequant": (None, [_P, _P, _P, _P, _I64, _I64, ctypes.c_int, _P, _P]),
+            "orc_quantize_weight_fixed": (None, [_P, _I64, _I64, ctypes.c_int, _P, _I64, _P, _P, _P]),
+            "orc_outlier_gemm_exact": (None, [_P, _I64, ctypes.c_int, _P, _I64, _P, _I64, _P, _P, _P]),
+            "orc_dequant_fixed": (None, [_P, _P, _P, _P, _I64, _I64, ctypes.c_int, _P, _P]),
             "orc_block_quantize": (None, [_P, _I64, _I64, _P, _P]),
             "orc_block_dequantize": (None, [_P, _P, _I64, _I64, _P]),
         }
@@ -252,3 +255,56 @@ def block_dequantize(q: np.ndarray, absmax: np.ndarray, block: int) -> np.ndarra
     if q.size:
         _load().orc_block_dequantize(_p(q), _p(absmax), q.size, block, _p(x))
     return x
+
+
+# ---- fixed (caller-supplied) outlier dimensions
+
+def quantize_weight_fixed(W: np.ndarray, dt: str, O: np.ndarray):
+    """Weight conversion with the outlier set O fixed: (Wq N x K, s_w[N], WO N x nO exact 16-bit)."""
+    W = _c(W, np.uint16)
+    K, N = W.shape
+    O = _c(O, np.int32)
+    Wq = np.zeros((N, K), np.int8)
+    s_w = np.zeros(N, np.float32)
+    WO = np.zeros((N, O.size), np.uint16)
+    _load().orc_quantize_weight_fixed(_p(W), K, N, DT[dt], _p(O), O.size, _p(Wq), _p(s_w), _p(WO))
+    return Wq, s_w, WO
+
+
+def outlier_gemm_exact(XO: np.ndarray, dt: str, WO: np.ndarray, rows=None):
+    """F = X[:,O] W_O^T with the exact 16-bit W rows (fp32, t ascending); also F64 and A."""
+    XO = _c(XO, np.uint16)
+    WO = _c(WO, np.uint16)
+    M, nO = XO.shape
+    N = WO.shape[0]
+    r, nr = _rows(rows, M)
+    F = np.zeros((nr, N), np.float32)
+    F64 = np.zeros((nr, N), np.float64)
+    A = np.zeros((nr, N), np.float64)
+    _load().orc_outlier_gemm_exact(_p(XO), nO, DT[dt], _p(WO), N, _p(r), nr, _p(F), _p(F64), _p(A))
+    return F, F64, A
+
+
+def dequant_fixed(C: np.ndarray, F: np.ndarray, s_x_rows: np.ndarray, s_w: np.ndarray, dt: str):
+    """Epilogue of the fixed-outlier product: y = RN(RN(RN(C r) c) + F); returns (y, Y bits)."""
+    C = _c(C, np.int32)
+    F = _c(F, np.float32)
+    nr, N = C.shape
+    y = np.zeros((nr, N), np.float32)
+    Y = np.zeros((nr, N), np.uint16)
+    _load().orc_dequant_fixed(_p(C), _p(F), _p(_c(s_x_rows, np.float32)), _p(_c(s_w, np.float32)), nr, N, DT[dt],
+                              _p(y), _p(Y))
+    return y, Y
+
+
+def matmul_fixed(X: np.ndarray, dt: str, Wq: np.ndarray, s_w: np.ndarray, WO: np.ndarray, O: np.ndarray,
+                 rows=None) -> dict:
+    """The whole fixed-outlier product of the oracle (X pass against O, int8 and exact 16-bit
+    parts, epilogue) for the given rows (None: all)."""
+    O = _c(O, np.int32)
+    Xq, s_x, XO = quantize_rows(X, dt, O)
+    rr = np.arange(X.shape[0]) if rows is None else np.asarray(rows, np.int64)
+    C = int_gemm(Xq, Wq, rr)
+    F, F64, A = outlier_gemm_exact(XO, dt, WO, rr)
+    y, Y = dequant_fixed(C, F, s_x[rr], s_w, dt)
+    return dict(O=O, Xq=Xq, s_x=s_x, XO=XO, rows=rr, C=C, F=F, F64=F64, A=A, y=y, Y=Y)

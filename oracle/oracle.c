@@ -247,6 +247,67 @@ void orc_dequant(const int32_t* C, const float* F, const float* s_x_rows, const 
     }
 }
 
+/* ------------------------------------------------ fixed outlier dimensions */
+
+void orc_quantize_weight_fixed(const uint16_t* W, int64_t K, int64_t N, int dt, const int32_t* O, int64_t nO,
+                               int8_t* Wq, float* s_w, uint16_t* WO) {
+    unsigned char* is_out = (unsigned char*)calloc((size_t)(K > 0 ? K : 1), 1);
+    for (int64_t t = 0; t < nO; ++t) is_out[O[t]] = 1;
+    int nt = nthreads();
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        float s = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            if (is_out[k]) continue;
+            float a = fabsf(orc_to_f32(W[k * N + n], dt));
+            if (a > s) s = a;
+        }
+        s_w[n] = s;
+        float inv = orc_inv_scale(s);
+        for (int64_t k = 0; k < K; ++k)
+            Wq[n * K + k] = is_out[k] ? 0 : orc_quantize(orc_to_f32(W[k * N + n], dt), inv);
+        for (int64_t t = 0; t < nO; ++t) WO[n * nO + t] = W[(int64_t)O[t] * N + n];
+    }
+    free(is_out);
+}
+
+void orc_outlier_gemm_exact(const uint16_t* XO, int64_t nO, int dt, const uint16_t* WO, int64_t N,
+                            const int64_t* rows, int64_t nrows, float* F, double* F64, double* A) {
+    int nt = nthreads();
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const uint16_t* xo = XO + (rows ? rows[r] : r) * nO;
+        for (int64_t n = 0; n < N; ++n) {
+            float sum = 0.0f;
+            double sum64 = 0.0, mag = 0.0;
+            for (int64_t t = 0; t < nO; ++t) {
+                float prod = orc_to_f32(xo[t], dt) * orc_to_f32(WO[n * nO + t], dt); /* exact: <= 22 bits */
+                sum = sum + prod;
+                sum64 += (double)prod;
+                mag += fabs((double)prod);
+            }
+            F[r * N + n] = sum;
+            if (F64) F64[r * N + n] = sum64;
+            if (A) A[r * N + n] = mag;
+        }
+    }
+}
+
+void orc_dequant_fixed(const int32_t* C, const float* F, const float* s_x_rows, const float* s_w,
+                       int64_t nrows, int64_t N, int dt, float* y, uint16_t* Y) {
+    for (int64_t r = 0; r < nrows; ++r) {
+        float ri = s_x_rows[r] / 127.0f;
+        for (int64_t n = 0; n < N; ++n) {
+            float cn = s_w[n] / 127.0f;
+            float cf = (float)C[r * N + n];
+            float y_int = (cf * ri) * cn;
+            float v = y_int + F[r * N + n];
+            if (y) y[r * N + n] = v;
+            Y[r * N + n] = orc_from_f32(v, dt);
+        }
+    }
+}
+
 /* ------------------------------------------------------- block-wise codec */
 
 void orc_block_quantize(const float* x, int64_t n, int64_t block, int8_t* q, float* absmax) {

@@ -85,6 +85,26 @@ void orc_outlier_gemm(const uint16_t* XO, int64_t nO, int dt, const int8_t* Wq, 
 void orc_dequant(const int32_t* C, const float* F, const float* s_x_rows, const float* s_w,
                  int64_t nrows, int64_t N, int dt, float* y, uint16_t* Y);
 
+/* Fixed outlier dimensions (caller-supplied, e.g. found offline: the talk summary,
+ * "Understanding Outliers in Transformer Models", calls the outlier dimensions systematic
+ * and context-independent; the HN discussion on the "LLM.int8()" page describes the
+ * outliers as kept in their original precision).  O: n_O distinct column indices of X /
+ * row indices of W, ascending.
+ * Weight conversion with O fixed: s_w[n] = max over k not in O of |W[k,n]|; Wq[n,k] = 0
+ * for k in O, else the code above; WO[n * nO + t] = W[O[t], n] (exact 16-bit copy). */
+void orc_quantize_weight_fixed(const uint16_t* W, int64_t K, int64_t N, int dt, const int32_t* O, int64_t nO,
+                               int8_t* Wq, float* s_w, uint16_t* WO);
+
+/* Outlier product with the exact 16-bit rows: F[r,n] = sum over t ascending of
+ * (float)XO[row r, t] * (float)WO[n, t] in fp32 (each product exact), F64 in double, A the
+ * sum of |products|. */
+void orc_outlier_gemm_exact(const uint16_t* XO, int64_t nO, int dt, const uint16_t* WO, int64_t N,
+                            const int64_t* rows, int64_t nrows, float* F, double* F64, double* A);
+
+/* Epilogue with the unscaled outlier part: y = RN32(RN32(RN32((float)C * r_i) * c_n) + F). */
+void orc_dequant_fixed(const int32_t* C, const float* F, const float* s_x_rows, const float* s_w,
+                       int64_t nrows, int64_t N, int dt, float* y, uint16_t* Y);
+
 /* Block-wise absmax int8 codec of a flat fp32 tensor ("llama3-model-quantization" talk
  * summary, Key Points, 8-bit optimizers: the state is cut into blocks, each block is
  * normalised by its own maximum and stored as 8-bit values; the linear code is read, the

@@ -13,6 +13,7 @@ from tests import test_oracle_formats as tf
 from tests import test_oracle_pipeline as tp
 from tests import test_oracle_quantizer as tq
 from tests import test_oracle_codec as tc
+from tests import test_oracle_fixed as tfx
 
 MUTANTS = {
     "ties_away_from_zero": ("float v = rintf(x * inv);", "float v = roundf(x * inv);"),
@@ -33,6 +34,11 @@ MUTANTS = {
     "codec_scale_first_element": ("            if (a > s) s = a;\n        }\n        absmax[b] = s;",
                                   "            if (a > s && i == lo) s = a;\n        }\n        absmax[b] = s;"),
     "codec_decode_128": ("float step = absmax[b] / 127.0f;", "float step = absmax[b] / 128.0f;"),
+    "fixed_outlier_part_scaled": ("float v = y_int + F[r * N + n];", "float v = y_int + cn * F[r * N + n];"),
+    "fixed_scale_over_all_rows": ("            if (is_out[k]) continue;\n            float a = fabsf(orc_to_f32(W[k * N + n], dt));",
+                                  "            float a = fabsf(orc_to_f32(W[k * N + n], dt));"),
+    "fixed_rows_from_codes": ("WO[n * nO + t] = W[(int64_t)O[t] * N + n];",
+                              "WO[n * nO + t] = orc_from_f32((float)Wq[n * K + O[t]], dt);"),
 }
 
 PINS = [
@@ -49,6 +55,9 @@ PINS = [
     lambda: tc.test_codec_lattice_round_trip_is_exact(64),
     lambda: tc.test_codec_blocks_use_the_scalar_quantizer(64),
     lambda: tc.test_codec_error_bound_and_range(256),
+    tfx.test_fixed_lattice_closed_form,
+    tfx.test_fixed_weight_conversion_uses_the_scalar_quantizer,
+    tfx.test_fixed_all_columns_is_the_16bit_product,
 ]
 
 
