@@ -161,6 +161,40 @@ int int8_matmul_accumulators(const void* X, int64_t M, int64_t K, int dtype,
                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Fixed (caller-supplied) outlier dimensions.  The outlier feature dimensions are
+ * systematic and context-independent (talk summary "llama3-model-quantization",
+ * "Understanding Outliers in Transformer Models"), so a caller may fix the set O offline
+ * (for example from calibration) instead of detecting it per call; their rows of W are
+ * then kept in 16 bits (the HN discussion on the "LLM.int8()" page: outliers kept in
+ * their original precision).  O: n_O column indices of X (= row indices of W), strictly
+ * ascending, in [0, K) -- otherwise the result is undefined (entries outside [0, K) are
+ * ignored; no access leaves the buffers).  W_O: N x P 16-bit, P = n_O rounded up to a
+ * multiple of 32, row-major, zero past n_O.
+ *
+ * Weight conversion: s_w[n] = max over k not in O of |W[k,n]|; Wq[n,k] = 0 for k in O,
+ * else the code of the conversion above; W_O[n,t] = W[O[t], n] exactly.
+ *   outlier_cols  device int32[n_O], 4-byte aligned; n_outlier_cols in [0, K].
+ *   workspace     >= int8_quantize_weight_fixed_workspace_bytes(K) bytes, 16-byte aligned.
+ */
+size_t int8_quantize_weight_fixed_workspace_bytes(int64_t K);
+int int8_quantize_weight_fixed(const void* W, int64_t K, int64_t N, int dtype, const int32_t* outlier_cols,
+                               int64_t n_outlier_cols, int8_t* Wq, float* w_scale, void* W_O, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * The product with the fixed set: no detection; the X pass codes every row against O (s_x
+ * over the columns not in O, Xq zero on O, X[:,O] gathered), then
+ *   y = RN32( RN32( RN32((float)C * r_i) * c_n ) + F ),   F = X[:,O] W_O^T
+ * (16-bit inputs, fp32 accumulation; the exact W rows, so the term is not scaled by c_n).
+ * Arguments as int8_matmul, plus outlier_cols / n_outlier_cols / W_O as above; the
+ * workspace is int8_matmul_workspace_bytes(M, K, N) and afterwards holds the X pass's
+ * products (its W_O region is unused).  No threshold is involved.
+ */
+int int8_matmul_fixed(const void* X, int64_t M, int64_t K, int dtype, const int32_t* outlier_cols,
+                      int64_t n_outlier_cols, const int8_t* Wq, const float* w_scale, const void* W_O, int64_t N,
+                      void* Y, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Block-wise absmax int8 codec of a flat fp32 tensor ("llama3-model-quantization" talk
  * summary, Key Points, 8-bit optimizers: the optimizer state is cut into blocks, each
  * block is normalised by its own maximum and kept as 8-bit values; the linear code is

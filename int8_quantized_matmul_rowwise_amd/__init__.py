@@ -55,6 +55,9 @@ _SIGNATURES = {
     "int8_matmul_accumulators": (_I, [_P, _I64, _I64, _I, _P, _I64, _F, _P, _P, _P, _SZ, _P]),
     "int8_matmul_prepare": (_I, [_P, _I64, _I64, _I, _P, _I64, _F, _P, _SZ, _P]),
     "int8_matmul_products": (_I, [_I64, _I64, _I, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "int8_quantize_weight_fixed_workspace_bytes": (_SZ, [_I64]),
+    "int8_quantize_weight_fixed": (_I, [_P, _I64, _I64, _I, _P, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "int8_matmul_fixed": (_I, [_P, _I64, _I64, _I, _P, _I64, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "int8_blockwise_quantize": (_I, [_P, _I64, _I64, _P, _P, _P]),
     "int8_blockwise_dequantize": (_I, [_P, _P, _I64, _I64, _P, _P]),
 }
@@ -249,6 +252,55 @@ def workspace_views(ws: torch.Tensor, M: int, K: int, N: int, dtype: torch.dtype
     }
 
 
+def _fixed_pitch(n_o: int) -> int:
+    return (n_o + 31) // 32 * 32
+
+
+def int8_quantize_weight_fixed(W: torch.Tensor, outlier_cols: torch.Tensor, stream=None):
+    """Weight conversion with a fixed outlier set (device int32, ascending):
+    (Wq N x K int8, w_scale fp32[N], W_O N x P 16-bit exact rows)."""
+    _dev_tensor(W, "W")
+    if W.dtype not in _DT or W.dim() != 2:
+        raise TypeError("W must be a 2-D fp16 or bf16 tensor")
+    _dev_tensor(outlier_cols, "outlier_cols", torch.int32)
+    K, N = W.shape
+    n_o = outlier_cols.numel()
+    Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    s_w = torch.empty(N, dtype=torch.float32, device=W.device)
+    W_O = torch.empty((N, _fixed_pitch(n_o)), dtype=W.dtype, device=W.device)
+    ws = torch.empty(max(int(lib().int8_quantize_weight_fixed_workspace_bytes(K)), 1), dtype=torch.uint8,
+                     device=W.device)
+    _check(lib().int8_quantize_weight_fixed(_ptr(W), K, N, _DT[W.dtype], _ptr(outlier_cols), n_o, _ptr(Wq), _ptr(s_w),
+                                            _ptr(W_O), _ptr(ws), ws.numel(), _stream(W, stream)),
+           "int8_quantize_weight_fixed")
+    return Wq, s_w, W_O
+
+
+def int8_matmul_fixed(X: torch.Tensor, outlier_cols: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor,
+                      W_O: torch.Tensor, Y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Y = X W with the fixed outlier set (no detection; exact 16-bit W rows on the set)."""
+    _dev_tensor(X, "X")
+    if X.dtype not in _DT or X.dim() != 2:
+        raise TypeError("X must be a 2-D fp16 or bf16 tensor")
+    _dev_tensor(outlier_cols, "outlier_cols", torch.int32)
+    _dev_tensor(Wq, "Wq", torch.int8)
+    _dev_tensor(w_scale, "w_scale", torch.float32)
+    _dev_tensor(W_O, "W_O", X.dtype)
+    M, K = X.shape
+    N = Wq.shape[0]
+    n_o = outlier_cols.numel()
+    if W_O.shape != (N, _fixed_pitch(n_o)):
+        raise ValueError("W_O must be N x (n_O rounded up to 32)")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    ws = _workspace(workspace, int8_matmul_workspace_bytes(M, K, N), X.device)
+    _check(lib().int8_matmul_fixed(_ptr(X), M, K, _DT[X.dtype], _ptr(outlier_cols), n_o, _ptr(Wq), _ptr(w_scale),
+                                   _ptr(W_O), N, _ptr(Y), _ptr(ws), ws.numel(), _stream(X, stream)),
+           "int8_matmul_fixed")
+    return Y
+
+
 def int8_blockwise_quantize(x: torch.Tensor, block: int = 2048, q: Optional[torch.Tensor] = None,
                             absmax: Optional[torch.Tensor] = None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Block-wise absmax int8 code of an fp32 tensor, taken flat: (q int8 of x's shape,
@@ -288,6 +340,6 @@ def int8_blockwise_dequantize(q: torch.Tensor, absmax: torch.Tensor, block: int 
 __all__ = [
     "int8_quantize_weight", "int8_matmul", "int8_matmul_stats", "int8_matmul_prepare", "int8_matmul_products", "int8_matmul_workspace_bytes",
     "int8_matmul_workspace_layout", "int8_matmul_accumulators", "workspace_views", "LLMInt8Error", "lib",
-    "int8_blockwise_quantize", "int8_blockwise_dequantize",
+    "int8_blockwise_quantize", "int8_blockwise_dequantize", "int8_quantize_weight_fixed", "int8_matmul_fixed",
     "status_string",
 ]

@@ -139,7 +139,7 @@ int prepare_common(const void* X, int64_t M, int64_t K, int dtype, const int8_t*
 // Products + epilogue (Y != NULL) or the accumulator dump (C, F) from a prepared workspace.
 int products_common(int64_t M, int64_t K, int dtype, const int8_t* Wq, const float* w_scale, int64_t N, void* Y,
                     int32_t* C, float* F, const void* workspace, size_t workspace_bytes, void* stream,
-                    bool enqueue) {
+                    bool enqueue, const void* WO_fixed = nullptr, int64_t wo_pitch_fixed = 0) {
     int rc = check_shape(M, K, N, dtype);
     if (rc) return rc;
     const bool acc = Y == nullptr;
@@ -172,8 +172,10 @@ int products_common(int64_t M, int64_t K, int dtype, const int8_t* Wq, const flo
     g.s_x = (const float*)(ws + L.s_x);
     g.s_w = w_scale;
     g.XO = ws + L.xo;
-    g.WO = ws + L.wo;
     g.xo_pitch = (int64_t)L.xo_pitch;
+    g.f_scaled = WO_fixed == nullptr;
+    g.WO = g.f_scaled ? (const void*)(ws + L.wo) : WO_fixed;
+    g.wo_pitch = g.f_scaled ? (int64_t)L.xo_pitch : wo_pitch_fixed;
     g.n_out = (const int32_t*)(ws + L.n_outliers);
     g.O = (const int32_t*)(ws + L.outliers);
     g.Y = Y;
@@ -182,6 +184,41 @@ int products_common(int64_t M, int64_t K, int dtype, const int8_t* Wq, const flo
     if (small_batch(M, K)) return hip_status(launch_gemm_small(g, (hipStream_t)stream));
     return hip_status(launch_gemm(g, (hipStream_t)stream));
 }
+
+// X pass against a caller's fixed outlier set: its bitmap (as one partial), the
+// compaction (O, n_O in the workspace), then the row coding; no W_O gather.
+int run_xpass_fixed(const void* X, int64_t M, int64_t K, int dtype, const int32_t* Ofix, int64_t nO, int8_t* ws,
+                    const Layout& L, hipStream_t st) {
+    uint32_t* partial = (uint32_t*)(ws + L.partial);
+    uint32_t* bitmap = (uint32_t*)(ws + L.bitmap);
+    int32_t* O = (int32_t*)(ws + L.outliers);
+    int32_t* n_out = (int32_t*)(ws + L.n_outliers);
+    hipError_t e = launch_list_bitmap(K, Ofix, nO, partial, st);
+    if (e == hipSuccess) e = launch_compact(1, K, partial, bitmap, O, n_out, st);
+    if (e == hipSuccess) {
+        XPassArgs a;
+        a.dt = dtype;
+        a.X = X;
+        a.tau = 0.0f;
+        a.M = M;
+        a.K = K;
+        a.N = 0;
+        a.bitmap = bitmap;
+        a.O = O;
+        a.n_out = n_out;
+        a.Xq = ws + L.xq;
+        a.xq_pitch = (int64_t)L.xq_pitch;
+        a.s_x = (float*)(ws + L.s_x);
+        a.XO = ws + L.xo;
+        a.xo_pitch = (int64_t)L.xo_pitch;
+        a.Wq = nullptr;
+        a.WO = nullptr;
+        e = launch_code_rows(a, bitmap, O, n_out, st);
+    }
+    return hip_status(e);
+}
+
+int64_t fixed_pitch(int64_t nO) { return (nO + 31) / 32 * 32; }
 
 int matmul_common(const void* X, int64_t M, int64_t K, int dtype, const int8_t* Wq, const float* w_scale,
                   int64_t N, float threshold, void* Y, int32_t* C, float* F, void* workspace,
@@ -329,4 +366,72 @@ LLMINT8_API int int8_blockwise_dequantize(const int8_t* q, const float* absmax, 
     if (overlap(x, (size_t)n * 4, q, (size_t)n) || overlap(x, (size_t)n * 4, absmax, (size_t)nb * 4))
         return LLMINT8_EINVAL;
     return hip_status(launch_block_dequantize(q, absmax, n, block, x, (hipStream_t)stream));
+}
+
+// ---- fixed (caller-supplied) outlier dimensions
+
+LLMINT8_API size_t int8_quantize_weight_fixed_workspace_bytes(int64_t K) {
+    if (K < 0) return 0;
+    return align_up((size_t)ceil_div(K, 32) * 4 + 1);
+}
+
+LLMINT8_API int int8_quantize_weight_fixed(const void* W, int64_t K, int64_t N, int dtype, const int32_t* outlier_cols,
+                                           int64_t n_outlier_cols, int8_t* Wq, float* w_scale, void* W_O,
+                                           void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_shape(0, K, N, dtype);
+    if (rc) return rc;
+    const int64_t nO = n_outlier_cols, P = fixed_pitch(nO);
+    if (nO < 0 || nO > K) return LLMINT8_EINVAL;
+    if (N == 0) return LLMINT8_OK;
+    if (!w_scale || !aligned(w_scale, 4)) return LLMINT8_EINVAL;
+    if (K > 0 && (!W || !Wq || !aligned(W, 16) || !aligned(Wq, 16))) return LLMINT8_EINVAL;
+    if (nO > 0 && (!outlier_cols || !aligned(outlier_cols, 4) || !W_O || !aligned(W_O, 16))) return LLMINT8_EINVAL;
+    if (K > 0 && (!workspace || !aligned(workspace, 16) ||
+                  workspace_bytes < int8_quantize_weight_fixed_workspace_bytes(K)))
+        return LLMINT8_EWORKSPACE;
+    const size_t wb = (size_t)K * N * 2, qb = (size_t)K * N, sb = (size_t)N * 4, ob = (size_t)N * P * 2;
+    const size_t kb = int8_quantize_weight_fixed_workspace_bytes(K);
+    if (overlap(W, wb, Wq, qb) || overlap(W, wb, w_scale, sb) || overlap(Wq, qb, w_scale, sb) ||
+        overlap(W_O, ob, W, wb) || overlap(W_O, ob, Wq, qb) || overlap(W_O, ob, w_scale, sb) ||
+        overlap(workspace, kb, W, wb) || overlap(workspace, kb, Wq, qb) || overlap(workspace, kb, w_scale, sb) ||
+        overlap(workspace, kb, W_O, ob) || overlap(outlier_cols, (size_t)nO * 4, W_O, ob) ||
+        overlap(outlier_cols, (size_t)nO * 4, Wq, qb) || overlap(outlier_cols, (size_t)nO * 4, w_scale, sb))
+        return LLMINT8_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    uint32_t* skip = (uint32_t*)workspace;
+    hipError_t e = launch_list_bitmap(K, outlier_cols, nO, skip, st);
+    if (e == hipSuccess) e = launch_weight(dtype, W, K, N, Wq, w_scale, K > 0 ? skip : nullptr, st);
+    if (e == hipSuccess) e = launch_gather_wo(W, K, N, outlier_cols, nO, P, W_O, st);
+    return hip_status(e);
+}
+
+LLMINT8_API int int8_matmul_fixed(const void* X, int64_t M, int64_t K, int dtype, const int32_t* outlier_cols,
+                                  int64_t n_outlier_cols, const int8_t* Wq, const float* w_scale, const void* W_O,
+                                  int64_t N, void* Y, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_shape(M, K, N, dtype);
+    if (rc) return rc;
+    const int64_t nO = n_outlier_cols, P = fixed_pitch(nO);
+    if (nO < 0 || nO > K) return LLMINT8_EINVAL;
+    if (M > 0 && K > 0 && (!X || !aligned(X, 16))) return LLMINT8_EINVAL;
+    if (M > 0 && nO > 0 && (!outlier_cols || !aligned(outlier_cols, 4))) return LLMINT8_EINVAL;
+    if (M > 0 && N > 0 && nO > 0 && (!W_O || !aligned(W_O, 16))) return LLMINT8_EINVAL;
+    const Layout L = make_layout(M, K, N);
+    if (M > 0 && (!workspace || !aligned(workspace, 16) || workspace_bytes < L.total)) return LLMINT8_EWORKSPACE;
+    if (overlap(workspace, L.total, X, (size_t)M * (size_t)K * 2) ||
+        overlap(workspace, L.total, Wq, (size_t)N * (size_t)K) ||
+        overlap(workspace, L.total, outlier_cols, (size_t)nO * 4) ||
+        overlap(workspace, L.total, W_O, (size_t)N * P * 2))
+        return LLMINT8_EINVAL;
+    rc = products_common(M, K, dtype, Wq, w_scale, N, Y, nullptr, nullptr, workspace, workspace_bytes, stream, false,
+                         W_O, P);
+    if (rc) return rc;
+    if (Y && (overlap(Y, (size_t)M * (size_t)N * 2, X, (size_t)M * (size_t)K * 2) ||
+              overlap(Y, (size_t)M * (size_t)N * 2, W_O, (size_t)N * P * 2) ||
+              overlap(Y, (size_t)M * (size_t)N * 2, outlier_cols, (size_t)nO * 4)))
+        return LLMINT8_EINVAL;
+    if (M == 0) return LLMINT8_OK;
+    rc = run_xpass_fixed(X, M, K, dtype, outlier_cols, nO, (int8_t*)workspace, L, (hipStream_t)stream);
+    if (rc) return rc;
+    return products_common(M, K, dtype, Wq, w_scale, N, Y, nullptr, nullptr, workspace, workspace_bytes, stream, true,
+                           W_O, P);
 }

@@ -1,7 +1,8 @@
 // The products of the LLM.int8() matmul and its dequantizing epilogue, one kernel:
 //   C = Xq Wq^T            int8 x int8 -> int32 on v_mfma_i32_32x32x32_i8 (exact),
 //   F = X[:,O] Wq[:,O]^T   16-bit x 16-bit -> fp32 on v_mfma_f32_32x32x16_{f16,bf16},
-//   y = RN((RN(RN((float)C * r_i) * c_n)) + RN(c_n * F)),  r_i = s_x/127, c_n = s_w/127,
+//   y = RN((RN(RN((float)C * r_i) * c_n)) + RN(c_n * F)),  r_i = s_x/127, c_n = s_w/127
+//     (with a fixed outlier set whose W rows are kept in 16 bits: + F, unscaled),
 //   Y = y rounded to the 16-bit type.
 // "LLM.int8(): 8-bit Matrix Multiplication for Transformers at Scale", abstract: the
 // int8 product with one normalization constant per inner-product vector, and the
@@ -92,7 +93,8 @@ struct Params {
     const float* s_w;
     const uint16_t* XO;
     const uint16_t* WO;
-    int64_t xo_pitch;
+    int64_t xo_pitch, wo_pitch;
+    int f_scaled;
     const int32_t* n_out;
     uint16_t* Y;
     int32_t* C_acc;
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
     const int64_t wm0 = m0 + wm * 128, wn0 = n0 + wn * (32 * NJ);
     auto outlier_product = [&](const uint16_t* xo, int64_t n) {
         const int64_t bn = n < p.N ? n : p.N - 1;
-        const uint16_t* wo = p.WO + bn * p.xo_pitch + h * 8;
+        const uint16_t* wo = p.WO + bn * p.wo_pitch + h * 8;
         v16f F = v16f{};
         for (int ch = 0; ch < nsub; ++ch)
             F = mfma16<DT>(*(const u32x4*)(xo + ch * 16), *(const u32x4*)(wo + ch * 16), F);
@@ -345,7 +347,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const float yi = __fmul_rn(__fmul_rn((float)acc[i][j][e], r[e]), c);
-                    const float y = __fadd_rn(yi, __fmul_rn(c, F[e]));
+                    const float y = __fadd_rn(yi, p.f_scaled ? __fmul_rn(c, F[e]) : F[e]);
                     ys[(32 * i + 8 * (e >> 2) + 4 * h + (e & 3)) * kYPitch + 32 * j + rl] = from_f32<DT>(y);
                 }
             }
@@ -384,6 +386,8 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     p.XO = (const uint16_t*)a.XO;
     p.WO = (const uint16_t*)a.WO;
     p.xo_pitch = a.xo_pitch;
+    p.wo_pitch = a.wo_pitch;
+    p.f_scaled = a.f_scaled ? 1 : 0;
     p.n_out = a.n_out;
     p.Y = (uint16_t*)a.Y;
     p.C_acc = a.C_acc;

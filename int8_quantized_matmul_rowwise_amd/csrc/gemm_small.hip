@@ -29,6 +29,8 @@ struct SmallParams {
     const float* s_w;
     const uint16_t* XO;
     int64_t xo_pitch;
+    const uint16_t* WO;  // NULL: gather Wq[n, O[t]] (scaled outlier term); else exact rows
+    int64_t wo_pitch;
     const int32_t* O;
     const int32_t* n_out;
     uint16_t* Y;
@@ -77,7 +79,8 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(SmallParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int t = q * 8 + e;
-            const uint16_t hv = t < nO ? from_f32<DT>((float)brow[p.O[t]]) : (uint16_t)0;
+            const uint16_t hv = t >= nO ? (uint16_t)0
+                                : p.WO ? p.WO[n * p.wo_pitch + t] : from_f32<DT>((float)brow[p.O[t]]);
             wo0[e >> 1] |= (uint32_t)hv << (16 * (e & 1));
         }
     }
@@ -139,7 +142,8 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(SmallParams p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int t = t0 + q * 8 + e;
-                const uint16_t h = t < nO ? from_f32<DT>((float)brow[p.O[t]]) : (uint16_t)0;
+                const uint16_t h = t >= nO ? (uint16_t)0
+                                   : p.WO ? p.WO[n * p.wo_pitch + t] : from_f32<DT>((float)brow[p.O[t]]);
                 bv[e >> 1] |= (uint32_t)h << (16 * (e & 1));
             }
             F = mfma16x16<DT>(av, bv, F);
@@ -157,7 +161,7 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(SmallParams p) {
         } else {
             const float r = p.s_x[m] / 127.0f;
             const float yi = __fmul_rn(__fmul_rn((float)c[e], r), cn);
-            const float y = __fadd_rn(yi, __fmul_rn(cn, F[e]));
+            const float y = __fadd_rn(yi, p.WO ? F[e] : __fmul_rn(cn, F[e]));
             p.Y[m * p.N + n] = from_f32<DT>(y);
         }
     }
@@ -190,6 +194,8 @@ hipError_t launch_gemm_small(const GemmArgs& a, hipStream_t stream) {
     p.s_w = a.s_w;
     p.XO = (const uint16_t*)a.XO;
     p.xo_pitch = a.xo_pitch;
+    p.WO = a.f_scaled ? nullptr : (const uint16_t*)a.WO;
+    p.wo_pitch = a.wo_pitch;
     p.O = a.O;
     p.n_out = a.n_out;
     p.Y = (uint16_t*)a.Y;

@@ -12,7 +12,14 @@ namespace llmint8 {
 // quantize-transpose into Wq (N x K).
 int64_t weight_splits(int64_t K);
 hipError_t launch_weight(int dt, const void* W, int64_t K, int64_t N, int8_t* Wq, float* w_scale,
-                         float* partial /* weight_splits(K) x N */, hipStream_t stream);
+                         const uint32_t* skip /* nullable: rows of W (outlier set) to leave out */,
+                         hipStream_t stream);
+// W_O (N x P, 16-bit): W[O[t], n] for t < nO, zero up to P.
+hipError_t launch_gather_wo(const void* W, int64_t K, int64_t N, const int32_t* O, int64_t nO, int64_t P, void* WO,
+                            hipStream_t stream);
+// The bitmap of a caller's column list (single workgroup), as one row-block partial for
+// launch_compact: the fixed-outlier paths then share the compaction and the row coding.
+hipError_t launch_list_bitmap(int64_t K, const int32_t* O, int64_t nO, uint32_t* partial, hipStream_t stream);
 
 // ---- X pass
 int64_t detect_row_blocks(int64_t M);
@@ -56,10 +63,14 @@ struct GemmArgs {
     const float* s_x;
     const float* s_w;
     const void* XO;
-    const void* WO;
+    const void* WO;     // 16-bit outlier rows of W, N x wo_pitch (the small-batch kernel
+                        // gathers them from Wq itself when f_scaled)
     int64_t xo_pitch;
+    int64_t wo_pitch;
+    bool f_scaled;      // W_O holds Wq's codes (the outlier term is scaled by c_n) or exact
+                        // 16-bit W rows (fixed outlier set: unscaled)
     const int32_t* n_out;
-    const int32_t* O;  // outlier columns (the small-batch kernel gathers Wq[:,O] itself)
+    const int32_t* O;   // outlier columns
     void* Y;          // product path
     int32_t* C_acc;   // accumulator dump (test hook); Y == NULL then
     float* F_acc;

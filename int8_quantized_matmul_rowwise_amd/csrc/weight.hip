@@ -5,7 +5,9 @@
 // 16-bit checkpoint is loaded, converted to Int8 and used immediately (one data-free
 // pass; round to nearest -- "nuQmm" report page, GPTQ statements under
 // "Large-model Quantization" and "The Gptq Algorithm").  One normalization constant
-// per output column of W: its absmax.
+// per output column of W: its absmax.  With a fixed outlier set (skip: a bitmap over the
+// rows of W), those rows are left out of the scale, coded 0, and copied exactly into the
+// 16-bit W_O (N x P) by gather_wo_kernel.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -19,9 +21,14 @@ __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
 // s_w[n] = max_k |W[k,n]|: each block reduces a 512-column x (K/splits)-row slab and
 // merges with atomicMax on the fp32 bit pattern (|w| >= 0, so the unsigned order of
 // the bits is the numeric order: exact and independent of the merge order).
+__device__ __forceinline__ bool skipped(const uint32_t* skip, int64_t k) {
+    return skip && ((skip[k >> 5] >> (k & 31)) & 1u);
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void colmax_kernel(const uint16_t* __restrict__ W, int64_t K, int64_t N,
-                                                     int64_t rows_per_split, float* __restrict__ s_w) {
+                                                     int64_t rows_per_split, const uint32_t* __restrict__ skip,
+                                                     float* __restrict__ s_w) {
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int64_t n8 = ((int64_t)blockIdx.x * 64 + lane) * 8;
     const int64_t k0 = (int64_t)blockIdx.y * rows_per_split;
@@ -29,6 +36,7 @@ __global__ __launch_bounds__(256) void colmax_kernel(const uint16_t* __restrict_
     float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (n8 < N) {
         for (int64_t k = k0 + w; k < k1; k += 4) {
+            if (skipped(skip, k)) continue;  // the same row for the whole wave
             const u32x4 v = *(const u32x4*)(W + k * N + n8);
 #pragma unroll
             for (int j = 0; j < 8; ++j)
@@ -53,6 +61,7 @@ __global__ __launch_bounds__(256) void colmax_kernel(const uint16_t* __restrict_
 template <int DT>
 __global__ __launch_bounds__(256) void quantize_weight_kernel(const uint16_t* __restrict__ W, int64_t K, int64_t N,
                                                               const float* __restrict__ s_w,
+                                                              const uint32_t* __restrict__ skip,
                                                               int8_t* __restrict__ Wq) {
     __shared__ float inv[64];
     __shared__ __attribute__((aligned(16))) uint8_t tile[64][128 + 16];
@@ -67,10 +76,11 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(const uint16_t* __
         const int64_t k = k0 + kk, n = n0 + cc * 8;
         if (k < K && n < N) {
             const u32x4 v = *(const u32x4*)(W + k * N + n);
+            const bool out = skipped(skip, k);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float f = to_f32<DT>((uint16_t)(v[j >> 1] >> (16 * (j & 1))));
-                tile[cc * 8 + j][kk] = (uint8_t)quantize(f, inv[cc * 8 + j]);
+                tile[cc * 8 + j][kk] = out ? (uint8_t)0 : (uint8_t)quantize(f, inv[cc * 8 + j]);
             }
         }
     }
@@ -84,13 +94,33 @@ __global__ __launch_bounds__(256) void quantize_weight_kernel(const uint16_t* __
     }
 }
 
+// W_O[n, t] = W[O[t], n] (exact), zero for t >= n_O up to the pitch P; entries of O
+// outside [0, K) give zero (never an access outside W).
+__global__ __launch_bounds__(256) void gather_wo_kernel(const uint16_t* __restrict__ W, int64_t K, int64_t N,
+                                                        const int32_t* __restrict__ O, int64_t nO, int64_t P,
+                                                        uint16_t* __restrict__ WO) {
+    const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t t = blockIdx.y;
+    if (n >= N) return;
+    const int64_t k = t < nO ? (int64_t)O[t] : -1;
+    WO[n * P + t] = (k >= 0 && k < K) ? W[k * N + n] : (uint16_t)0;
+}
+
+hipError_t launch_gather_wo(const void* W, int64_t K, int64_t N, const int32_t* O, int64_t nO, int64_t P, void* WO,
+                            hipStream_t stream) {
+    if (N == 0 || P == 0) return hipSuccess;
+    dim3 g((unsigned)ceil_div(N, 256), (unsigned)P);
+    gather_wo_kernel<<<g, 256, 0, stream>>>((const uint16_t*)W, K, N, O, nO, P, (uint16_t*)WO);
+    return hipGetLastError();
+}
+
 int64_t weight_splits(int64_t K) {
     int64_t s = ceil_div(K, 256);
     return s < 1 ? 1 : (s > 64 ? 64 : s);
 }
 
-hipError_t launch_weight(int dt, const void* W, int64_t K, int64_t N, int8_t* Wq, float* w_scale, float*,
-                         hipStream_t stream) {
+hipError_t launch_weight(int dt, const void* W, int64_t K, int64_t N, int8_t* Wq, float* w_scale,
+                         const uint32_t* skip, hipStream_t stream) {
     if (N == 0) return hipSuccess;
     fill_zero_kernel<<<(unsigned)ceil_div(N, 256), 256, 0, stream>>>(w_scale, N);
     hipError_t e = hipGetLastError();
@@ -100,11 +130,11 @@ hipError_t launch_weight(int dt, const void* W, int64_t K, int64_t N, int8_t* Wq
     dim3 g1((unsigned)ceil_div(N, 512), (unsigned)ceil_div(K, rps));
     dim3 g2((unsigned)ceil_div(N, 64), (unsigned)ceil_div(K, 128));
     if (dt == F16) {
-        colmax_kernel<F16><<<g1, 256, 0, stream>>>((const uint16_t*)W, K, N, rps, w_scale);
-        quantize_weight_kernel<F16><<<g2, 256, 0, stream>>>((const uint16_t*)W, K, N, w_scale, Wq);
+        colmax_kernel<F16><<<g1, 256, 0, stream>>>((const uint16_t*)W, K, N, rps, skip, w_scale);
+        quantize_weight_kernel<F16><<<g2, 256, 0, stream>>>((const uint16_t*)W, K, N, w_scale, skip, Wq);
     } else {
-        colmax_kernel<BF16><<<g1, 256, 0, stream>>>((const uint16_t*)W, K, N, rps, w_scale);
-        quantize_weight_kernel<BF16><<<g2, 256, 0, stream>>>((const uint16_t*)W, K, N, w_scale, Wq);
+        colmax_kernel<BF16><<<g1, 256, 0, stream>>>((const uint16_t*)W, K, N, rps, skip, w_scale);
+        quantize_weight_kernel<BF16><<<g2, 256, 0, stream>>>((const uint16_t*)W, K, N, w_scale, skip, Wq);
     }
     return hipGetLastError();
 }

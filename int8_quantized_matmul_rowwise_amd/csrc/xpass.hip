@@ -130,6 +130,29 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint32_t* __restric
 
 // ---------------------------------------------------------------------------
 
+// Bitmap of a caller's list of outlier columns (fixed-outlier path), one workgroup:
+// bits in LDS (atomicOr), then the words out.  Entries outside [0, K) are ignored.
+__global__ __launch_bounds__(1024) void list_bitmap_kernel(int64_t K, const int32_t* __restrict__ O, int64_t nO,
+                                                           uint32_t* __restrict__ partial) {
+    __shared__ uint32_t bits[kMaxKw];
+    const int tid = threadIdx.x;
+    const int64_t Kw = ceil_div(K, 32);
+    for (int64_t w = tid; w < Kw; w += 1024) bits[w] = 0;
+    __syncthreads();
+    for (int64_t t = tid; t < nO; t += 1024) {
+        const int64_t k = O[t];
+        if (k >= 0 && k < K) atomicOr(&bits[k >> 5], 1u << (k & 31));
+    }
+    __syncthreads();
+    for (int64_t w = tid; w < Kw; w += 1024) partial[w] = bits[w];
+}
+
+hipError_t launch_list_bitmap(int64_t K, const int32_t* O, int64_t nO, uint32_t* partial, hipStream_t stream) {
+    if (K == 0) return hipSuccess;
+    list_bitmap_kernel<<<1, 1024, 0, stream>>>(K, O, nO, partial);
+    return hipGetLastError();
+}
+
 int64_t detect_row_blocks(int64_t M) {
     if (M <= 0) return 0;
     int64_t nrb = ceil_div(M, 64);

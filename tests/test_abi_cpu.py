@@ -126,3 +126,29 @@ def test_blockwise_codec_rejects():
     assert dq(Q, S, 4096, 2048, X + 4, None) == L.EINVAL        # x not 16-byte aligned
     assert qz(None, 0, 2048, None, None, None) == L.OK           # empty: nothing to do
     assert dq(None, None, 0, 64, None, None) == L.OK
+
+
+def test_fixed_outlier_entry_points_reject():
+    wf, mf = L.lib().int8_quantize_weight_fixed, L.lib().int8_matmul_fixed
+    kb = L.lib().int8_quantize_weight_fixed_workspace_bytes
+    assert kb(64) >= 8 and kb(-1) == 0
+    W, Wq, S, O, WO, WS = A16, A16 * 64, A16 * 128, A16 * 192, A16 * 256, A16 * 320
+    assert wf(W, 64, 8, 0, O, -1, Wq, S, WO, WS, 1 << 16, None) == L.EINVAL      # n_O < 0
+    assert wf(W, 64, 8, 0, O, 65, Wq, S, WO, WS, 1 << 16, None) == L.EINVAL      # n_O > K
+    assert wf(W, 64, 8, 0, None, 3, Wq, S, WO, WS, 1 << 16, None) == L.EINVAL    # no list
+    assert wf(W, 64, 8, 0, O, 3, Wq, S, None, WS, 1 << 16, None) == L.EINVAL     # no W_O
+    assert wf(W, 64, 8, 0, O + 2, 3, Wq, S, WO, WS, 1 << 16, None) == L.EINVAL   # list misaligned
+    assert wf(W, 64, 8, 0, O, 3, Wq, S, WO, WS, 4, None) == L.EWORKSPACE          # workspace too small
+    assert wf(W, 64, 8, 0, O, 3, Wq, S, WO, WO + 16, 1 << 16, None) == L.EINVAL  # workspace overlaps W_O
+    assert wf(W, 60, 8, 0, O, 3, Wq, S, WO, WS, 1 << 16, None) == L.EINVAL       # K % 16
+    assert wf(None, 64, 0, 0, None, 0, None, None, None, None, 0, None) == L.OK  # N = 0
+    X, Y = A16, A16 * 512
+    big = 1 << 30
+    assert mf(X, 4, 64, 0, O, -1, Wq, S, WO, 8, Y, WS, big, None) == L.EINVAL
+    assert mf(X, 4, 64, 0, O, 65, Wq, S, WO, 8, Y, WS, big, None) == L.EINVAL
+    assert mf(X, 4, 64, 0, None, 2, Wq, S, WO, 8, Y, WS, big, None) == L.EINVAL
+    assert mf(X, 4, 64, 0, O, 2, Wq, S, None, 8, Y, WS, big, None) == L.EINVAL
+    assert mf(X, 4, 64, 0, O, 2, Wq, S, WO, 8, Y, WS, 16, None) == L.EWORKSPACE
+    assert mf(X, 4, 64, 0, O, 2, Wq, S, WO, 8, WO + 64, WS, big, None) == L.EINVAL  # Y overlaps W_O
+    assert mf(X, 4, 64, 2, O, 2, Wq, S, WO, 8, Y, WS, big, None) == L.EINVAL        # dtype
+    assert mf(None, 0, 64, 0, None, 0, Wq, S, None, 8, None, None, 0, None) == L.OK  # M = 0
