@@ -353,6 +353,8 @@ def main() -> int:
                     help="before the steps, run a plain copy-shaped kernel over this many MiB (counter calibration)")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarize two rocprofv3 counter runs into the stored traffic record and exit")
+    ap.add_argument("--fixed", action="store_true",
+                    help="time the fixed-outlier path (the workload's injected columns as the set) instead")
     ap.add_argument("--codec", action="store_true",
                     help="benchmark the block-wise int8 codec instead (its own JSON line)")
     ap.add_argument("--trace-summary", nargs=3, metavar=("TRACE_DIR", "BENCH_OUT", "COMMAND"),
@@ -402,8 +404,17 @@ def main() -> int:
         del src, dst
         torch.cuda.empty_cache()
 
-    def step():
-        lm.int8_matmul(X, Wq, s_w, wl.tau, Y=Y, workspace=ws)
+    if args.fixed:
+        # the workload's injected outlier columns, fixed offline: no detection per call
+        Ofix = torch.as_tensor(sorted(int(c) for c in cols), dtype=torch.int32, device=dev)
+        Wq, s_w, W_O = lm.int8_quantize_weight_fixed(W, Ofix)
+        torch.cuda.synchronize()
+
+        def step():
+            lm.int8_matmul_fixed(X, Ofix, Wq, s_w, W_O, Y=Y, workspace=ws)
+    else:
+        def step():
+            lm.int8_matmul(X, Wq, s_w, wl.tau, Y=Y, workspace=ws)
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -413,7 +424,7 @@ def main() -> int:
     t_wall = time.perf_counter()
     ms_step = time_loop(step, args.steps, torch)
     t_wall = time.perf_counter() - t_wall
-    n_out, _ = lm.int8_matmul_stats(X, wl.tau)
+    n_out = len(cols) if args.fixed else lm.int8_matmul_stats(X, wl.tau)[0]
     ops = 2.0 * wl.M * wl.N * wl.K
     tops = ops / (ms_step * 1e-3) / 1e12
 
@@ -426,6 +437,8 @@ def main() -> int:
     ms_gemm = time_loop(lambda: lm.int8_matmul_products(wl.M, wl.K, X.dtype, Wq, s_w, ws, Y=Y, stream=stream),
                         args.steps, torch)
     ms_xpass = time_loop(lambda: lm.int8_matmul_prepare(X, Wq, wl.tau, workspace=ws, stream=stream), args.steps, torch)
+    if args.fixed:
+        ms_xpass = ms_step - ms_gemm  # the fixed X pass (list bitmap, compaction, row coding) is the rest of a step
     cold = None
     if args.cold:
         # every step after a 512 MiB write that evicts L2 and the memory-side cache
@@ -484,7 +497,8 @@ def main() -> int:
         "dtype": "i8",
         "data": "synthetic",
         "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "x_dtype": wl.dtype,
-                   "threshold": wl.tau, "n_outliers": n_out, "seed": 0},
+                   "threshold": None if args.fixed else wl.tau, "n_outliers": n_out, "seed": 0,
+                   **({"outliers": "fixed (caller-supplied)"} if args.fixed else {})},
         "pct_of_i8_peak": tops / I8_PEAK_TOPS * 100.0,
         "roofline": roof,
         "cpu_baseline": None,
