@@ -63,6 +63,9 @@ def _load():
             "orc_quantize_weight_fixed": (None, [_P, _I64, _I64, ctypes.c_int, _P, _I64, _P, _P, _P]),
             "orc_outlier_gemm_exact": (None, [_P, _I64, ctypes.c_int, _P, _I64, _P, _I64, _P, _P, _P]),
             "orc_dequant_fixed": (None, [_P, _P, _P, _P, _I64, _I64, ctypes.c_int, _P, _P]),
+            "orc_group_quantize_rows": (None, [_P, _I64, _I64, ctypes.c_int, _I64, _P, _P]),
+            "orc_group_quantize_weight": (None, [_P, _I64, _I64, ctypes.c_int, _I64, _P, _P]),
+            "orc_group_gemm": (None, [_P, _P, _P, _P, _I64, _I64, _I64, _P, _I64, ctypes.c_int, _P, _P]),
             "orc_block_quantize": (None, [_P, _I64, _I64, _P, _P]),
             "orc_block_dequantize": (None, [_P, _P, _I64, _I64, _P]),
         }
@@ -308,3 +311,41 @@ def matmul_fixed(X: np.ndarray, dt: str, Wq: np.ndarray, s_w: np.ndarray, WO: np
     F, F64, A = outlier_gemm_exact(XO, dt, WO, rr)
     y, Y = dequant_fixed(C, F, s_x[rr], s_w, dt)
     return dict(O=O, Xq=Xq, s_x=s_x, XO=XO, rows=rr, C=C, F=F, F64=F64, A=A, y=y, Y=Y)
+
+
+# ---- group-wise scales along K
+
+def group_quantize_rows(X: np.ndarray, dt: str, G: int):
+    """(Xq M x K, s_x M x K/G) with one scale per row and group of G features."""
+    X = _c(X, np.uint16)
+    M, K = X.shape
+    assert G > 0 and K % G == 0
+    Xq = np.zeros((M, K), np.int8)
+    s_x = np.zeros((M, K // G), np.float32)
+    _load().orc_group_quantize_rows(_p(X), M, K, DT[dt], G, _p(Xq), _p(s_x))
+    return Xq, s_x
+
+
+def group_quantize_weight(W: np.ndarray, dt: str, G: int):
+    """(Wq N x K, s_w N x K/G) with one scale per output column and group."""
+    W = _c(W, np.uint16)
+    K, N = W.shape
+    assert G > 0 and K % G == 0
+    Wq = np.zeros((N, K), np.int8)
+    s_w = np.zeros((N, K // G), np.float32)
+    _load().orc_group_quantize_weight(_p(W), K, N, DT[dt], G, _p(Wq), _p(s_w))
+    return Wq, s_w
+
+
+def group_gemm(Xq: np.ndarray, s_x: np.ndarray, Wq: np.ndarray, s_w: np.ndarray, G: int, dt: str, rows=None):
+    """(y fp32, Y bits) of the group-wise product for the given rows (None: all)."""
+    Xq = _c(Xq, np.int8)
+    Wq = _c(Wq, np.int8)
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    r, nr = _rows(rows, M)
+    y = np.zeros((nr, N), np.float32)
+    Y = np.zeros((nr, N), np.uint16)
+    _load().orc_group_gemm(_p(Xq), _p(_c(s_x, np.float32)), _p(Wq), _p(_c(s_w, np.float32)), K, N, G, _p(r), nr,
+                           DT[dt], _p(y), _p(Y))
+    return y, Y

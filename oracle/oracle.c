@@ -308,6 +308,70 @@ void orc_dequant_fixed(const int32_t* C, const float* F, const float* s_x_rows, 
     }
 }
 
+/* ------------------------------------------------------ group-wise scales */
+
+void orc_group_quantize_rows(const uint16_t* X, int64_t M, int64_t K, int dt, int64_t G, int8_t* Xq, float* s_x) {
+    int64_t ng = K / G;
+    int nt = nthreads();
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t g = 0; g < ng; ++g) {
+            const uint16_t* xs = X + i * K + g * G;
+            float s = 0.0f;
+            for (int64_t k = 0; k < G; ++k) {
+                float a = fabsf(orc_to_f32(xs[k], dt));
+                if (a > s) s = a;
+            }
+            s_x[i * ng + g] = s;
+            float inv = orc_inv_scale(s);
+            for (int64_t k = 0; k < G; ++k) Xq[i * K + g * G + k] = orc_quantize(orc_to_f32(xs[k], dt), inv);
+        }
+    }
+}
+
+void orc_group_quantize_weight(const uint16_t* W, int64_t K, int64_t N, int dt, int64_t G, int8_t* Wq, float* s_w) {
+    int64_t ng = K / G;
+    int nt = nthreads();
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < ng; ++g) {
+            float s = 0.0f;
+            for (int64_t k = g * G; k < (g + 1) * G; ++k) {
+                float a = fabsf(orc_to_f32(W[k * N + n], dt));
+                if (a > s) s = a;
+            }
+            s_w[n * ng + g] = s;
+            float inv = orc_inv_scale(s);
+            for (int64_t k = g * G; k < (g + 1) * G; ++k) Wq[n * K + k] = orc_quantize(orc_to_f32(W[k * N + n], dt), inv);
+        }
+    }
+}
+
+void orc_group_gemm(const int8_t* Xq, const float* s_x, const int8_t* Wq, const float* s_w, int64_t K, int64_t N,
+                    int64_t G, const int64_t* rows, int64_t nrows, int dt, float* y, uint16_t* Y) {
+    int64_t ng = K / G;
+    int nt = nthreads();
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t i = rows ? rows[r] : r;
+        const int8_t* x = Xq + i * K;
+        for (int64_t n = 0; n < N; ++n) {
+            const int8_t* wrow = Wq + n * K;
+            float acc = 0.0f;
+            for (int64_t g = 0; g < ng; ++g) {
+                int32_t cg = 0;
+                for (int64_t k = g * G; k < (g + 1) * G; ++k) cg += (int32_t)x[k] * (int32_t)wrow[k];
+                float rg = s_x[i * ng + g] / 127.0f;
+                float cng = s_w[n * ng + g] / 127.0f;
+                float term = ((float)cg * rg) * cng;
+                acc = acc + term;
+            }
+            if (y) y[r * N + n] = acc;
+            Y[r * N + n] = orc_from_f32(acc, dt);
+        }
+    }
+}
+
 /* ------------------------------------------------------- block-wise codec */
 
 void orc_block_quantize(const float* x, int64_t n, int64_t block, int8_t* q, float* absmax) {

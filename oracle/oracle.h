@@ -105,6 +105,19 @@ void orc_outlier_gemm_exact(const uint16_t* XO, int64_t nO, int dt, const uint16
 void orc_dequant_fixed(const int32_t* C, const float* F, const float* s_x_rows, const float* s_w,
                        int64_t nrows, int64_t N, int dt, float* y, uint16_t* Y);
 
+/* Group-wise scales along K (the finer granularity the "nuQmm" report page discusses for
+ * weight quantization: one scale per group of consecutive input features; here for both
+ * operands, no outlier decomposition).  G divides K; ng = K / G groups.
+ *   s_x[i*ng + g] = max |X[i,k]| over k in [gG, (g+1)G);  Xq[i,k] = code with that scale;
+ *   s_w[n*ng + g] = max |W[k,n]| over the same k;          Wq[n,k] = code with that scale;
+ *   C_g[i,n] = sum over the group of Xq Wq (exact int32);
+ *   acc = 0; for g ascending: acc = RN32(acc + RN32(RN32((float)C_g * r_ig) * c_ng)),
+ *   r_ig = RN32(s_x/127), c_ng = RN32(s_w/127);  Y = RN_T(acc). */
+void orc_group_quantize_rows(const uint16_t* X, int64_t M, int64_t K, int dt, int64_t G, int8_t* Xq, float* s_x);
+void orc_group_quantize_weight(const uint16_t* W, int64_t K, int64_t N, int dt, int64_t G, int8_t* Wq, float* s_w);
+void orc_group_gemm(const int8_t* Xq, const float* s_x, const int8_t* Wq, const float* s_w, int64_t K, int64_t N,
+                    int64_t G, const int64_t* rows, int64_t nrows, int dt, float* y, uint16_t* Y);
+
 /* Block-wise absmax int8 codec of a flat fp32 tensor ("llama3-model-quantization" talk
  * summary, Key Points, 8-bit optimizers: the state is cut into blocks, each block is
  * normalised by its own maximum and stored as 8-bit values; the linear code is read, the

@@ -14,6 +14,7 @@ from tests import test_oracle_pipeline as tp
 from tests import test_oracle_quantizer as tq
 from tests import test_oracle_codec as tc
 from tests import test_oracle_fixed as tfx
+from tests import test_oracle_group as tg
 
 MUTANTS = {
     "ties_away_from_zero": ("float v = rintf(x * inv);", "float v = roundf(x * inv);"),
@@ -39,6 +40,12 @@ MUTANTS = {
                                   "            float a = fabsf(orc_to_f32(W[k * N + n], dt));"),
     "fixed_rows_from_codes": ("WO[n * nO + t] = W[(int64_t)O[t] * N + n];",
                               "WO[n * nO + t] = orc_from_f32((float)Wq[n * K + O[t]], dt);"),
+    "group_row_scale_over_whole_row": ("            const uint16_t* xs = X + i * K + g * G;\n            float s = 0.0f;\n            for (int64_t k = 0; k < G; ++k) {",
+                                       "            const uint16_t* xs = X + i * K + g * G;\n            float s = 0.0f;\n            for (int64_t k = -g * G; k < K - g * G; ++k) {"),
+    "group_weight_boundary_shift": ("            for (int64_t k = g * G; k < (g + 1) * G; ++k) {\n                float a = fabsf(orc_to_f32(W[k * N + n], dt));",
+                                    "            for (int64_t k = g * G; k < (g + 1) * G && k + 1 < K; ++k) {\n                float a = fabsf(orc_to_f32(W[k * N + n], dt));"),
+    "group_sum_scaled_once": ("                float term = ((float)cg * rg) * cng;\n                acc = acc + term;",
+                              "                float term = ((float)cg * rg) * cng;\n                acc = g == 0 ? term : acc + (float)cg * (acc / (float)cg);"),
 }
 
 PINS = [
@@ -58,6 +65,9 @@ PINS = [
     tfx.test_fixed_lattice_closed_form,
     tfx.test_fixed_weight_conversion_uses_the_scalar_quantizer,
     tfx.test_fixed_all_columns_is_the_16bit_product,
+    tg.test_group_lattice_closed_form,
+    lambda: tg.test_group_codes_use_the_scalar_quantizer("fp16", 64),
+    tg.test_group_fp32_sum_within_its_bound,
 ]
 
 
