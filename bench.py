@@ -49,6 +49,7 @@ CSRC = "int8_quantized_matmul_rowwise_amd/csrc/"
 KERNELS = {
     "gemm_kernel": [CSRC + "gemm.hip", CSRC + "common.hpp"],
     "gemm_small_kernel": [CSRC + "gemm_small.hip", CSRC + "common.hpp"],
+    "gemm_group_kernel": [CSRC + "gemm_group.hip", CSRC + "common.hpp"],
 }
 SMALL_M, SMALL_K = 64, 32768  # the library's small-batch switch (M <= 64 and K <= 32768)
 
@@ -57,8 +58,21 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def product_kernel(M: int, K: int) -> str:
+def product_kernel(M: int, K: int, group: int = 0) -> str:
+    if group:
+        return "gemm_group_kernel"
     return "gemm_small_kernel" if (M <= SMALL_M and K <= SMALL_K) else "gemm_kernel"
+
+
+def workload_tag(wl, group: int = 0) -> str:
+    """The name of a timed configuration: the workload, with the group size for the group-wise path."""
+    return f"{wl.name}_g{group}" if group else wl.name
+
+
+def algorithmic_bytes(wl, group: int = 0) -> int:
+    """Bytes the product kernel must move per launch: Xq, Wq, their scales (or factors), Y."""
+    ng = wl.K // group if group else 1
+    return wl.M * wl.K + wl.N * wl.K + 4 * ng * (wl.N + wl.M) + 2 * wl.M * wl.N
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -181,14 +195,16 @@ def _per_dispatch(rows, counter: str, match) -> list:
     return list(vals.values())
 
 
-def traffic_summary(fetch_dir: str, write_dir: str, wl, copy_mib: int) -> int:
-    kernel = product_kernel(wl.M, wl.K)
+def traffic_summary(fetch_dir: str, write_dir: str, wl, copy_mib: int, group: int = 0) -> int:
+    kernel = product_kernel(wl.M, wl.K, group)
+    tag = workload_tag(wl, group)
+    gflag = f" --group {group}" if group else ""
     copy_bytes = copy_mib * 1024 * 1024
     is_copy = lambda name: "elementwise_kernel" in name  # the calibration copy (torch add of 1 GiB)
     is_prod = lambda name: f"::{kernel}<" in name
-    out = {"kernel": kernel, "workload": wl.name, "kernel_source_sha256": kernel_source_hash(kernel),
+    out = {"kernel": kernel, "workload": tag, "kernel_source_sha256": kernel_source_hash(kernel),
            "copy_calibration_bytes": copy_bytes}
-    lines = [f"# {kernel} HBM traffic, workload {wl.name} ({wl.M}x{wl.K}x{wl.N} {wl.dtype})", ""]
+    lines = [f"# {kernel} HBM traffic, workload {tag} ({wl.M}x{wl.K}x{wl.N} {wl.dtype})", ""]
     total = 0.0
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _counter_rows(d)
@@ -212,29 +228,29 @@ def traffic_summary(fetch_dir: str, write_dir: str, wl, copy_mib: int) -> int:
                   f"(factor {factor:.4f}); {kernel}: {prod_kib:.0f} KiB per launch over {len(prods)} launches "
                   f"-> {bytes_ / 1e9:.4f} GB"]
     out["hbm_bytes_per_launch"] = total
-    alg = wl.M * wl.K + wl.N * wl.K + 4 * wl.N + 4 * wl.M + 2 * wl.M * wl.N
+    alg = algorithmic_bytes(wl, group)
     out["algorithmic_bytes_per_launch"] = alg
     lines += [f"- HBM bytes per launch: {total / 1e9:.4f} GB; algorithmic (Xq + Wq + scales + Y): {alg / 1e9:.4f} GB "
               f"({total / alg:.2f}x)", "",
               "Commands (from the repository root on the GPU box, then on any host):", "",
               "    cd /tmp && export TMPDIR=/tmp; cd -",
               f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- python3 bench.py "
-              f"--workload {wl.name} --steps 3 --warmup 1 --no-cpu-baseline --no-fp16-gemm --copy-mib {copy_mib}",
+              f"--workload {wl.name}{gflag} --steps 3 --warmup 1 --no-cpu-baseline --no-fp16-gemm --copy-mib {copy_mib}",
               f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- python3 bench.py "
-              f"--workload {wl.name} --steps 3 --warmup 1 --no-cpu-baseline --no-fp16-gemm --copy-mib {copy_mib}",
-              f"    python3 bench.py --traffic-summary {fetch_dir} {write_dir} --workload {wl.name} "
+              f"--workload {wl.name}{gflag} --steps 3 --warmup 1 --no-cpu-baseline --no-fp16-gemm --copy-mib {copy_mib}",
+              f"    python3 bench.py --traffic-summary {fetch_dir} {write_dir} --workload {wl.name}{gflag} "
               f"--copy-mib {copy_mib}", ""]
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(traffic_path(kernel, wl.name, "json"), "w") as f:
+    with open(traffic_path(kernel, tag, "json"), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
-    with open(traffic_path(kernel, wl.name, "md"), "w") as f:
+    with open(traffic_path(kernel, tag, "md"), "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
     return 0
 
 
-def trace_summary(trace_dir: str, bench_json: str, wl, cmd: str) -> int:
+def trace_summary(trace_dir: str, bench_json: str, wl, cmd: str, group: int = 0) -> int:
     """Kernel-trace statistics of a profiled bench run (rocprofv3 --kernel-trace --stats),
     beside the bench line of that same run."""
     files = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True))
@@ -242,8 +258,9 @@ def trace_summary(trace_dir: str, bench_json: str, wl, cmd: str) -> int:
         raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
     with open(files[0], newline="") as fh:
         rows = list(csv.DictReader(fh))
-    kernel = product_kernel(wl.M, wl.K)
-    lines = [f"# Kernel trace, workload {wl.name} ({wl.M}x{wl.K}x{wl.N} {wl.dtype})", "",
+    kernel = product_kernel(wl.M, wl.K, group)
+    tag = workload_tag(wl, group)
+    lines = [f"# Kernel trace, workload {tag} ({wl.M}x{wl.K}x{wl.N} {wl.dtype})", "",
              "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
     avg_prod = None
     for r in rows:
@@ -265,7 +282,7 @@ def trace_summary(trace_dir: str, bench_json: str, wl, cmd: str) -> int:
             lines.append(f"trace average of {kernel}: {avg_prod:.1f} us ({(avg_prod / (ms * 1e3) - 1) * 100:+.1f} % "
                          f"vs the events)")
     lines += ["", "Command (repository root on the GPU box):", "", "    " + cmd, ""]
-    out = os.path.join(ROOT, "profiles", f"kernel_trace_{wl.name}.md")
+    out = os.path.join(ROOT, "profiles", f"kernel_trace_{tag}.md")
     with open(out, "w") as f:
         f.write("\n".join(lines))
     print("\n".join(lines))
@@ -337,6 +354,115 @@ def codec_bench(args) -> int:
     return 0
 
 
+def calibration_copy(copy_mib: int, dev, torch) -> None:
+    """Counter calibration: an elementwise kernel that reads and writes copy_mib MiB once."""
+    n = copy_mib * 1024 * 1024 // 4
+    src = torch.empty(n, dtype=torch.int32, device=dev)  # no fill kernel: the add is the only elementwise one
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.add(src, 1, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
+def group_bench(args, wl) -> int:
+    """The group-wise path (groups of G features along K on both operands, no outlier
+    decomposition) on the workload's shape: a step is one int8_matmul_group call (X pass +
+    products); the dominant kernel is the grouped product kernel (bound "mfma")."""
+    import numpy as np
+    import torch
+
+    import int8_quantized_matmul_rowwise_amd as lm
+    import oracle
+    import workloads
+
+    G = args.group
+    if wl.K % G:
+        raise SystemExit(f"--group {G} does not divide K = {wl.K}")
+    lm.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kernel = product_kernel(wl.M, wl.K, G)
+    tag = workload_tag(wl, G)
+    log(f"workload {tag}: X {wl.M}x{wl.K} {wl.dtype}, W {wl.K}x{wl.N}, groups of {G}; product kernel {kernel}")
+    x, w, _, _ = workloads.make_workload(wl.name)
+    X, W = x.to(dev), w.to(dev)
+    Wq, s_w = lm.int8_quantize_weight_group(W, G)
+    del W
+    ws = torch.empty(lm.int8_matmul_group_workspace_bytes(wl.M, wl.K, G), dtype=torch.uint8, device=dev)
+    Y = torch.empty((wl.M, wl.N), dtype=X.dtype, device=dev)
+    torch.cuda.synchronize()
+    if args.copy_mib > 0:
+        calibration_copy(args.copy_mib, dev, torch)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        lm.int8_matmul_group(X, Wq, s_w, G, Y=Y, workspace=ws, stream=stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    t_wall = time.perf_counter()
+    ms_step = time_loop(step, args.steps, torch)
+    t_wall = time.perf_counter() - t_wall
+    ops = 2.0 * wl.M * wl.N * wl.K
+    tops = ops / (ms_step * 1e-3) / 1e12
+    ms_gemm = time_loop(lambda: lm.int8_matmul_group_products(wl.M, wl.K, X.dtype, G, Wq, s_w, ws, Y=Y,
+                                                              stream=stream), args.steps, torch)
+    ms_xpass = time_loop(lambda: lm.int8_matmul_group_prepare(X, G, ws, stream=stream), args.steps, torch)
+    achieved = ops / (ms_gemm * 1e-3) / 1e12
+    log(f"step {ms_step * 1e3:.1f} us = {tops:.0f} TOPS; {kernel} {ms_gemm * 1e3:.1f} us = {achieved:.0f} TOPS; "
+        f"X pass {ms_xpass * 1e3:.1f} us")
+    roof = {"bound": "mfma", "achieved": achieved, "peak": I8_PEAK_TOPS, "unit": "TFLOP/s",
+            "frac": achieved / I8_PEAK_TOPS, "traffic": stored_traffic(kernel, tag), "kernel": kernel,
+            "kernel_ms": ms_gemm, "xpass_ms": ms_xpass}
+    line = {
+        "metric": "effective TOPS of int8 matmul with group-wise scales along K; % i8 MFMA peak",
+        "value": tops,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": tag, "M": wl.M, "K": wl.K, "N": wl.N, "x_dtype": wl.dtype, "group": G, "seed": 0},
+        "pct_of_i8_peak": tops / I8_PEAK_TOPS * 100.0,
+        "roofline": roof,
+        "cpu_baseline": None,
+        "wall_s_timed": t_wall,
+    }
+    if not args.no_cpu_baseline:
+        cores = oracle.set_threads(min(int(os.environ.get("OMP_NUM_THREADS") or os.cpu_count()), os.cpu_count()))
+        Xb, Wb = workloads.bits(x), workloads.bits(w)
+        log(f"cpu baseline: oracle group weight conversion (untimed, offline) on {cores} threads")
+        Wq_o, s_w_o = oracle.group_quantize_weight(Wb, wl.dtype, G)
+        t0 = time.perf_counter()
+        Xq_o, s_x_o = oracle.group_quantize_rows(Xb, wl.dtype, G)
+        t_xpass = time.perf_counter() - t0
+        probe = np.arange(min(cores, wl.M))
+        t0 = time.perf_counter()
+        oracle.group_gemm(Xq_o, s_x_o, Wq_o, s_w_o, G, wl.dtype, probe)
+        t_probe = time.perf_counter() - t0
+        rounds = int(max(1.0, (args.cpu_seconds - t_xpass) / max(t_probe, 1e-9)))
+        R = int(min(wl.M, probe.size * rounds))
+        t0 = time.perf_counter()
+        oracle.group_gemm(Xq_o, s_x_o, Wq_o, s_w_o, G, wl.dtype, np.arange(R))
+        t = time.perf_counter() - t0 + t_xpass * R / wl.M
+        line["cpu_baseline"] = {
+            "value": 2.0 * R * wl.N * wl.K / t / 1e12, "unit": "TOPS", "cores": cores, "kind": "oracle",
+            "sample": (f"group X pass over all {wl.M} rows (time prorated to the sample) + group-wise products for "
+                       f"rows 0..{R - 1} of {wl.M}; {t:.1f} s of CPU work")}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 # ---------------------------------------------------------------------------------------
 
 def main() -> int:
@@ -355,6 +481,9 @@ def main() -> int:
                     help="summarize two rocprofv3 counter runs into the stored traffic record and exit")
     ap.add_argument("--fixed", action="store_true",
                     help="time the fixed-outlier path (the workload's injected columns as the set) instead")
+    ap.add_argument("--group", type=int, default=0, metavar="G",
+                    help="time the group-wise path with groups of G features along K instead (no outlier "
+                         "decomposition)")
     ap.add_argument("--codec", action="store_true",
                     help="benchmark the block-wise int8 codec instead (its own JSON line)")
     ap.add_argument("--trace-summary", nargs=3, metavar=("TRACE_DIR", "BENCH_OUT", "COMMAND"),
@@ -365,9 +494,10 @@ def main() -> int:
 
     wl = workloads.WORKLOADS[args.workload]
     if args.trace_summary:
-        return trace_summary(args.trace_summary[0], args.trace_summary[1], wl, args.trace_summary[2])
+        return trace_summary(args.trace_summary[0], args.trace_summary[1], wl, args.trace_summary[2], args.group)
     if args.traffic_summary:
-        return traffic_summary(args.traffic_summary[0], args.traffic_summary[1], wl, args.copy_mib or 1024)
+        return traffic_summary(args.traffic_summary[0], args.traffic_summary[1], wl, args.copy_mib or 1024,
+                               args.group)
     if args.gpus != 1:
         print(f"bench.py: one GPU only; --gpus {args.gpus} is not supported (the library has no multi-GPU "
               f"path: each GPU would run the same kernels on its own column shard)", file=sys.stderr)
@@ -375,6 +505,8 @@ def main() -> int:
 
     if args.codec:
         return codec_bench(args)
+    if args.group:
+        return group_bench(args, wl)
 
     import torch
 
@@ -394,15 +526,7 @@ def main() -> int:
     torch.cuda.synchronize()
 
     if args.copy_mib > 0:
-        # counter calibration: an elementwise kernel that reads and writes copy_mib MiB once
-        n = args.copy_mib * 1024 * 1024 // 4
-        src = torch.empty(n, dtype=torch.int32, device=dev)  # no fill kernel: the add is the only elementwise one
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.add(src, 1, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
-        torch.cuda.empty_cache()
+        calibration_copy(args.copy_mib, dev, torch)
 
     if args.fixed:
         # the workload's injected outlier columns, fixed offline: no detection per call
@@ -460,7 +584,7 @@ def main() -> int:
         log(f"step {ms_step * 1e3:.1f} us = {tops:.0f} TOPS; {kernel} {ms_gemm * 1e3:.1f} us = {achieved:.0f} TOPS;"
             f" X pass {ms_xpass * 1e3:.1f} us; n_outliers {n_out}")
     else:
-        alg_bytes = wl.N * wl.K + wl.M * wl.K + 4 * wl.N + 4 * wl.M + 2 * wl.M * wl.N
+        alg_bytes = algorithmic_bytes(wl)
         achieved = alg_bytes / (ms_gemm * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS}

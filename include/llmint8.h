@@ -215,6 +215,52 @@ int int8_blockwise_quantize(const float* x, int64_t n, int64_t block, int8_t* q,
 int int8_blockwise_dequantize(const int8_t* q, const float* absmax, int64_t n, int64_t block, float* x,
                               void* stream);
 
+/*
+ * Group-wise scales along K: the finer granularity than one scale per row or column that
+ * the "nuQmm" report page names (its citation snippets on nuQmm/ZeroQuant and on GPTQ's
+ * grouping, with groups of 1024 weights), applied here to both operands and without the
+ * outlier decomposition.  K is cut into ng = K / G groups of G consecutive features:
+ *   s_x[i*ng + g] = max |X[i,k]| over group g of row i, Xq = the code of that group,
+ *   s_w[n*ng + g] = max |W[k,n]| over group g of column n, Wq = the code of that group
+ *   (the quantizer of the vector-wise conversion: clamp(rne(RN32(x * RN32(127/s))), ±127),
+ *   s = 0 codes 0), and
+ *   y[i,n] = sum over g ascending, in fp32:
+ *            acc = RN32(acc + RN32(RN32((float)C_g * RN32(s_x/127)) * RN32(s_w/127))),
+ *   C_g = the exact int32 product of the group's codes;  Y = RN_T(acc).
+ *   group : G, a power of two in [128, 4096] that divides K, else LLMINT8_EINVAL
+ *           (any value is accepted when K = 0).
+ *
+ * Weight conversion: Wq N x K int8 (16-byte aligned), w_scale N x ng fp32 row-major.
+ * Shape rules, dtype and alignments as int8_quantize_weight.
+ */
+int int8_quantize_weight_group(const void* W, int64_t K, int64_t N, int dtype, int64_t group, int8_t* Wq,
+                               float* w_scale, void* stream);
+
+/*
+ * The group-wise product.  Workspace: int8_matmul_group_workspace_bytes(M, K, group)
+ * bytes, 256-byte aligned (0 if the arguments are invalid).  Afterwards it holds the X
+ * pass's products: Xq (M x K int8, row-major) at offset 0, s_x (M x ng fp32, row-major)
+ * at offset round_up(M*K, 256), and the dequantization factors RN32(s_x/127) transposed
+ * (ng x M) after that.  Y: M x N of X's dtype, 16-byte aligned.  K = 0 gives Y = 0.
+ * Inputs, Y and the workspace must not overlap (LLMINT8_EINVAL).
+ */
+size_t int8_matmul_group_workspace_bytes(int64_t M, int64_t K, int64_t group);
+int int8_matmul_group(const void* X, int64_t M, int64_t K, int dtype, int64_t group, const int8_t* Wq,
+                      const float* w_scale, int64_t N, void* Y, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
+/*
+ * int8_matmul_group in two calls on one workspace, as int8_matmul_prepare / _products: the
+ * X pass (codes, scales and factors of X's row groups) and then the products with their
+ * per-group dequantization.  The products read only the workspace, Wq and w_scale, so one
+ * X pass can serve several weights of the same K and group size.
+ */
+int int8_matmul_group_prepare(const void* X, int64_t M, int64_t K, int dtype, int64_t group, void* workspace,
+                              size_t workspace_bytes, void* stream);
+int int8_matmul_group_products(int64_t M, int64_t K, int dtype, int64_t group, const int8_t* Wq,
+                               const float* w_scale, int64_t N, void* Y, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -60,6 +60,11 @@ _SIGNATURES = {
     "int8_matmul_fixed": (_I, [_P, _I64, _I64, _I, _P, _I64, _P, _P, _P, _I64, _P, _P, _SZ, _P]),
     "int8_blockwise_quantize": (_I, [_P, _I64, _I64, _P, _P, _P]),
     "int8_blockwise_dequantize": (_I, [_P, _P, _I64, _I64, _P, _P]),
+    "int8_quantize_weight_group": (_I, [_P, _I64, _I64, _I, _I64, _P, _P, _P]),
+    "int8_matmul_group_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "int8_matmul_group": (_I, [_P, _I64, _I64, _I, _I64, _P, _P, _I64, _P, _P, _SZ, _P]),
+    "int8_matmul_group_prepare": (_I, [_P, _I64, _I64, _I, _I64, _P, _SZ, _P]),
+    "int8_matmul_group_products": (_I, [_I64, _I64, _I, _I64, _P, _P, _I64, _P, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -337,9 +342,99 @@ def int8_blockwise_dequantize(q: torch.Tensor, absmax: torch.Tensor, block: int 
     return x
 
 
+def int8_quantize_weight_group(W: torch.Tensor, group: int = 1024, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """W (K x N, fp16/bf16) -> (Wq N x K int8, w_scale fp32 N x K/group): one scale per
+    output column and group of `group` consecutive rows of W."""
+    _dev_tensor(W, "W")
+    if W.dtype not in _DT or W.dim() != 2:
+        raise TypeError("W must be a 2-D fp16 or bf16 tensor")
+    K, N = W.shape
+    if group <= 0 or K % group:
+        raise ValueError("group must divide K")
+    Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    s_w = torch.empty((N, K // group), dtype=torch.float32, device=W.device)
+    _check(lib().int8_quantize_weight_group(_ptr(W), K, N, _DT[W.dtype], int(group), _ptr(Wq), _ptr(s_w),
+                                            _stream(W, stream)), "int8_quantize_weight_group")
+    return Wq, s_w
+
+
+def int8_matmul_group_workspace_bytes(M: int, K: int, group: int) -> int:
+    return int(lib().int8_matmul_group_workspace_bytes(M, K, group))
+
+
+def int8_matmul_group(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor, group: int = 1024,
+                      Y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """Y = X W with group-wise scales along K on both operands (no outlier decomposition)."""
+    _dev_tensor(X, "X")
+    if X.dtype not in _DT or X.dim() != 2:
+        raise TypeError("X must be a 2-D fp16 or bf16 tensor")
+    _dev_tensor(Wq, "Wq", torch.int8)
+    _dev_tensor(w_scale, "w_scale", torch.float32)
+    M, K = X.shape
+    N = Wq.shape[0]
+    if group <= 0 or K % group or Wq.dim() != 2 or Wq.shape[1] != K or tuple(w_scale.shape) != (N, K // group):
+        raise ValueError("Wq must be N x K and w_scale N x K/group, with group dividing K")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    _dev_tensor(Y, "Y", X.dtype)
+    if tuple(Y.shape) != (M, N):
+        raise ValueError("Y must be M x N")
+    ws = _workspace(workspace, int8_matmul_group_workspace_bytes(M, K, group), X.device)
+    _check(lib().int8_matmul_group(_ptr(X), M, K, _DT[X.dtype], int(group), _ptr(Wq), _ptr(w_scale), N, _ptr(Y),
+                                   _ptr(ws), ws.numel(), _stream(X, stream)), "int8_matmul_group")
+    return Y
+
+
+def int8_matmul_group_prepare(X: torch.Tensor, group: int, workspace: torch.Tensor, stream=None) -> None:
+    """The X pass of int8_matmul_group into `workspace`."""
+    _dev_tensor(X, "X")
+    if X.dtype not in _DT or X.dim() != 2:
+        raise TypeError("X must be a 2-D fp16 or bf16 tensor")
+    _dev_tensor(workspace, "workspace")
+    M, K = X.shape
+    _check(lib().int8_matmul_group_prepare(_ptr(X), M, K, _DT[X.dtype], int(group), _ptr(workspace),
+                                           workspace.numel(), _stream(X, stream)), "int8_matmul_group_prepare")
+
+
+def int8_matmul_group_products(M: int, K: int, dtype: torch.dtype, group: int, Wq: torch.Tensor,
+                               w_scale: torch.Tensor, workspace: torch.Tensor, Y: Optional[torch.Tensor] = None,
+                               stream=None) -> torch.Tensor:
+    """The products of int8_matmul_group from a workspace filled by int8_matmul_group_prepare."""
+    _dev_tensor(Wq, "Wq", torch.int8)
+    _dev_tensor(w_scale, "w_scale", torch.float32)
+    _dev_tensor(workspace, "workspace")
+    N = Wq.shape[0]
+    if group <= 0 or K % group or Wq.dim() != 2 or Wq.shape[1] != K or tuple(w_scale.shape) != (N, K // group):
+        raise ValueError("Wq must be N x K and w_scale N x K/group, with group dividing K")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=dtype, device=Wq.device)
+    _dev_tensor(Y, "Y", dtype)
+    if tuple(Y.shape) != (M, N):
+        raise ValueError("Y must be M x N")
+    _check(lib().int8_matmul_group_products(M, K, _DT[dtype], int(group), _ptr(Wq), _ptr(w_scale), N, _ptr(Y),
+                                            _ptr(workspace), workspace.numel(), _stream(Wq, stream)),
+           "int8_matmul_group_products")
+    return Y
+
+
+def group_workspace_views(ws: torch.Tensor, M: int, K: int, group: int) -> dict:
+    """The X pass's products left in an int8_matmul_group workspace (see the header)."""
+    ng = K // group
+    b = ws.view(torch.uint8)
+    o_s = (M * K + 255) // 256 * 256
+    o_r = (o_s + 4 * M * ng + 255) // 256 * 256
+    return {
+        "Xq": b[: M * K].view(torch.int8).view(M, K),
+        "s_x": b[o_s: o_s + 4 * M * ng].view(torch.float32).view(M, ng),
+        "r": b[o_r: o_r + 4 * M * ng].view(torch.float32).view(ng, M),
+    }
+
+
 __all__ = [
     "int8_quantize_weight", "int8_matmul", "int8_matmul_stats", "int8_matmul_prepare", "int8_matmul_products", "int8_matmul_workspace_bytes",
     "int8_matmul_workspace_layout", "int8_matmul_accumulators", "workspace_views", "LLMInt8Error", "lib",
     "int8_blockwise_quantize", "int8_blockwise_dequantize", "int8_quantize_weight_fixed", "int8_matmul_fixed",
-    "status_string",
+    "status_string", "int8_quantize_weight_group", "int8_matmul_group", "int8_matmul_group_workspace_bytes",
+    "group_workspace_views", "int8_matmul_group_prepare", "int8_matmul_group_products",
 ]

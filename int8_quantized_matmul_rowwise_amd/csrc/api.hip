@@ -435,3 +435,110 @@ LLMINT8_API int int8_matmul_fixed(const void* X, int64_t M, int64_t K, int dtype
     return products_common(M, K, dtype, Wq, w_scale, N, Y, nullptr, nullptr, workspace, workspace_bytes, stream, true,
                            W_O, P);
 }
+
+// ---- group-wise scales along K
+
+namespace {
+
+struct GroupLayout {
+    size_t xq, s_x, rg, total;
+};
+
+GroupLayout group_layout(int64_t M, int64_t K, int64_t G) {
+    GroupLayout L;
+    const size_t m = (size_t)M, ng = (size_t)(K / G);
+    L.xq = 0;
+    L.s_x = align_up(m * (size_t)K);
+    L.rg = align_up(L.s_x + 4 * m * ng);
+    L.total = align_up(L.rg + 4 * m * ng);
+    return L;
+}
+
+int check_group(int64_t M, int64_t K, int64_t N, int dtype, int64_t G) {
+    int rc = check_shape(M, K, N, dtype);
+    if (rc) return rc;
+    if (K > 0 && !group_size_ok(G, K)) return LLMINT8_EINVAL;
+    if (ceil_div(M, 256) * ceil_div(N, 128) > kMaxDim) return LLMINT8_ERANGE;
+    return LLMINT8_OK;
+}
+
+}  // namespace
+
+LLMINT8_API int int8_quantize_weight_group(const void* W, int64_t K, int64_t N, int dtype, int64_t group, int8_t* Wq,
+                                           float* w_scale, void* stream) {
+    int rc = check_group(0, K, N, dtype, group);
+    if (rc) return rc;
+    if (N == 0 || K == 0) return LLMINT8_OK;
+    const size_t wb = (size_t)K * N * 2, qb = (size_t)K * N, sb = (size_t)N * (size_t)(K / group) * 4;
+    if (!W || !Wq || !w_scale || !aligned(W, 16) || !aligned(Wq, 16) || !aligned(w_scale, 4)) return LLMINT8_EINVAL;
+    if (overlap(W, wb, Wq, qb) || overlap(W, wb, w_scale, sb) || overlap(Wq, qb, w_scale, sb)) return LLMINT8_EINVAL;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = launch_group_colmax(dtype, W, K, N, group, w_scale, st);
+    if (e == hipSuccess) e = launch_quantize_weight_groups(dtype, W, K, N, w_scale, group, Wq, st);
+    return hip_status(e);
+}
+
+LLMINT8_API size_t int8_matmul_group_workspace_bytes(int64_t M, int64_t K, int64_t group) {
+    if (M < 0 || K < 0 || (K > 0 && !group_size_ok(group, K))) return 0;
+    if (K == 0) return align_up(0);
+    return group_layout(M, K, group).total;
+}
+
+namespace {
+
+// int8_matmul_group and its two halves: the X pass (xpass) into the workspace and the
+// products (products) from it.
+int group_common(const void* X, int64_t M, int64_t K, int dtype, int64_t group, const int8_t* Wq,
+                 const float* w_scale, int64_t N, void* Y, void* workspace, size_t workspace_bytes, void* stream,
+                 bool xpass, bool products) {
+    int rc = check_group(M, K, N, dtype, group);
+    if (rc) return rc;
+    if (M == 0 || (products && N == 0 && !xpass)) return LLMINT8_OK;
+    hipStream_t st = (hipStream_t)stream;
+    if (products && N > 0) {
+        if (!Y || !aligned(Y, 16)) return LLMINT8_EINVAL;
+        if (K == 0) return hip_status(launch_fill_zero((float*)Y, M * N / 2, st));  // the empty sum; N is even
+        if (!Wq || !w_scale || !aligned(Wq, 16) || !aligned(w_scale, 4)) return LLMINT8_EINVAL;
+    }
+    if (K == 0) return LLMINT8_OK;
+    if (xpass && (!X || !aligned(X, 16))) return LLMINT8_EINVAL;
+    const GroupLayout L = group_layout(M, K, group);
+    if (!workspace || !aligned(workspace, 256) || workspace_bytes < L.total) return LLMINT8_EWORKSPACE;
+    const size_t xb = xpass ? (size_t)M * K * 2 : 0, yb = products ? (size_t)M * N * 2 : 0,
+                 qb = products ? (size_t)N * K : 0, sb = products ? (size_t)N * (size_t)(K / group) * 4 : 0;
+    if (overlap(workspace, L.total, X, xb) || overlap(workspace, L.total, Wq, qb) ||
+        overlap(workspace, L.total, w_scale, sb) || overlap(workspace, L.total, Y, yb) || overlap(Y, yb, X, xb) ||
+        overlap(Y, yb, Wq, qb) || overlap(Y, yb, w_scale, sb))
+        return LLMINT8_EINVAL;
+    int8_t* ws = (int8_t*)workspace;
+    int8_t* Xq = ws + L.xq;
+    float* s_x = (float*)(ws + L.s_x);
+    float* rg = (float*)(ws + L.rg);
+    hipError_t e = hipSuccess;
+    if (xpass) e = launch_group_xpass(dtype, X, M, K, group, Xq, s_x, rg, st);
+    if (e == hipSuccess && products && N > 0) e = launch_gemm_group(dtype, Xq, rg, Wq, w_scale, M, N, K, group, Y, st);
+    return hip_status(e);
+}
+
+}  // namespace
+
+LLMINT8_API int int8_matmul_group(const void* X, int64_t M, int64_t K, int dtype, int64_t group, const int8_t* Wq,
+                                  const float* w_scale, int64_t N, void* Y, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    int rc = check_group(M, K, N, dtype, group);
+    if (rc || M == 0 || N == 0) return rc;
+    return group_common(X, M, K, dtype, group, Wq, w_scale, N, Y, workspace, workspace_bytes, stream, true, true);
+}
+
+LLMINT8_API int int8_matmul_group_prepare(const void* X, int64_t M, int64_t K, int dtype, int64_t group,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+    return group_common(X, M, K, dtype, group, nullptr, nullptr, 0, nullptr, workspace, workspace_bytes, stream, true,
+                        false);
+}
+
+LLMINT8_API int int8_matmul_group_products(int64_t M, int64_t K, int dtype, int64_t group, const int8_t* Wq,
+                                           const float* w_scale, int64_t N, void* Y, void* workspace,
+                                           size_t workspace_bytes, void* stream) {
+    return group_common(nullptr, M, K, dtype, group, Wq, w_scale, N, Y, workspace, workspace_bytes, stream, false,
+                        true);
+}

@@ -1,0 +1,422 @@
+// Group-wise scales along K: one absmax scale per group of G consecutive input features,
+// for every row of X and every column of W (the finer granularity the "nuQmm" report page
+// discusses for weight quantization; here for both operands, without the outlier
+// decomposition).  G is a power of two, G >= 128 and G divides K; ng = K / G.
+//   s_x[i*ng + g], Xq[i,k]: the vector-wise code of each row group;
+//   s_w[n*ng + g], Wq[n,k]: the same for each column group of W;
+//   C_g = Xq_g Wq_g^T (exact int32), and per output element
+//   acc = 0; for g ascending: acc = RN32(acc + RN32(RN32((float)C_g * r_ig) * c_ng)),
+//   r_ig = RN32(s_x/127), c_ng = RN32(s_w/127);  Y = RN_T(acc).
+//
+// Product kernel: the tiled int8 MFMA kernel's scheme (K stages of 128 bytes through
+// global_load_lds, 3 A / 2 B slots, counted waits, XOR chunk swizzle, XCD-contiguous tile
+// order) with a 256 x 128 tile, so that each lane holds 128 int32 accumulators (AGPRs) and
+// 128 fp32 sums.  At the end of each group every wave folds its int32 partials into the
+// fp32 sums and clears them.  The group's factors come through LDS: r (precomputed by the X
+// pass, group-major) and s_w for the tile's rows and columns, loaded straight into LDS at
+// the group's first stage, before that stage's operand loads, so the stage's counted wait
+// and barrier cover them too; two slots alternate between groups.
+#include <type_traits>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace llmint8 {
+
+namespace {
+
+constexpr int NJ = 2;                           // 32-column MFMA tiles per wave along N
+constexpr int BM = 256, BN = 64 * NJ;           // 256 x 128
+constexpr int BK = 128;
+constexpr int kTileBytesA = BM * BK;            // 32 KB
+constexpr int kTileBytesB = BN * BK;            // 16 KB
+constexpr int kChunks = BK / 16;
+constexpr int kRowsPerLoad = 64 / kChunks;      // 8
+constexpr int kLoadsA = BM / kRowsPerLoad / 4;  // 8 per wave and stage
+constexpr int kLoadsB = BN / kRowsPerLoad / 4;  // 4 per wave and stage
+constexpr int kSlotsA = 3, kSlotsB = 2;
+constexpr int kOperandBytes = kSlotsA * kTileBytesA + kSlotsB * kTileBytesB;  // 128 KB
+constexpr int kScaleBytes = 2 * (BM + BN) * 4;                                // two slots of r and s_w
+constexpr int kSubSteps = BK / 32;
+constexpr int kGroupM = 8;
+constexpr int kXcds = 8;
+constexpr int kYPitch = 32 * NJ + 8;             // epilogue staging row, 16-bit elements
+constexpr int kYStageBytes = 128 * kYPitch * 2;
+static_assert(kOperandBytes + kScaleBytes <= 160 * 1024, "LDS");
+static_assert(4 * kYStageBytes <= kOperandBytes, "epilogue LDS");
+static_assert(kLoadsA == 8, "the barrier's wait leaves the 8 loads of the long-lead operand in flight");
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Every lambda of the product kernel is inlined: one left out of line would take the
+// accumulator arrays it captures by reference into private (scratch) memory.
+#define LLMINT8_INLINE __attribute__((always_inline))
+
+__device__ __forceinline__ void load_lds16(const void* g, int8_t* lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(const void* g, int8_t* lds) {
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 4, 0, 0);
+}
+
+__host__ __device__ constexpr int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+#define LLMINT8_GROUP_WAIT_BARRIER(N)                                              \
+    do {                                                                           \
+        __builtin_amdgcn_s_waitcnt(0xC07F);                                        \
+        asm volatile("s_waitcnt vmcnt(" #N ")\n\ts_barrier" ::: "memory");         \
+    } while (0)
+
+struct GroupParams {
+    const int8_t* Xq;   // M x K (pitch K)
+    const float* rg;    // ng x M: r = RN32(s_x / 127), group-major
+    const int8_t* Wq;   // N x K
+    const float* s_w;   // N x ng
+    int64_t M, N, K, ng;
+    int gs;             // K stages per group (G / 128)
+    uint16_t* Y;
+    int tiles_m, tiles_n;
+};
+
+template <int DT>
+__global__ __launch_bounds__(256, 1) void gemm_group_kernel(GroupParams p) {
+    __shared__ __attribute__((aligned(1024))) int8_t smem[kOperandBytes + kScaleBytes];
+    float* rbuf = (float*)(smem + kOperandBytes);  // [2][BM]
+    float* cbuf = rbuf + 2 * BM;                   // [2][BN]: s_w of the tile's columns
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int wm = w >> 1, wn = w & 1;
+
+    const int T = p.tiles_m * p.tiles_n;
+    const int bid = blockIdx.x;
+    const int xcd = bid % kXcds, local = bid / kXcds;
+    const int per = T / kXcds, rem = T % kXcds;
+    const int t = xcd * per + (xcd < rem ? xcd : rem) + local;
+    const int in_group = kGroupM * p.tiles_n;
+    const int first_m = (t / in_group) * kGroupM;
+    const int gm = p.tiles_m - first_m < kGroupM ? p.tiles_m - first_m : kGroupM;
+    const int tm = first_m + (t % in_group) % gm;
+    const int tn = (t % in_group) / gm;
+    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    uint32_t a_off[kLoadsA], b_off[kLoadsB];
+#pragma unroll
+    for (int j = 0; j < kLoadsA; ++j) {
+        const int r = kRowsPerLoad * (kLoadsA * wu + j) + lane / kChunks;
+        const int c = (lane % kChunks) ^ swz(r);
+        const int64_t m = m0 + r < p.M ? m0 + r : p.M - 1;
+        a_off[j] = (uint32_t)((m - m0) * p.K + c * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < kLoadsB; ++j) {
+        const int r = kRowsPerLoad * (kLoadsB * wu + j) + lane / kChunks;
+        const int c = (lane % kChunks) ^ swz(r);
+        const int64_t n = n0 + r < p.N ? n0 + r : p.N - 1;
+        b_off[j] = (uint32_t)((n - n0) * p.K + c * 16);
+    }
+    const int8_t* a_tile = p.Xq + m0 * p.K;
+    const int8_t* b_tile = p.Wq + n0 * p.K;
+    const int nk = (int)(p.K / BK);  // K is a multiple of G >= 128
+
+    auto slot_a = [&](int kt) LLMINT8_INLINE { return smem + (kt % kSlotsA) * kTileBytesA; };
+    auto slot_b = [&](int kt) LLMINT8_INLINE { return smem + kSlotsA * kTileBytesA + (kt % kSlotsB) * kTileBytesB; };
+    auto issue_a = [&](int kt) LLMINT8_INLINE {
+        int8_t* As = slot_a(kt);
+#pragma unroll
+        for (int j = 0; j < kLoadsA; ++j) load_lds16(a_tile + kt * BK + a_off[j], As + (kLoadsA * wu + j) * 1024);
+    };
+    auto issue_b = [&](int kt) LLMINT8_INLINE {
+        int8_t* Bs = slot_b(kt);
+#pragma unroll
+        for (int j = 0; j < kLoadsB; ++j) load_lds16(b_tile + kt * BK + b_off[j], Bs + (kLoadsB * wu + j) * 1024);
+    };
+    // the factors of group g: r of the tile's 256 rows (each wave 64), s_w of its 128 columns
+    // (waves 0 and 1, 64 each); rows and columns past the matrix read the last one (unused)
+    auto issue_scales = [&](int g) LLMINT8_INLINE {
+        const int64_t m = m0 + 64 * wu + lane < p.M ? m0 + 64 * wu + lane : p.M - 1;
+        load_lds4(p.rg + (int64_t)g * p.M + m, (int8_t*)(rbuf + (g & 1) * BM + 64 * wu));
+        if (wu < 2) {
+            const int64_t n = n0 + 64 * wu + lane < p.N ? n0 + 64 * wu + lane : p.N - 1;
+            load_lds4(p.s_w + n * p.ng + g, (int8_t*)(cbuf + (g & 1) * BN + 64 * wu));
+        }
+    };
+
+    const int rl = lane & 31, h = lane >> 5;
+    int rd[kSubSteps];
+#pragma unroll
+    for (int u = 0; u < kSubSteps; ++u) rd[u] = rl * BK + (((2 * u + h) ^ swz(rl)) << 4);
+    auto read_frags = [&](int kt, int u, v4i (&fa)[4], v4i (&fb)[NJ]) LLMINT8_INLINE {
+        const int8_t* As = slot_a(kt) + wm * 128 * BK + rd[u];
+        const int8_t* Bs = slot_b(kt) + wn * (32 * NJ) * BK + rd[u];
+        fa[0] = *(const v4i*)As;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) fb[j] = *(const v4i*)(Bs + j * 32 * BK);
+#pragma unroll
+        for (int i = 1; i < 4; ++i) fa[i] = *(const v4i*)(As + i * 32 * BK);
+    };
+
+    v16i acc[4][NJ];
+    v16f accf[4][NJ];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            acc[i][j] = v16i{};
+            accf[i][j] = v16f{};
+        }
+    auto mfma_rows = [&](const v4i (&fa)[4], const v4i (&fb)[NJ], int i0, int i1) LLMINT8_INLINE {
+#pragma unroll
+        for (int i = i0; i < i1; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    };
+    // fold group g into the fp32 sums (lane: column 32j + lane%32 of the wave's 64, rows
+    // 8*(e/4) + 4*(lane/32) + e%4 of each 32-row slice)
+    auto fold = [&](int g) LLMINT8_INLINE {
+        const float* rb = rbuf + (g & 1) * BM + wm * 128;
+        const float* cb = cbuf + (g & 1) * BN + wn * 64;
+        float c[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) c[j] = cb[32 * j + rl] / 127.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float r[16];
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+                const v4f t4 = *(const v4f*)(rb + 32 * i + 8 * a + 4 * h);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) r[4 * a + b] = t4[b];
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    accf[i][j][e] = __fadd_rn(accf[i][j][e], __fmul_rn(__fmul_rn((float)acc[i][j][e], r[e]), c[j]));
+                acc[i][j] = v16i{};
+            }
+        }
+    };
+
+    // One K stage (as the vector-wise kernel): sub-steps 0..2 with the next sub-step's LDS
+    // reads, sub-step 0 also issuing (at a group's first stage) the group's factors and
+    // B[kt+1], sub-step 1 A[kt+2]; sub-step 3 meets the barrier after 2 MFMAs.  At a group's
+    // last stage the fold follows.
+    v4i fa[2][4], fb[2][NJ];
+    auto stage = [&](int kt, auto steady_tag) LLMINT8_INLINE {
+        constexpr bool STEADY = decltype(steady_tag)::value;
+        const bool next = STEADY || kt + 1 < nk;
+#pragma unroll
+        for (int u = 0; u < kSubSteps - 1; ++u) {
+            const int cur = u & 1, nxt = cur ^ 1;
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            if (u == 0) {
+                if (kt % p.gs == 0) issue_scales(kt / p.gs);
+                if (next) issue_b(kt + 1);
+            }
+            if (u == 1 && STEADY) issue_a(kt + 2);
+            read_frags(kt, u + 1, fa[nxt], fb[nxt]);
+            mfma_rows(fa[cur], fb[cur], 0, 4);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        mfma_rows(fa[1], fb[1], 0, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (STEADY) LLMINT8_GROUP_WAIT_BARRIER(8);  // A[kt+2] may stay in flight
+        else LLMINT8_GROUP_WAIT_BARRIER(0);
+        if (next) read_frags(kt + 1, 0, fa[0], fb[0]);
+        mfma_rows(fa[1], fb[1], 1, 4);
+        __builtin_amdgcn_sched_barrier(0);
+        if ((kt + 1) % p.gs == 0) fold(kt / p.gs);
+    };
+
+    // prologue: A[0], B[0], A[1] in flight; wait for A[0] and B[0]
+    issue_a(0);
+    issue_b(0);
+    if (nk > 1) {
+        issue_a(1);
+        LLMINT8_GROUP_WAIT_BARRIER(8);
+    } else {
+        LLMINT8_GROUP_WAIT_BARRIER(0);
+    }
+    read_frags(0, 0, fa[0], fb[0]);
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) stage(kt, std::true_type{});
+    for (; kt < nk; ++kt) stage(kt, std::false_type{});
+
+    // ---- epilogue: Y = RN_T(sums), staged per wave in LDS, written as 16-byte row segments
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    uint16_t* ys = (uint16_t*)(smem + w * kYStageBytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                ys[(32 * i + 8 * (e >> 2) + 4 * h + (e & 3)) * kYPitch + 32 * j + rl] = from_f32<DT>(accf[i][j][e]);
+    const int64_t wm0 = m0 + wm * 128, wn0 = n0 + wn * (32 * NJ);
+    constexpr int kLanesPerRow = 32 * NJ / 8;        // 16-byte segments per staged row
+    constexpr int kRowsPerIter = 64 / kLanesPerRow;
+#pragma unroll 4
+    for (int it = 0; it < 128 / kRowsPerIter; ++it) {
+        const int row = it * kRowsPerIter + lane / kLanesPerRow, ch = lane % kLanesPerRow;
+        const u32x4 v = *(const u32x4*)(ys + row * kYPitch + ch * 8);
+        const int64_t m = wm0 + row, n = wn0 + ch * 8;
+        if (m < p.M && n < p.N) *(u32x4*)(p.Y + m * p.N + n) = v;
+    }
+}
+
+// ---- X pass: the group-wise codes of X.  Row groups never cross rows (G divides K), so X
+// is a flat run of M * ng groups of G elements: SEG lanes take one group (SEG = 64, or 16 /
+// 32 for G = 128 / 256), each lane NV 16-byte chunks of 8 elements, one wave access 1 KB.
+template <int DT, int NV, int SEG>
+__global__ __launch_bounds__(256) void group_rows_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                         int64_t G, int8_t* __restrict__ Xq, float* __restrict__ s_x,
+                                                         float* __restrict__ rg) {
+    constexpr int BPW = 64 / SEG;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int sub = lane / SEG, sl = lane % SEG;
+    const int64_t ng = K / G, nblocks = M * ng;
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    for (int64_t b0 = ((int64_t)blockIdx.x * 4 + w) * BPW; b0 < nblocks; b0 += nwaves * BPW) {
+        const int64_t b = b0 + sub;
+        const bool in = b < nblocks;
+        const int64_t lo = (in ? b : 0) * G;
+        u32x4 v[NV];
+#pragma unroll
+        for (int j = 0; j < NV; ++j) v[j] = in ? *(const u32x4*)(X + lo + 8 * ((int64_t)j * SEG + sl)) : u32x4{0u, 0u, 0u, 0u};
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const uint32_t a = v[j][d] & 0x7fff7fffu;  // magnitudes: unsigned order = |x| order
+                const uint32_t lo16 = a & 0xffffu, hi16 = a >> 16;
+                m = m > lo16 ? m : lo16;
+                m = m > hi16 ? m : hi16;
+            }
+#pragma unroll
+        for (int off = SEG / 2; off > 0; off >>= 1) {
+            const uint32_t o = (uint32_t)__shfl_xor((int)m, off, kWave);
+            m = m > o ? m : o;
+        }
+        const float s = to_f32<DT>((uint16_t)m);
+        const float inv = inv_scale(s);
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            uint32_t t[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                float f = __fmul_rn(to_f32<DT>((uint16_t)(v[j][k >> 1] >> (16 * (k & 1)))), inv);
+                f = fminf(fmaxf(f, -127.0f), 127.0f);
+                t[k] = __builtin_bit_cast(uint32_t, __fadd_rn(f, 12582912.0f));  // rne into the low byte
+            }
+            u32x2 q;
+            q[0] = __builtin_amdgcn_perm(t[1], t[0], 0x0c0c0400u) | __builtin_amdgcn_perm(t[3], t[2], 0x04000c0cu);
+            q[1] = __builtin_amdgcn_perm(t[5], t[4], 0x0c0c0400u) | __builtin_amdgcn_perm(t[7], t[6], 0x04000c0cu);
+            if (in) *(u32x2*)(Xq + lo + 8 * ((int64_t)j * SEG + sl)) = q;
+        }
+        if (sl == 0 && in) {
+            const int64_t i = b / ng, g = b % ng;
+            s_x[b] = s;                    // row-major: i * ng + g
+            rg[g * M + i] = s / 127.0f;    // group-major dequantization factor
+        }
+    }
+}
+
+// ---- weight scales: s_w[n*ng + g] = max |W[k,n]| over group g; one workgroup per (512
+// columns, group), its four waves split the group's rows, no atomics.
+template <int DT>
+__global__ __launch_bounds__(256) void group_colmax_kernel(const uint16_t* __restrict__ W, int64_t K, int64_t N,
+                                                           int64_t G, float* __restrict__ s_w) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int64_t n8 = ((int64_t)blockIdx.x * 64 + lane) * 8;
+    const int64_t g = blockIdx.y, ng = K / G;
+    float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (n8 < N) {
+        for (int64_t k = g * G + w; k < (g + 1) * G; k += 4) {
+            const u32x4 v = *(const u32x4*)(W + k * N + n8);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                m[j] = fmaxf(m[j], __builtin_fabsf(to_f32<DT>((uint16_t)(v[j >> 1] >> (16 * (j & 1))))));
+        }
+    }
+    __shared__ float sm[4][64][9];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sm[w][lane][j] = m[j];
+    __syncthreads();
+    if (w == 0 && n8 < N) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            s_w[(n8 + j) * ng + g] = fmaxf(fmaxf(sm[0][lane][j], sm[1][lane][j]), fmaxf(sm[2][lane][j], sm[3][lane][j]));
+    }
+}
+
+template <int DT, int NV, int SEG>
+hipError_t group_rows_launch(const void* X, int64_t M, int64_t K, int64_t G, int8_t* Xq, float* s_x, float* rg,
+                             hipStream_t stream) {
+    const int64_t nblocks = M * (K / G);
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    const int64_t need = ceil_div(nblocks, 4 * (64 / SEG));
+    const unsigned grid = (unsigned)(need < (int64_t)cus * 8 ? need : (int64_t)cus * 8);
+    group_rows_kernel<DT, NV, SEG><<<grid, 256, 0, stream>>>((const uint16_t*)X, M, K, G, Xq, s_x, rg);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t group_rows_dispatch(const void* X, int64_t M, int64_t K, int64_t G, int8_t* Xq, float* s_x, float* rg,
+                               hipStream_t stream) {
+    switch (G) {
+        case 128: return group_rows_launch<DT, 1, 16>(X, M, K, G, Xq, s_x, rg, stream);
+        case 256: return group_rows_launch<DT, 1, 32>(X, M, K, G, Xq, s_x, rg, stream);
+        case 512: return group_rows_launch<DT, 1, 64>(X, M, K, G, Xq, s_x, rg, stream);
+        case 1024: return group_rows_launch<DT, 2, 64>(X, M, K, G, Xq, s_x, rg, stream);
+        case 2048: return group_rows_launch<DT, 4, 64>(X, M, K, G, Xq, s_x, rg, stream);
+        default: return group_rows_launch<DT, 8, 64>(X, M, K, G, Xq, s_x, rg, stream);  // 4096
+    }
+}
+
+}  // namespace
+
+bool group_size_ok(int64_t G, int64_t K) { return G >= 128 && G <= 4096 && (G & (G - 1)) == 0 && K % G == 0; }
+
+hipError_t launch_group_xpass(int dt, const void* X, int64_t M, int64_t K, int64_t G, int8_t* Xq, float* s_x,
+                              float* rg, hipStream_t stream) {
+    if (M == 0 || K == 0) return hipSuccess;
+    return dt == F16 ? group_rows_dispatch<F16>(X, M, K, G, Xq, s_x, rg, stream)
+                     : group_rows_dispatch<BF16>(X, M, K, G, Xq, s_x, rg, stream);
+}
+
+hipError_t launch_group_colmax(int dt, const void* W, int64_t K, int64_t N, int64_t G, float* s_w,
+                               hipStream_t stream) {
+    if (N == 0 || K == 0) return hipSuccess;
+    dim3 g((unsigned)ceil_div(N, 512), (unsigned)(K / G));
+    if (dt == F16) group_colmax_kernel<F16><<<g, 256, 0, stream>>>((const uint16_t*)W, K, N, G, s_w);
+    else group_colmax_kernel<BF16><<<g, 256, 0, stream>>>((const uint16_t*)W, K, N, G, s_w);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_group(int dt, const int8_t* Xq, const float* rg, const int8_t* Wq, const float* s_w, int64_t M,
+                             int64_t N, int64_t K, int64_t G, void* Y, hipStream_t stream) {
+    if (M == 0 || N == 0) return hipSuccess;
+    GroupParams p;
+    p.Xq = Xq;
+    p.rg = rg;
+    p.Wq = Wq;
+    p.s_w = s_w;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.ng = K / G;
+    p.gs = (int)(G / BK);
+    p.Y = (uint16_t*)Y;
+    p.tiles_m = (int)ceil_div(M, BM);
+    p.tiles_n = (int)ceil_div(N, BN);
+    const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
+    if (dt == F16) gemm_group_kernel<F16><<<grid, 256, 0, stream>>>(p);
+    else gemm_group_kernel<BF16><<<grid, 256, 0, stream>>>(p);
+    return hipGetLastError();
+}
+
+}  // namespace llmint8

@@ -14,6 +14,8 @@ int64_t weight_splits(int64_t K);
 hipError_t launch_weight(int dt, const void* W, int64_t K, int64_t N, int8_t* Wq, float* w_scale,
                          const uint32_t* skip /* nullable: rows of W (outlier set) to leave out */,
                          hipStream_t stream);
+// p[0, n) = 0 (a kernel, not a memset node, so that the call can be captured in a graph)
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream);
 // W_O (N x P, 16-bit): W[O[t], n] for t < nO, zero up to P.
 hipError_t launch_gather_wo(const void* W, int64_t K, int64_t N, const int32_t* O, int64_t nO, int64_t P, void* WO,
                             hipStream_t stream);
@@ -84,5 +86,20 @@ hipError_t launch_block_quantize(const float* x, int64_t n, int64_t block, int8_
                                  hipStream_t stream);
 hipError_t launch_block_dequantize(const int8_t* q, const float* absmax, int64_t n, int64_t block, float* x,
                                    hipStream_t stream);
+
+// ---- group-wise scales along K (G a power of two in [128, 4096] dividing K)
+bool group_size_ok(int64_t G, int64_t K);
+// s_w[n*ng + g] = absmax of column n of W over rows [g*G, (g+1)*G)
+hipError_t launch_group_colmax(int dt, const void* W, int64_t K, int64_t N, int64_t G, float* s_w,
+                               hipStream_t stream);
+// Wq (N x K) with the per-group column scales
+hipError_t launch_quantize_weight_groups(int dt, const void* W, int64_t K, int64_t N, const float* s_w, int64_t G,
+                                         int8_t* Wq, hipStream_t stream);
+// Xq (M x K), s_x (M x ng) and rg (ng x M, RN32(s_x/127), group-major) of X's row groups
+hipError_t launch_group_xpass(int dt, const void* X, int64_t M, int64_t K, int64_t G, int8_t* Xq, float* s_x,
+                              float* rg, hipStream_t stream);
+// Y (M x N, 16-bit) = the group-wise product (per-group int32 partials folded into fp32)
+hipError_t launch_gemm_group(int dt, const int8_t* Xq, const float* rg, const int8_t* Wq, const float* s_w, int64_t M,
+                             int64_t N, int64_t K, int64_t G, void* Y, hipStream_t stream);
 
 }  // namespace llmint8

@@ -57,17 +57,19 @@ __global__ __launch_bounds__(256) void colmax_kernel(const uint16_t* __restrict_
 }
 
 // Wq[n,k] = code of W[k,n] with the column's scale.  Tile: 128 rows of W (k) x 64
-// columns (n); read along n (coalesced), transpose through LDS, write along k.
+// columns (n); read along n (coalesced), transpose through LDS, write along k.  Scales
+// per group of G rows (G a multiple of 128, so a tile lies in one group): the scale of
+// column n and group g is s_w[n*ng + g]; the vector-wise case is ng = 1, G = K.
 template <int DT>
 __global__ __launch_bounds__(256) void quantize_weight_kernel(const uint16_t* __restrict__ W, int64_t K, int64_t N,
-                                                              const float* __restrict__ s_w,
+                                                              const float* __restrict__ s_w, int64_t ng, int64_t G,
                                                               const uint32_t* __restrict__ skip,
                                                               int8_t* __restrict__ Wq) {
     __shared__ float inv[64];
     __shared__ __attribute__((aligned(16))) uint8_t tile[64][128 + 16];
     const int tid = threadIdx.x;
     const int64_t n0 = (int64_t)blockIdx.x * 64, k0 = (int64_t)blockIdx.y * 128;
-    if (tid < 64) inv[tid] = (n0 + tid < N) ? inv_scale(s_w[n0 + tid]) : 0.0f;
+    if (tid < 64) inv[tid] = (n0 + tid < N) ? inv_scale(s_w[(n0 + tid) * ng + k0 / G]) : 0.0f;
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -114,6 +116,12 @@ hipError_t launch_gather_wo(const void* W, int64_t K, int64_t N, const int32_t* 
     return hipGetLastError();
 }
 
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    fill_zero_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, stream>>>(p, n);
+    return hipGetLastError();
+}
+
 int64_t weight_splits(int64_t K) {
     int64_t s = ceil_div(K, 256);
     return s < 1 ? 1 : (s > 64 ? 64 : s);
@@ -131,11 +139,22 @@ hipError_t launch_weight(int dt, const void* W, int64_t K, int64_t N, int8_t* Wq
     dim3 g2((unsigned)ceil_div(N, 64), (unsigned)ceil_div(K, 128));
     if (dt == F16) {
         colmax_kernel<F16><<<g1, 256, 0, stream>>>((const uint16_t*)W, K, N, rps, skip, w_scale);
-        quantize_weight_kernel<F16><<<g2, 256, 0, stream>>>((const uint16_t*)W, K, N, w_scale, skip, Wq);
+        quantize_weight_kernel<F16><<<g2, 256, 0, stream>>>((const uint16_t*)W, K, N, w_scale, 1, K, skip, Wq);
     } else {
         colmax_kernel<BF16><<<g1, 256, 0, stream>>>((const uint16_t*)W, K, N, rps, skip, w_scale);
-        quantize_weight_kernel<BF16><<<g2, 256, 0, stream>>>((const uint16_t*)W, K, N, w_scale, skip, Wq);
+        quantize_weight_kernel<BF16><<<g2, 256, 0, stream>>>((const uint16_t*)W, K, N, w_scale, 1, K, skip, Wq);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_weight_groups(int dt, const void* W, int64_t K, int64_t N, const float* s_w, int64_t G,
+                                         int8_t* Wq, hipStream_t stream) {
+    if (N == 0 || K == 0) return hipSuccess;
+    dim3 g2((unsigned)ceil_div(N, 64), (unsigned)ceil_div(K, 128));
+    if (dt == F16)
+        quantize_weight_kernel<F16><<<g2, 256, 0, stream>>>((const uint16_t*)W, K, N, s_w, K / G, G, nullptr, Wq);
+    else
+        quantize_weight_kernel<BF16><<<g2, 256, 0, stream>>>((const uint16_t*)W, K, N, s_w, K / G, G, nullptr, Wq);
     return hipGetLastError();
 }
 

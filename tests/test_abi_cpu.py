@@ -152,3 +152,49 @@ def test_fixed_outlier_entry_points_reject():
     assert mf(X, 4, 64, 0, O, 2, Wq, S, WO, 8, WO + 64, WS, big, None) == L.EINVAL  # Y overlaps W_O
     assert mf(X, 4, 64, 2, O, 2, Wq, S, WO, 8, Y, WS, big, None) == L.EINVAL        # dtype
     assert mf(None, 0, 64, 0, None, 0, Wq, S, None, 8, None, None, 0, None) == L.OK  # M = 0
+
+
+def test_group_entry_points_reject():
+    wg, mg = L.lib().int8_quantize_weight_group, L.lib().int8_matmul_group
+    wb = L.lib().int8_matmul_group_workspace_bytes
+    MB = 0x100000
+    W, Wq, S, X, Y, WS = MB, 2 * MB, 3 * MB, 4 * MB, 5 * MB, 8 * MB
+    need = wb(4, 1024, 128)
+    assert need >= 4 * 1024 + 2 * 4 * 4 * 8 and need % 256 == 0
+    assert wb(4, 1024, 100) == 0 and wb(-1, 1024, 128) == 0 and wb(4, 1024, 2048) == 0
+    for G in (0, 64, 100, 192, -128, 8192):
+        assert wg(W, 8192, 8, 0, G, Wq, S, None) == L.EINVAL, G
+        assert mg(X, 4, 8192, 0, G, Wq, S, 8, Y, WS, 1 << 30, None) == L.EINVAL, G
+    assert wg(W, 384, 8, 0, 256, Wq, S, None) == L.EINVAL                       # G does not divide K
+    assert wg(W, 1024, 8, 2, 128, Wq, S, None) == L.EINVAL                      # dtype
+    assert wg(None, 1024, 8, 0, 128, Wq, S, None) == L.EINVAL
+    assert wg(W, 1024, 8, 0, 128, Wq + 8, S, None) == L.EINVAL                  # Wq not 16-byte aligned
+    assert wg(W, 1024, 8, 0, 128, W + 64, S, None) == L.EINVAL                  # Wq overlaps W
+    assert wg(W, 1024, 0, 0, 128, None, None, None) == L.OK                     # N = 0
+    assert mg(X, 4, 1024, 0, 128, Wq, S, 8, Y, WS, need - 1, None) == L.EWORKSPACE
+    assert mg(X, 4, 1024, 0, 128, Wq, S, 8, Y, WS + 16, need + 256, None) == L.EWORKSPACE  # not 256-aligned
+    assert mg(X, 4, 1024, 0, 128, Wq, S, 8, None, WS, need, None) == L.EINVAL   # no Y
+    assert mg(X, 4, 1024, 0, 128, Wq, S, 8, X + 64, WS, need, None) == L.EINVAL  # Y overlaps X
+    assert mg(X, 4, 1024, 0, 128, Wq, S, 8, Y, X, need, None) == L.EINVAL       # workspace overlaps X
+    assert mg(None, 4, 1024, 0, 128, Wq, S, 8, Y, WS, need, None) == L.EINVAL
+    assert mg(X, 4, 1040, 0, 128, Wq, S, 8, Y, WS, 1 << 30, None) == L.EINVAL  # G does not divide K
+    assert mg(X, 4, 1024, 0, 128, Wq, S, 12, Y, WS, 1 << 30, None) == L.EINVAL  # N % 8
+    assert mg(None, 0, 1024, 0, 128, Wq, S, 8, None, None, 0, None) == L.OK     # M = 0
+    assert mg(X, 4, 1024, 0, 128, Wq, S, 0, None, None, 0, None) == L.OK        # N = 0
+
+
+def test_group_two_stage_entry_points_reject():
+    pg, gp = L.lib().int8_matmul_group_prepare, L.lib().int8_matmul_group_products
+    need = L.lib().int8_matmul_group_workspace_bytes(4, 1024, 128)
+    MB = 0x100000
+    X, Wq, S, Y, WS = MB, 2 * MB, 3 * MB, 5 * MB, 8 * MB
+    assert pg(X, 4, 1024, 0, 100, WS, need, None) == L.EINVAL            # group size
+    assert pg(X, 4, 1024, 0, 128, WS, need - 1, None) == L.EWORKSPACE
+    assert pg(None, 4, 1024, 0, 128, WS, need, None) == L.EINVAL
+    assert pg(X, 4, 1024, 0, 128, X + 256, need, None) == L.EINVAL       # workspace overlaps X
+    assert pg(None, 0, 1024, 0, 128, None, 0, None) == L.OK              # M = 0
+    assert gp(4, 1024, 0, 128, Wq, S, 8, Y, WS, need - 1, None) == L.EWORKSPACE
+    assert gp(4, 1024, 0, 128, Wq, S, 8, None, WS, need, None) == L.EINVAL
+    assert gp(4, 1024, 0, 128, None, S, 8, Y, WS, need, None) == L.EINVAL
+    assert gp(4, 1024, 0, 128, Wq, S, 8, WS + 256, WS, need, None) == L.EINVAL  # Y overlaps the workspace
+    assert gp(4, 1024, 0, 128, Wq, S, 0, None, None, 0, None) == L.OK    # N = 0
