@@ -34,8 +34,9 @@ constexpr int kChunks = BK / 16;
 constexpr int kRowsPerLoad = 64 / kChunks;      // 8
 constexpr int kLoadsA = BM / kRowsPerLoad / 4;  // 8 per wave and stage
 constexpr int kLoadsB = BN / kRowsPerLoad / 4;  // 4 per wave and stage
-constexpr int kSlotsA = 3, kSlotsB = 2;
-constexpr int kOperandBytes = kSlotsA * kTileBytesA + kSlotsB * kTileBytesB;  // 128 KB
+// Both operands are loaded two stages ahead (three slots each: 144 KB).
+constexpr int kSlotsA = 3, kSlotsB = 3;
+constexpr int kOperandBytes = kSlotsA * kTileBytesA + kSlotsB * kTileBytesB;
 constexpr int kScaleBytes = 2 * (BM + BN) * 4;                                // two slots of r and s_w
 constexpr int kSubSteps = BK / 32;
 constexpr int kGroupM = 8;
@@ -44,7 +45,7 @@ constexpr int kYPitch = 32 * NJ + 8;             // epilogue staging row, 16-bit
 constexpr int kYStageBytes = 128 * kYPitch * 2;
 static_assert(kOperandBytes + kScaleBytes <= 160 * 1024, "LDS");
 static_assert(4 * kYStageBytes <= kOperandBytes, "epilogue LDS");
-static_assert(kLoadsA == 8, "the barrier's wait leaves the 8 loads of the long-lead operand in flight");
+static_assert(kLoadsA + kLoadsB == 12, "the barrier's wait leaves the 12 loads of stage kt+2 in flight");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -130,15 +131,15 @@ __global__ __launch_bounds__(256, 1) void gemm_group_kernel(GroupParams p) {
 #pragma unroll
         for (int j = 0; j < kLoadsB; ++j) load_lds16(b_tile + kt * BK + b_off[j], Bs + (kLoadsB * wu + j) * 1024);
     };
-    // the factors of group g: r of the tile's 256 rows (each wave 64), s_w of its 128 columns
-    // (waves 0 and 1, 64 each); rows and columns past the matrix read the last one (unused)
+    // the factors of group g: r of the tile's 256 rows (each wave 64) and s_w of its 128
+    // columns (waves 0 and 2 the first 64, 1 and 3 the other 64: the pairs write the same
+    // values, so that every wave issues the same loads); rows and columns past the matrix
+    // read the last one (unused)
     auto issue_scales = [&](int g) LLMINT8_INLINE {
         const int64_t m = m0 + 64 * wu + lane < p.M ? m0 + 64 * wu + lane : p.M - 1;
         load_lds4(p.rg + (int64_t)g * p.M + m, (int8_t*)(rbuf + (g & 1) * BM + 64 * wu));
-        if (wu < 2) {
-            const int64_t n = n0 + 64 * wu + lane < p.N ? n0 + 64 * wu + lane : p.N - 1;
-            load_lds4(p.s_w + n * p.ng + g, (int8_t*)(cbuf + (g & 1) * BN + 64 * wu));
-        }
+        const int64_t n = n0 + 64 * (wu & 1) + lane < p.N ? n0 + 64 * (wu & 1) + lane : p.N - 1;
+        load_lds4(p.s_w + n * p.ng + g, (int8_t*)(cbuf + (g & 1) * BN + 64 * (wu & 1)));
     };
 
     const int rl = lane & 31, h = lane >> 5;
@@ -160,16 +161,16 @@ __global__ __launch_bounds__(256, 1) void gemm_group_kernel(GroupParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            acc[i][j] = v16i{};
-            accf[i][j] = v16f{};
-        }
-    auto mfma_rows = [&](const v4i (&fa)[4], const v4i (&fb)[NJ], int i0, int i1) LLMINT8_INLINE {
+        for (int j = 0; j < NJ; ++j) accf[i][j] = v16f{};
+    // ZERO: the group's first products, which start from 0 instead of the previous group's
+    // partial (so the partials are never cleared)
+    auto mfma_rows = [&](const v4i (&fa)[4], const v4i (&fb)[NJ], int i0, int i1, auto zero_tag) LLMINT8_INLINE {
+        constexpr bool ZERO = decltype(zero_tag)::value;
 #pragma unroll
         for (int i = i0; i < i1; ++i)
 #pragma unroll
             for (int j = 0; j < NJ; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], ZERO ? v16i{} : acc[i][j], 0, 0, 0);
     };
     // fold group g into the fp32 sums (lane: column 32j + lane%32 of the wave's 64, rows
     // 8*(e/4) + 4*(lane/32) + e%4 of each 32-row slice)
@@ -189,59 +190,88 @@ __global__ __launch_bounds__(256, 1) void gemm_group_kernel(GroupParams p) {
                 for (int b = 0; b < 4; ++b) r[4 * a + b] = t4[b];
             }
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
                     accf[i][j][e] = __fadd_rn(accf[i][j][e], __fmul_rn(__fmul_rn((float)acc[i][j][e], r[e]), c[j]));
-                acc[i][j] = v16i{};
-            }
+            // one 32-row slice at a time: hoisting every partial's read would need 128 more
+            // registers than the sums and the next operands leave
+            __builtin_amdgcn_sched_barrier(0);
         }
     };
 
-    // One K stage (as the vector-wise kernel): sub-steps 0..2 with the next sub-step's LDS
-    // reads, sub-step 0 also issuing (at a group's first stage) the group's factors and
-    // B[kt+1], sub-step 1 A[kt+2]; sub-step 3 meets the barrier after 2 MFMAs.  At a group's
-    // last stage the fold follows.
+    // One K stage: sub-steps 0..2 run their 8 MFMAs under the next sub-step's 6 LDS reads
+    // and, in sub-step 0 of a group's first stage, the loads of the group's factors, in
+    // sub-step 1 the global loads of stage kt+2 (both operands, into the slots stage kt-1
+    // freed); sub-step 3 runs 2 MFMAs, waits for stage kt+1 and meets the other waves at the
+    // barrier, then reads stage kt+1's first operands under its other 6.  STEADY: stage kt+2
+    // exists.  FIRST: the group's first stage.
     v4i fa[2][4], fb[2][NJ];
-    auto stage = [&](int kt, auto steady_tag) LLMINT8_INLINE {
+    auto stage = [&](int kt, int g, auto steady_tag, auto first_tag) LLMINT8_INLINE {
         constexpr bool STEADY = decltype(steady_tag)::value;
+        constexpr bool FIRST = decltype(first_tag)::value;
         const bool next = STEADY || kt + 1 < nk;
 #pragma unroll
         for (int u = 0; u < kSubSteps - 1; ++u) {
             const int cur = u & 1, nxt = cur ^ 1;
             __builtin_amdgcn_s_waitcnt(0xC07F);
-            if (u == 0) {
-                if (kt % p.gs == 0) issue_scales(kt / p.gs);
-                if (next) issue_b(kt + 1);
+            if (u == 0 && FIRST) issue_scales(g);
+            if (u == 1 && STEADY) {
+                issue_a(kt + 2);
+                issue_b(kt + 2);
             }
-            if (u == 1 && STEADY) issue_a(kt + 2);
             read_frags(kt, u + 1, fa[nxt], fb[nxt]);
-            mfma_rows(fa[cur], fb[cur], 0, 4);
+            if (u == 0) mfma_rows(fa[cur], fb[cur], 0, 4, std::integral_constant<bool, FIRST>{});
+            else mfma_rows(fa[cur], fb[cur], 0, 4, std::false_type{});
+            if (u == 1 && STEADY) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    if (q < 4) __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
+                    else __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+                    if (q < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 6; ++q) {
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
-        mfma_rows(fa[1], fb[1], 0, 1);
+        mfma_rows(fa[1], fb[1], 0, 1, std::false_type{});
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (STEADY) LLMINT8_GROUP_WAIT_BARRIER(8);  // A[kt+2] may stay in flight
+        if constexpr (STEADY) LLMINT8_GROUP_WAIT_BARRIER(12);  // stage kt+2 may stay in flight
         else LLMINT8_GROUP_WAIT_BARRIER(0);
         if (next) read_frags(kt + 1, 0, fa[0], fb[0]);
-        mfma_rows(fa[1], fb[1], 1, 4);
+        mfma_rows(fa[1], fb[1], 1, 4, std::false_type{});
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
         __builtin_amdgcn_sched_barrier(0);
-        if ((kt + 1) % p.gs == 0) fold(kt / p.gs);
+    };
+    auto run_stage = [&](int kt, int g, auto first_tag) LLMINT8_INLINE {
+        if (kt + 2 < nk) stage(kt, g, std::true_type{}, first_tag);
+        else stage(kt, g, std::false_type{}, first_tag);
     };
 
-    // prologue: A[0], B[0], A[1] in flight; wait for A[0] and B[0]
+    // prologue: stages 0 and 1 in flight; wait for stage 0
     issue_a(0);
     issue_b(0);
     if (nk > 1) {
         issue_a(1);
-        LLMINT8_GROUP_WAIT_BARRIER(8);
+        issue_b(1);
+        LLMINT8_GROUP_WAIT_BARRIER(12);
     } else {
         LLMINT8_GROUP_WAIT_BARRIER(0);
     }
     read_frags(0, 0, fa[0], fb[0]);
-    int kt = 0;
-    for (; kt + 2 < nk; ++kt) stage(kt, std::true_type{});
-    for (; kt < nk; ++kt) stage(kt, std::false_type{});
+    for (int g = 0, kt = 0; g < (int)p.ng; ++g) {
+        run_stage(kt++, g, std::true_type{});
+        for (int s = 1; s < p.gs; ++s) run_stage(kt++, g, std::false_type{});
+        fold(g);
+    }
 
     // ---- epilogue: Y = RN_T(sums), staged per wave in LDS, written as 16-byte row segments
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
