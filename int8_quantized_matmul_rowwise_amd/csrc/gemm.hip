@@ -12,8 +12,10 @@
 //   block tile 256 x 256, 4 waves in 2 x 2, each wave 128 x 128 = 4 x 4 MFMA tiles of
 //   32 x 32 -> 256 int32 accumulators per lane (AGPRs).  (On gfx950 the 32x32x32 i8
 //   MFMA sustains the full int8 rate; the 16x16x64 form issues at about half of it.)
-//   Operands go HBM/L2 -> LDS with global_load_lds (16 B per lane, no register
-//   staging), one 128-byte line per row per K stage (full-line requests).  The LDS
+//   Operands go HBM/L2 -> LDS with buffer loads straight into LDS (16 B per lane, no
+//   register staging; a buffer resource per operand over the tile's rows, so a load sends
+//   32-bit offsets and the stage's K position rides in the scalar offset), one 128-byte
+//   line per row per K stage (full-line requests).  The LDS
 //   holds 3 A slots and 2 B slots of 32 KB: during stage k the loads of B[k+1] and
 //   A[k+2] are issued.  (The 32 tiles running together on one XCD span 8 row panels and 4
 //   column panels, so the activation lines miss that XCD's L2 twice as often as the
@@ -67,8 +69,15 @@ static_assert(BM == 256 && BN == 256, "the factor tables take one row and one co
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ void load_lds16(const void* g, int8_t* lds_base) {
-    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds_base, 16, 0, 0);
+// A raw buffer resource over `bytes` bytes from `base` (dword data format, as gfx9 buffer
+// loads expect): loads at offsets past `bytes` return zero and touch no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+// 16 bytes per lane from the resource at voffset + soffset into LDS at lds_base + 16 * lane.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t voffset, int soffset, int8_t* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds_base, 16, (int)voffset, soffset, 0, 0);
 }
 
 // Chunk swizzle: the 16-byte chunk c of LDS row r is stored at chunk c ^ swz(r), so that
@@ -134,7 +143,6 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
     // logical chunk c_ld(j) = (lane%8) ^ swz(r).
     const int wu = __builtin_amdgcn_readfirstlane(w);
     uint32_t a_off[kLoadsA], b_off[kLoadsB];
-    int cb_ld[kLoadsB];
 #pragma unroll
     for (int j = 0; j < kLoadsA; ++j) {
         const int r = kRowsPerLoad * (kLoadsA * wu + j) + lane / kChunks;
@@ -145,13 +153,20 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
 #pragma unroll
     for (int j = 0; j < kLoadsB; ++j) {
         const int r = kRowsPerLoad * (kLoadsB * wu + j) + lane / kChunks;
-        cb_ld[j] = (lane % kChunks) ^ swz(r);
+        const int c = (lane % kChunks) ^ swz(r);
         const int64_t n = n0 + r < p.N ? n0 + r : p.N - 1;
-        b_off[j] = (uint32_t)((n - n0) * p.K + cb_ld[j] * 16);
+        b_off[j] = (uint32_t)((n - n0) * p.K + c * 16);
     }
     const int8_t* a_tile = p.Xq + m0 * p.xq_pitch;
     const int8_t* b_tile = p.Wq + n0 * p.K;
     const int nk = (int)ceil_div(p.K, BK);
+    // The resources span the tile's rows (at most 256 of them: offsets fit 32 bits for any
+    // K the library accepts).  In a partial last stage the chunks past K of a B row read the
+    // next row's first bytes, or nothing (zero) past the last row: their A side is the zero
+    // padding of Xq, so they add exact zeros.
+    const int64_t rows_a = p.M - m0 < BM ? p.M - m0 : BM, rows_b = p.N - n0 < BN ? p.N - n0 : BN;
+    const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(a_tile, rows_a * p.xq_pitch);
+    const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(b_tile, rows_b * p.K);
 
     auto slot_a = [&](int kt) { return smem + (kt % kSlotsA) * kTileBytes; };
     auto slot_b = [&](int kt) { return smem + kSlotsA * kTileBytes + (kt % kSlotsB) * kSlotBytesB; };
@@ -159,18 +174,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
         int8_t* As = slot_a(kt);
         const int kb = kt * BK;
 #pragma unroll
-        for (int j = 0; j < kLoadsA; ++j) load_lds16(a_tile + kb + a_off[j], As + (kLoadsA * wu + j) * 1024);
+        for (int j = 0; j < kLoadsA; ++j) load_lds16(rsa, a_off[j], kb, As + (kLoadsA * wu + j) * 1024);
     };
-    // Chunks past K (a partial last stage) read the row start instead: their A side is zero.
-    // Written branch-free so that a stage of the main loop is one scheduling region.
     auto issue_b = [&](int kt) {
         int8_t* Bs = slot_b(kt);
         const int kb = kt * BK;
 #pragma unroll
-        for (int j = 0; j < kLoadsB; ++j) {
-            const int kk = kb + cb_ld[j] * 16;
-            load_lds16(b_tile + b_off[j] - cb_ld[j] * 16 + (kk < p.K ? kk : 0), Bs + (kLoadsB * wu + j) * 1024);
-        }
+        for (int j = 0; j < kLoadsB; ++j) load_lds16(rsb, b_off[j], kb, Bs + (kLoadsB * wu + j) * 1024);
     };
 
     // ---- MFMA operand reads (32x32x32: lane holds row lane%32, 16 k at 16*(lane/32)):

@@ -8,14 +8,15 @@
 //   acc = 0; for g ascending: acc = RN32(acc + RN32(RN32((float)C_g * r_ig) * c_ng)),
 //   r_ig = RN32(s_x/127), c_ng = RN32(s_w/127);  Y = RN_T(acc).
 //
-// Product kernel: the tiled int8 MFMA kernel's scheme (K stages of 128 bytes through
-// global_load_lds, 3 A / 2 B slots, counted waits, XOR chunk swizzle, XCD-contiguous tile
-// order) with a 256 x 128 tile, so that each lane holds 128 int32 accumulators (AGPRs) and
-// 128 fp32 sums.  At the end of each group every wave folds its int32 partials into the
-// fp32 sums and clears them.  The group's factors come through LDS: r (precomputed by the X
-// pass, group-major) and s_w for the tile's rows and columns, loaded straight into LDS at
-// the group's first stage, before that stage's operand loads, so the stage's counted wait
-// and barrier cover them too; two slots alternate between groups.
+// Product kernel: the tiled int8 MFMA kernel's scheme (K stages of 128 bytes loaded
+// straight into LDS, counted waits, XOR chunk swizzle, XCD-contiguous tile order) with a
+// 256 x 128 tile, so that each lane holds 128 int32 accumulators (AGPRs) and 128 fp32
+// sums, and both operands loaded two stages ahead (3 + 3 slots).  A group's first products
+// start from zero; after its last stage every wave folds its int32 partials into the fp32
+// sums.  The group's factors come through LDS: r (precomputed by the X pass, group-major)
+// and s_w for the tile's rows and columns, loaded straight into LDS at the group's first
+// stage, before the stage's operand loads, so the counted wait and barrier that cover
+// stage kt+1 cover them too; two slots alternate between groups.
 #include <type_traits>
 
 #include "common.hpp"
@@ -53,8 +54,13 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // accumulator arrays it captures by reference into private (scratch) memory.
 #define LLMINT8_INLINE __attribute__((always_inline))
 
-__device__ __forceinline__ void load_lds16(const void* g, int8_t* lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 16, 0, 0);
+// Operand loads: a raw buffer resource over the tile's rows (dword data format), 32-bit
+// offsets, the stage's K position in the scalar offset; 16 bytes per lane into LDS.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t voffset, int soffset, int8_t* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 16, (int)voffset, soffset, 0, 0);
 }
 __device__ __forceinline__ void load_lds4(const void* g, int8_t* lds) {
     __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 4, 0, 0);
@@ -118,18 +124,21 @@ __global__ __launch_bounds__(256, 1) void gemm_group_kernel(GroupParams p) {
     const int8_t* a_tile = p.Xq + m0 * p.K;
     const int8_t* b_tile = p.Wq + n0 * p.K;
     const int nk = (int)(p.K / BK);  // K is a multiple of G >= 128
+    const int64_t rows_a = p.M - m0 < BM ? p.M - m0 : BM, rows_b = p.N - n0 < BN ? p.N - n0 : BN;
+    const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(a_tile, rows_a * p.K);
+    const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(b_tile, rows_b * p.K);
 
     auto slot_a = [&](int kt) LLMINT8_INLINE { return smem + (kt % kSlotsA) * kTileBytesA; };
     auto slot_b = [&](int kt) LLMINT8_INLINE { return smem + kSlotsA * kTileBytesA + (kt % kSlotsB) * kTileBytesB; };
     auto issue_a = [&](int kt) LLMINT8_INLINE {
         int8_t* As = slot_a(kt);
 #pragma unroll
-        for (int j = 0; j < kLoadsA; ++j) load_lds16(a_tile + kt * BK + a_off[j], As + (kLoadsA * wu + j) * 1024);
+        for (int j = 0; j < kLoadsA; ++j) load_lds16(rsa, a_off[j], kt * BK, As + (kLoadsA * wu + j) * 1024);
     };
     auto issue_b = [&](int kt) LLMINT8_INLINE {
         int8_t* Bs = slot_b(kt);
 #pragma unroll
-        for (int j = 0; j < kLoadsB; ++j) load_lds16(b_tile + kt * BK + b_off[j], Bs + (kLoadsB * wu + j) * 1024);
+        for (int j = 0; j < kLoadsB; ++j) load_lds16(rsb, b_off[j], kt * BK, Bs + (kLoadsB * wu + j) * 1024);
     };
     // the factors of group g: r of the tile's 256 rows (each wave 64) and s_w of its 128
     // columns (waves 0 and 2 the first 64, 1 and 3 the other 64: the pairs write the same
