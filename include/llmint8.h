@@ -238,10 +238,11 @@ int int8_quantize_weight_group(const void* W, int64_t K, int64_t N, int dtype, i
 
 /*
  * The group-wise product.  Workspace: int8_matmul_group_workspace_bytes(M, K, group)
- * bytes, 256-byte aligned (0 if the arguments are invalid).  Afterwards it holds the X
- * pass's products: Xq (M x K int8, row-major) at offset 0, s_x (M x ng fp32, row-major)
- * at offset round_up(M*K, 256), and the dequantization factors RN32(s_x/127) transposed
- * (ng x M) after that.  Y: M x N of X's dtype, 16-byte aligned.  K = 0 gives Y = 0.
+ * bytes, 256-byte aligned (0 if the arguments are invalid).  After a call with M, N and
+ * K nonzero it holds the X pass's products: Xq (M x K int8, row-major) at offset 0, s_x
+ * (M x ng fp32, row-major) at offset round_up(M*K, 256), and the dequantization factors
+ * RN32(s_x/127) transposed (ng x M) after that.  Y: M x N of X's dtype, 16-byte aligned.
+ * M = 0 or N = 0 is a no-op; K = 0 gives Y = 0 (the workspace is then not needed).
  * Inputs, Y and the workspace must not overlap (LLMINT8_EINVAL).
  */
 size_t int8_matmul_group_workspace_bytes(int64_t M, int64_t K, int64_t group);
