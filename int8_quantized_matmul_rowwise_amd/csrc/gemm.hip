@@ -8,21 +8,25 @@
 // int8 product with one normalization constant per inner-product vector, and the
 // outlier feature dimensions through a 16-bit product, summed into the same output.
 //
-// Tiling (gfx950: 64-wide waves, 160 KB LDS, 512 registers per lane at one wave/SIMD):
-//   block tile 256 x 256, 4 waves in 2 x 2, each wave 128 x 128 = 4 x 4 MFMA tiles of
-//   32 x 32 -> 256 int32 accumulators per lane (AGPRs).  (On gfx950 the 32x32x32 i8
-//   MFMA sustains the full int8 rate; the 16x16x64 form issues at about half of it.)
+// Tiling (gfx950: 64-wide waves, 160 KB LDS, 512 registers per lane per SIMD):
+//   block tile 256 x 256, 8 waves in 2 x 4 -- two per SIMD, 256 registers each --, each
+//   wave 128 x 64 = 4 x 2 MFMA tiles of 32 x 32 -> 128 int32 accumulators per lane.  With
+//   two waves on a SIMD, one wave's MFMAs keep the matrix unit busy while the other waits
+//   at a barrier or for its operands (one wave of 128 x 128 per SIMD left it idle there);
+//   the LDS, which then serves 0.75 KB per MFMA instead of 0.5, has the bandwidth for it.
+//   (On gfx950 the 32x32x32 i8 MFMA sustains the full int8 rate; the 16x16x64 form issues
+//   at about half of it.)
 //   Operands go HBM/L2 -> LDS with buffer loads straight into LDS (16 B per lane, no
 //   register staging; a buffer resource per operand over the tile's rows, so a load sends
 //   32-bit offsets and the stage's K position rides in the scalar offset), one 128-byte
 //   line per row per K stage (full-line requests).  The LDS
-//   holds 3 A slots and 2 B slots of 32 KB: during stage k the loads of B[k+1] and
-//   A[k+2] are issued.  (The 32 tiles running together on one XCD span 8 row panels and 4
-//   column panels, so the activation lines miss that XCD's L2 twice as often as the
-//   weight lines: they get the longer lead.)  Waits are counted
+//   holds 2 A slots and 3 B slots of 32 KB: during stage k the loads of A[k+1] and
+//   B[k+2] are issued (the weight panels get the longer lead: 1.4 % faster than the
+//   other way round on the 4096 x 12288 x 36864 projection, 1.3 % slower on the
+//   8192 x 28672 x 8192 one).  Waits are counted
 //   (vmcnt) and the workgroup barrier is a bare s_barrier, so a barrier never drains the
 //   loads still in flight.  Each stage is four 32-deep MFMA sub-steps; the operands of
-//   the next sub-step are read from LDS into a second register set while the 16 MFMAs
+//   the next sub-step are read from LDS into a second register set while the 8 MFMAs
 //   of the current one run.  The instruction order inside a sub-step (global loads and
 //   LDS reads front-loaded between the MFMAs) is pinned with scheduling-group hints, and
 //   each sub-step begins with an LDS wait that costs nothing.  The
@@ -41,30 +45,30 @@ namespace llmint8 {
 
 namespace {
 
-constexpr int NJ = 4;                                    // 32-column MFMA tiles per wave along N
-constexpr int BM = 256, BN = 64 * NJ;
+constexpr int NJ = 2;                                    // 32-column MFMA tiles per wave along N
+constexpr int kWaves = 8;                                // 2 (M) x 4 (N), two per SIMD
+constexpr int BM = 256, BN = 4 * 32 * NJ;
 constexpr int BK = 128;                                  // bytes of K per stage: one line per row
 constexpr int kTileBytes = BM * BK;                      // one operand's stage: 32 KB
 constexpr int kChunks = BK / 16;                         // 16-byte chunks per row segment
 constexpr int kRowsPerLoad = 64 / kChunks;               // rows covered by one 64-lane load
-constexpr int kLoadsA = BM / kRowsPerLoad / 4;           // per wave, per stage (8)
-constexpr int kLoadsB = BN / kRowsPerLoad / 4;           // per wave, per stage (8)
-constexpr bool kLeadA = true;                            // which operand is loaded two stages ahead
+constexpr int kLoadsA = BM / kRowsPerLoad / kWaves;      // per wave, per stage (4)
+constexpr int kLoadsB = BN / kRowsPerLoad / kWaves;      // per wave, per stage (4)
+constexpr bool kLeadA = false;                           // which operand is loaded two stages ahead
 constexpr int kSlotsA = kLeadA ? 3 : 2;                  // 5 x 32 KB: the whole 160 KB of LDS
 constexpr int kSlotsB = kLeadA ? 2 : 3;
 constexpr int kSlotBytesB = BN * BK;
 constexpr int kSubSteps = BK / 32;                       // 32-deep MFMA steps per stage
 constexpr int kGroupM = 8;
 // epilogue staging (reuses the operand slots): the tile's row and column factors, then per
-// wave its 128 x 128 outputs, rows padded to 272 bytes (16-byte aligned, half-waves on
-// different banks)
+// wave its 128 x 64 outputs, rows padded to 144 bytes (16-byte aligned)
 constexpr int kScaleBytes = 2 * 256 * 4;
-constexpr int kYPitch = 136;  // 16-bit elements
+constexpr int kYPitch = 72;  // 16-bit elements
 constexpr int kYStageBytes = 128 * kYPitch * 2;                               // row tiles per group of the tile order
 constexpr int kXcds = 8;
 static_assert(kSlotsA * kTileBytes + kSlotsB * kSlotBytesB <= 160 * 1024, "LDS");
-static_assert(kLoadsA == 8 && kLoadsB == 8, "the waits below count 8 loads per operand and wave");
-static_assert(kScaleBytes + 4 * kYStageBytes <= kSlotsA * kTileBytes + kSlotsB * kSlotBytesB, "epilogue LDS");
+static_assert(kLoadsA == 4 && kLoadsB == 4, "the waits below count 4 loads per operand and wave");
+static_assert(kScaleBytes + kWaves * kYStageBytes <= kSlotsA * kTileBytes + kSlotsB * kSlotBytesB, "epilogue LDS");
 static_assert(BM == 256 && BN == 256, "the factor tables take one row and one column per thread");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -120,10 +124,10 @@ __device__ __forceinline__ v16f mfma16(const u32x4& a, const u32x4& b, const v16
 }
 
 template <int DT, bool ACC_OUT>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
+__global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
     __shared__ __attribute__((aligned(1024))) int8_t smem[kSlotsA * kTileBytes + kSlotsB * kSlotBytesB];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w >> 2, wn = w & 3;
 
     // ---- tile of this workgroup (XCD-contiguous runs, grouped order)
     const int T = p.tiles_m * p.tiles_n;
@@ -138,9 +142,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
     const int tn = (t % in_group) / gm;
     const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
 
-    // ---- loader: wave w fills LDS slots [64*(8w+j), +64) of each operand, j = 0..7:
-    // row r = 8*(8w + j) + lane/8 (one 128-byte line per row), physical chunk lane%8,
-    // logical chunk c_ld(j) = (lane%8) ^ swz(r).
+    // ---- loader: wave w fills LDS slots [1024*(4w+j), +1024) of each operand, j = 0..3:
+    // row r = 8*(4w + j) + lane/8 (one 128-byte line per row), physical chunk lane%8,
+    // logical chunk (lane%8) ^ swz(r).
     const int wu = __builtin_amdgcn_readfirstlane(w);
     uint32_t a_off[kLoadsA], b_off[kLoadsB];
 #pragma unroll
@@ -214,12 +218,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
                 acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
     };
 
-    // One K stage.  Sub-steps 0..2 run their 16 MFMAs while the LDS reads of the next
+    // One K stage.  Sub-steps 0..2 run their 8 MFMAs while the 6 LDS reads of the next
     // sub-step (and, in 0 and 1, the global loads of stage kt+1 of the short-lead operand
     // and stage kt+2 of the long-lead one, into the slots stage kt-1 freed) are
     // interleaved, front-loaded so they have most of the sub-step to land.  Sub-step 3 runs
-    // 4 MFMAs, waits for stage kt+1 and meets the other waves at the barrier, then reads
-    // stage kt+1's first operands under its other 12.  Each sub-step is fenced
+    // 2 MFMAs, waits for stage kt+1 and meets the other waves at the barrier, then reads
+    // stage kt+1's first operands under its other 6.  Each sub-step is fenced
     // (sched_barrier) so that the interleave stays inside it.
     // STEADY: stage kt+2 exists (every stage but the last two).
     v4i fa[2][4], fb[2][NJ];  // operand sets of the current / next sub-step
@@ -245,29 +249,34 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
             mfma_rows(fa[cur], fb[cur], 0, 4);
             if (loads) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
+                for (int q = 0; q < 4; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                }
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 }
             } else {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
+                for (int q = 0; q < 6; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 }
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
         mfma_rows(fa[1], fb[1], 0, 1);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (STEADY) LLMINT8_WAIT_BARRIER(8);  // the stage kt+2 loads may stay in flight
+        if constexpr (STEADY) LLMINT8_WAIT_BARRIER(4);  // the stage kt+2 loads may stay in flight
         else LLMINT8_WAIT_BARRIER(0);
         if (next) read_frags(kt + 1, 0, fa[0], fb[0]);
         mfma_rows(fa[1], fb[1], 1, 4);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 12, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -278,7 +287,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
         if (nk > 1) {
             if (kLeadA) issue_a(1);
             else issue_b(1);
-            LLMINT8_WAIT_BARRIER(8);
+            LLMINT8_WAIT_BARRIER(4);
         } else {
             LLMINT8_WAIT_BARRIER(0);
         }
@@ -326,14 +335,16 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
     } else {
         // The operand slots are free once every wave is past its last reads and no load is in
         // flight: the LDS then holds the tile's dequantization factors and, per wave, its
-        // 128 x 128 outputs, which leave as 16-byte row segments (full lines).
+        // 128 x 64 outputs, which leave as 16-byte row segments (full lines).
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         float* rsc = (float*)smem;  // r_i = s_x[i]/127 of the tile's rows
         float* csc = rsc + BM;      // c_n = s_w[n]/127 of its columns
-        {
-            const int64_t m = m0 + tid, n = n0 + tid;
+        if (tid < BM) {
+            const int64_t m = m0 + tid;
             rsc[tid] = m < p.M ? p.s_x[m] / 127.0f : 0.0f;
-            csc[tid] = n < p.N ? p.s_w[n] / 127.0f : 0.0f;
+        } else {
+            const int64_t n = n0 + tid - BM;
+            csc[tid - BM] = n < p.N ? p.s_w[n] / 127.0f : 0.0f;
         }
         __syncthreads();
         uint16_t* ys = (uint16_t*)(smem + kScaleBytes + w * kYStageBytes);
@@ -364,8 +375,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
         }
         // read back the wave's own rows (one wave's LDS accesses complete in order)
 #pragma unroll 4
-        for (int it = 0; it < 32; ++it) {
-            const int row = it * 4 + (lane >> 4), ch = lane & 15;
+        for (int it = 0; it < 16; ++it) {
+            const int row = it * 8 + (lane >> 3), ch = lane & 7;
             const u32x4 v = *(const u32x4*)(ys + row * kYPitch + ch * 8);
             const int64_t m = wm0 + row, n = wn0 + ch * 8;
             if (m < p.M && n < p.N) *(u32x4*)(p.Y + m * p.N + n) = v;
@@ -376,7 +387,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Params p) {
 template <int DT, bool ACC_OUT>
 hipError_t launch_one(const Params& p, hipStream_t stream) {
     const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
-    gemm_kernel<DT, ACC_OUT><<<grid, 256, 0, stream>>>(p);
+    gemm_kernel<DT, ACC_OUT><<<grid, 64 * kWaves, 0, stream>>>(p);
     return hipGetLastError();
 }
 
