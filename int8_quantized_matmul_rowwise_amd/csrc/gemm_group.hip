@@ -10,10 +10,11 @@
 //
 // Product kernel: the tiled int8 MFMA kernel's scheme (K stages of 128 bytes loaded
 // straight into LDS, counted waits, XOR chunk swizzle, XCD-contiguous tile order) with a
-// 256 x 128 tile, so that each lane holds 128 int32 accumulators (AGPRs) and 128 fp32
-// sums, and both operands loaded two stages ahead (3 + 3 slots).  A group's first products
-// start from zero; after its last stage every wave folds its int32 partials into the fp32
-// sums.  The group's factors come through LDS: r (precomputed by the X pass, group-major)
+// 256 x 128 tile over 8 waves (4 x 2, two per SIMD), each 64 x 64: 64 int32 partials and
+// 64 fp32 sums per lane in its 256 registers.  Both operands are loaded two stages ahead
+// (3 + 3 slots).  A group's first products start from zero; after its last stage every
+// wave folds its int32 partials into the fp32 sums -- while it does, the other wave on its
+// SIMD keeps the matrix unit busy.  The group's factors come through LDS: r (precomputed by the X pass, group-major)
 // and s_w for the tile's rows and columns, loaded straight into LDS at the group's first
 // stage, before the stage's operand loads, so the counted wait and barrier that cover
 // stage kt+1 cover them too; two slots alternate between groups.
@@ -27,14 +28,16 @@ namespace llmint8 {
 namespace {
 
 constexpr int NJ = 2;                           // 32-column MFMA tiles per wave along N
-constexpr int BM = 256, BN = 64 * NJ;           // 256 x 128
+constexpr int MI = 2;                           // 32-row MFMA tiles per wave along M
+constexpr int kWaves = 8;                       // 4 (M) x 2 (N), two per SIMD, 64 x 64 each
+constexpr int BM = 4 * 32 * MI, BN = 2 * 32 * NJ;  // 256 x 128
 constexpr int BK = 128;
 constexpr int kTileBytesA = BM * BK;            // 32 KB
 constexpr int kTileBytesB = BN * BK;            // 16 KB
 constexpr int kChunks = BK / 16;
 constexpr int kRowsPerLoad = 64 / kChunks;      // 8
-constexpr int kLoadsA = BM / kRowsPerLoad / 4;  // 8 per wave and stage
-constexpr int kLoadsB = BN / kRowsPerLoad / 4;  // 4 per wave and stage
+constexpr int kLoadsA = BM / kRowsPerLoad / kWaves;  // 4 per wave and stage
+constexpr int kLoadsB = BN / kRowsPerLoad / kWaves;  // 2 per wave and stage
 // Both operands are loaded two stages ahead (three slots each: 144 KB).
 constexpr int kSlotsA = 3, kSlotsB = 3;
 constexpr int kOperandBytes = kSlotsA * kTileBytesA + kSlotsB * kTileBytesB;
@@ -43,10 +46,10 @@ constexpr int kSubSteps = BK / 32;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 constexpr int kYPitch = 32 * NJ + 8;             // epilogue staging row, 16-bit elements
-constexpr int kYStageBytes = 128 * kYPitch * 2;
+constexpr int kYStageBytes = 32 * MI * kYPitch * 2;
 static_assert(kOperandBytes + kScaleBytes <= 160 * 1024, "LDS");
-static_assert(4 * kYStageBytes <= kOperandBytes, "epilogue LDS");
-static_assert(kLoadsA + kLoadsB == 12, "the barrier's wait leaves the 12 loads of stage kt+2 in flight");
+static_assert(kWaves * kYStageBytes <= kOperandBytes, "epilogue LDS");
+static_assert(kLoadsA + kLoadsB == 6, "the barrier's wait leaves the 6 loads of stage kt+2 in flight");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -61,9 +64,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 }
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, uint32_t voffset, int soffset, int8_t* lds) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)lds, 16, (int)voffset, soffset, 0, 0);
-}
-__device__ __forceinline__ void load_lds4(const void* g, int8_t* lds) {
-    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t)lds, 4, 0, 0);
 }
 
 __host__ __device__ constexpr int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
@@ -86,7 +86,7 @@ struct GroupParams {
 };
 
 template <int DT>
-__global__ __launch_bounds__(256, 1) void gemm_group_kernel(GroupParams p) {
+__global__ __launch_bounds__(64 * kWaves) void gemm_group_kernel(GroupParams p) {
     __shared__ __attribute__((aligned(1024))) int8_t smem[kOperandBytes + kScaleBytes];
     float* rbuf = (float*)(smem + kOperandBytes);  // [2][BM]
     float* cbuf = rbuf + 2 * BM;                   // [2][BN]: s_w of the tile's columns
@@ -140,40 +140,44 @@ __global__ __launch_bounds__(256, 1) void gemm_group_kernel(GroupParams p) {
 #pragma unroll
         for (int j = 0; j < kLoadsB; ++j) load_lds16(rsb, b_off[j], kt * BK, Bs + (kLoadsB * wu + j) * 1024);
     };
-    // the factors of group g: r of the tile's 256 rows (each wave 64) and s_w of its 128
-    // columns (waves 0 and 2 the first 64, 1 and 3 the other 64: the pairs write the same
-    // values, so that every wave issues the same loads); rows and columns past the matrix
-    // read the last one (unused)
+    // the factors of group g, one 64-entry load per wave: waves 0..3 the r of the tile's
+    // 256 rows, waves 4 and 5 the s_w of its 128 columns, waves 6 and 7 the same columns
+    // again (same values to the same place, so that every wave issues the same loads); rows
+    // and columns past the matrix read the last one (unused)
+    const int cw = wu & 1;
+    const uint32_t r_off = (uint32_t)(((m0 + 64 * (wu & 3) + lane < p.M ? m0 + 64 * (wu & 3) + lane : p.M - 1) - m0) * 4);
+    const uint32_t c_off = (uint32_t)(((n0 + 64 * cw + lane < p.N ? n0 + 64 * cw + lane : p.N - 1) - n0) * p.ng * 4);
     auto issue_scales = [&](int g) LLMINT8_INLINE {
-        const int64_t m = m0 + 64 * wu + lane < p.M ? m0 + 64 * wu + lane : p.M - 1;
-        load_lds4(p.rg + (int64_t)g * p.M + m, (int8_t*)(rbuf + (g & 1) * BM + 64 * wu));
-        const int64_t n = n0 + 64 * (wu & 1) + lane < p.N ? n0 + 64 * (wu & 1) + lane : p.N - 1;
-        load_lds4(p.s_w + n * p.ng + g, (int8_t*)(cbuf + (g & 1) * BN + 64 * (wu & 1)));
+        // buffer resources over this group's factors of the tile (32-bit offsets)
+        const __amdgpu_buffer_rsrc_t rs = wu < 4 ? buffer_rsrc(p.rg + (int64_t)g * p.M + m0, rows_a * 4)
+                                                 : buffer_rsrc(p.s_w + n0 * p.ng + g, rows_b * p.ng * 4);
+        float* dst = wu < 4 ? rbuf + (g & 1) * BM + 64 * wu : cbuf + (g & 1) * BN + 64 * cw;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 4, (int)(wu < 4 ? r_off : c_off), 0, 0, 0);
     };
 
     const int rl = lane & 31, h = lane >> 5;
     int rd[kSubSteps];
 #pragma unroll
     for (int u = 0; u < kSubSteps; ++u) rd[u] = rl * BK + (((2 * u + h) ^ swz(rl)) << 4);
-    auto read_frags = [&](int kt, int u, v4i (&fa)[4], v4i (&fb)[NJ]) LLMINT8_INLINE {
-        const int8_t* As = slot_a(kt) + wm * 128 * BK + rd[u];
+    auto read_frags = [&](int kt, int u, v4i (&fa)[MI], v4i (&fb)[NJ]) LLMINT8_INLINE {
+        const int8_t* As = slot_a(kt) + wm * (32 * MI) * BK + rd[u];
         const int8_t* Bs = slot_b(kt) + wn * (32 * NJ) * BK + rd[u];
         fa[0] = *(const v4i*)As;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) fb[j] = *(const v4i*)(Bs + j * 32 * BK);
 #pragma unroll
-        for (int i = 1; i < 4; ++i) fa[i] = *(const v4i*)(As + i * 32 * BK);
+        for (int i = 1; i < MI; ++i) fa[i] = *(const v4i*)(As + i * 32 * BK);
     };
 
-    v16i acc[4][NJ];
-    v16f accf[4][NJ];
+    v16i acc[MI][NJ];
+    v16f accf[MI][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) accf[i][j] = v16f{};
     // ZERO: the group's first products, which start from 0 instead of the previous group's
     // partial (so the partials are never cleared)
-    auto mfma_rows = [&](const v4i (&fa)[4], const v4i (&fb)[NJ], int i0, int i1, auto zero_tag) LLMINT8_INLINE {
+    auto mfma_rows = [&](const v4i (&fa)[MI], const v4i (&fb)[NJ], int i0, int i1, auto zero_tag) LLMINT8_INLINE {
         constexpr bool ZERO = decltype(zero_tag)::value;
 #pragma unroll
         for (int i = i0; i < i1; ++i)
@@ -184,13 +188,13 @@ __global__ __launch_bounds__(256, 1) void gemm_group_kernel(GroupParams p) {
     // fold group g into the fp32 sums (lane: column 32j + lane%32 of the wave's 64, rows
     // 8*(e/4) + 4*(lane/32) + e%4 of each 32-row slice)
     auto fold = [&](int g) LLMINT8_INLINE {
-        const float* rb = rbuf + (g & 1) * BM + wm * 128;
+        const float* rb = rbuf + (g & 1) * BM + wm * (32 * MI);
         const float* cb = cbuf + (g & 1) * BN + wn * 64;
         float c[NJ];
 #pragma unroll
         for (int j = 0; j < NJ; ++j) c[j] = cb[32 * j + rl] / 127.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < MI; ++i) {
             float r[16];
 #pragma unroll
             for (int a = 0; a < 4; ++a) {
@@ -215,7 +219,7 @@ __global__ __launch_bounds__(256, 1) void gemm_group_kernel(GroupParams p) {
     // freed); sub-step 3 runs 2 MFMAs, waits for stage kt+1 and meets the other waves at the
     // barrier, then reads stage kt+1's first operands under its other 6.  STEADY: stage kt+2
     // exists.  FIRST: the group's first stage.
-    v4i fa[2][4], fb[2][NJ];
+    v4i fa[2][MI], fb[2][NJ];
     auto stage = [&](int kt, int g, auto steady_tag, auto first_tag) LLMINT8_INLINE {
         constexpr bool STEADY = decltype(steady_tag)::value;
         constexpr bool FIRST = decltype(first_tag)::value;
@@ -230,34 +234,33 @@ __global__ __launch_bounds__(256, 1) void gemm_group_kernel(GroupParams p) {
                 issue_b(kt + 2);
             }
             read_frags(kt, u + 1, fa[nxt], fb[nxt]);
-            if (u == 0) mfma_rows(fa[cur], fb[cur], 0, 4, std::integral_constant<bool, FIRST>{});
-            else mfma_rows(fa[cur], fb[cur], 0, 4, std::false_type{});
+            if (u == 0) mfma_rows(fa[cur], fb[cur], 0, MI, std::integral_constant<bool, FIRST>{});
+            else mfma_rows(fa[cur], fb[cur], 0, MI, std::false_type{});
             if (u == 1 && STEADY) {
 #pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    if (q < 4) __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
+                for (int q = 0; q < 4; ++q) {
+                    if (q < 2) __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
                     else __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-                    if (q < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 }
             } else {
 #pragma unroll
-                for (int q = 0; q < 6; ++q) {
+                for (int q = 0; q < 4; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                 }
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         mfma_rows(fa[1], fb[1], 0, 1, std::false_type{});
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (STEADY) LLMINT8_GROUP_WAIT_BARRIER(12);  // stage kt+2 may stay in flight
+        if constexpr (STEADY) LLMINT8_GROUP_WAIT_BARRIER(6);  // stage kt+2 may stay in flight
         else LLMINT8_GROUP_WAIT_BARRIER(0);
         if (next) read_frags(kt + 1, 0, fa[0], fb[0]);
-        mfma_rows(fa[1], fb[1], 1, 4, std::false_type{});
-        __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
+        mfma_rows(fa[1], fb[1], 1, MI, std::false_type{});
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     auto run_stage = [&](int kt, int g, auto first_tag) LLMINT8_INLINE {
@@ -271,7 +274,7 @@ __global__ __launch_bounds__(256, 1) void gemm_group_kernel(GroupParams p) {
     if (nk > 1) {
         issue_a(1);
         issue_b(1);
-        LLMINT8_GROUP_WAIT_BARRIER(12);
+        LLMINT8_GROUP_WAIT_BARRIER(6);
     } else {
         LLMINT8_GROUP_WAIT_BARRIER(0);
     }
@@ -286,17 +289,17 @@ __global__ __launch_bounds__(256, 1) void gemm_group_kernel(GroupParams p) {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     uint16_t* ys = (uint16_t*)(smem + w * kYStageBytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e)
                 ys[(32 * i + 8 * (e >> 2) + 4 * h + (e & 3)) * kYPitch + 32 * j + rl] = from_f32<DT>(accf[i][j][e]);
-    const int64_t wm0 = m0 + wm * 128, wn0 = n0 + wn * (32 * NJ);
+    const int64_t wm0 = m0 + wm * (32 * MI), wn0 = n0 + wn * (32 * NJ);
     constexpr int kLanesPerRow = 32 * NJ / 8;        // 16-byte segments per staged row
     constexpr int kRowsPerIter = 64 / kLanesPerRow;
 #pragma unroll 4
-    for (int it = 0; it < 128 / kRowsPerIter; ++it) {
+    for (int it = 0; it < 32 * MI / kRowsPerIter; ++it) {
         const int row = it * kRowsPerIter + lane / kLanesPerRow, ch = lane % kLanesPerRow;
         const u32x4 v = *(const u32x4*)(ys + row * kYPitch + ch * 8);
         const int64_t m = wm0 + row, n = wn0 + ch * 8;
@@ -453,8 +456,8 @@ hipError_t launch_gemm_group(int dt, const int8_t* Xq, const float* rg, const in
     p.tiles_m = (int)ceil_div(M, BM);
     p.tiles_n = (int)ceil_div(N, BN);
     const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
-    if (dt == F16) gemm_group_kernel<F16><<<grid, 256, 0, stream>>>(p);
-    else gemm_group_kernel<BF16><<<grid, 256, 0, stream>>>(p);
+    if (dt == F16) gemm_group_kernel<F16><<<grid, 64 * kWaves, 0, stream>>>(p);
+    else gemm_group_kernel<BF16><<<grid, 64 * kWaves, 0, stream>>>(p);
     return hipGetLastError();
 }
 
