@@ -21,11 +21,18 @@ Printed: one JSON line with
   fp16_gemm        torch.matmul (hipBLASLt) of X and W in the 16-bit type, same shape
 Progress goes to stderr.
 
+Other modes, each with its own JSON line of the same shape:
+  --fixed          the fixed-outlier path (the workload's injected columns as the set)
+  --group G        the group-wise path, groups of G features along K (no outlier split);
+                   the dominant kernel is the grouped product kernel
+  --codec          the block-wise absmax int8 codec on a 2^28-element fp32 state (GB/s)
+  --gpus N         N > 1 exits with a message: the library runs on one GPU
+
 Counter measurement of `traffic` (one rocprofv3 run per counter, then on any host):
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR_F -o run -- \\
       python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-fp16-gemm --copy-mib 1024
   (the same with WRITE_SIZE into DIR_W), then
-  python3 bench.py --traffic-summary DIR_F DIR_W [--workload NAME]
+  python3 bench.py --traffic-summary DIR_F DIR_W [--workload NAME] [--group G]
 which writes profiles/<kernel>_traffic_<workload>.json and .md.
 """
 from __future__ import annotations
