@@ -14,8 +14,8 @@
 namespace llmint8 {
 
 __global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0.0f;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.0f;
 }
 
 // s_w[n] = max_k |W[k,n]|: each block reduces a 512-column x (K/splits)-row slab and
@@ -102,23 +102,25 @@ __global__ __launch_bounds__(256) void gather_wo_kernel(const uint16_t* __restri
                                                         const int32_t* __restrict__ O, int64_t nO, int64_t P,
                                                         uint16_t* __restrict__ WO) {
     const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t t = blockIdx.y;
     if (n >= N) return;
-    const int64_t k = t < nO ? (int64_t)O[t] : -1;
-    WO[n * P + t] = (k >= 0 && k < K) ? W[k * N + n] : (uint16_t)0;
+    for (int64_t t = blockIdx.y; t < P; t += gridDim.y) {  // grid.y is capped at 65535
+        const int64_t k = t < nO ? (int64_t)O[t] : -1;
+        WO[n * P + t] = (k >= 0 && k < K) ? W[k * N + n] : (uint16_t)0;
+    }
 }
 
 hipError_t launch_gather_wo(const void* W, int64_t K, int64_t N, const int32_t* O, int64_t nO, int64_t P, void* WO,
                             hipStream_t stream) {
     if (N == 0 || P == 0) return hipSuccess;
-    dim3 g((unsigned)ceil_div(N, 256), (unsigned)P);
+    dim3 g((unsigned)ceil_div(N, 256), (unsigned)(P < 65535 ? P : 65535));
     gather_wo_kernel<<<g, 256, 0, stream>>>((const uint16_t*)W, K, N, O, nO, P, (uint16_t*)WO);
     return hipGetLastError();
 }
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t stream) {
     if (n == 0) return hipSuccess;
-    fill_zero_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, stream>>>(p, n);
+    const int64_t blocks = ceil_div(n, 256);
+    fill_zero_kernel<<<(unsigned)(blocks < 65536 ? blocks : 65536), 256, 0, stream>>>(p, n);
     return hipGetLastError();
 }
 
@@ -130,8 +132,7 @@ int64_t weight_splits(int64_t K) {
 hipError_t launch_weight(int dt, const void* W, int64_t K, int64_t N, int8_t* Wq, float* w_scale,
                          const uint32_t* skip, hipStream_t stream) {
     if (N == 0) return hipSuccess;
-    fill_zero_kernel<<<(unsigned)ceil_div(N, 256), 256, 0, stream>>>(w_scale, N);
-    hipError_t e = hipGetLastError();
+    hipError_t e = launch_fill_zero(w_scale, N, stream);
     if (e != hipSuccess || K == 0) return e;
     const int64_t S = weight_splits(K);
     const int64_t rps = ceil_div(K, S);

@@ -94,3 +94,12 @@ def test_fixed_full_size_sampled(name):
     rows = np.unique(np.concatenate([[0, wl.M - 1], rng.integers(0, wl.M, 6)])) if wl.M > 16 else None
     st = _run(x, w, np.sort(np.asarray(cols, np.int32)), wl.dtype, rows)
     print(f"[stats] {name}: {st}", flush=True)
+
+
+def test_fixed_set_larger_than_one_launch_dimension():
+    # n_O > 65535: the W_O gather covers the set with a capped grid (rows of W_O in a loop)
+    M, K, N = 4, 66048, 8
+    x, w, _ = _case(M, K, N, "fp16", seed=11)
+    cols = np.arange(0, 65600, dtype=np.int32)
+    print(f"\n[case] fixed {M}x{K}x{N} with {cols.size} outlier columns", flush=True)
+    _run(x, w, cols, "fp16")
