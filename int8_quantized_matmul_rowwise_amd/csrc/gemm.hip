@@ -333,19 +333,32 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
             }
         }
     } else {
+        // Every global read of the epilogue is issued first, together, so that their latencies
+        // overlap (and the wait for the last operand loads): this thread's entry of the
+        // factor tables and the first 16 outlier columns of the wave's rows and columns.
+        const int64_t fm = m0 + tid, fn = n0 + tid - BM;
+        const float sc = tid < BM ? (fm < p.M ? p.s_x[fm] : 0.0f) : (fn < p.N ? p.s_w[fn] : 0.0f);
+        u32x4 xo0[4], wo0[NJ];
+        if (nsub > 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t am = wm0 + 32 * i + rl < p.M ? wm0 + 32 * i + rl : p.M - 1;
+                xo0[i] = *(const u32x4*)(p.XO + am * p.xo_pitch + h * 8);
+            }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int64_t bn = wn0 + 32 * j + rl < p.N ? wn0 + 32 * j + rl : p.N - 1;
+                wo0[j] = *(const u32x4*)(p.WO + bn * p.wo_pitch + h * 8);
+            }
+        }
         // The operand slots are free once every wave is past its last reads and no load is in
         // flight: the LDS then holds the tile's dequantization factors and, per wave, its
         // 128 x 64 outputs, which leave as 16-byte row segments (full lines).
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         float* rsc = (float*)smem;  // r_i = s_x[i]/127 of the tile's rows
         float* csc = rsc + BM;      // c_n = s_w[n]/127 of its columns
-        if (tid < BM) {
-            const int64_t m = m0 + tid;
-            rsc[tid] = m < p.M ? p.s_x[m] / 127.0f : 0.0f;
-        } else {
-            const int64_t n = n0 + tid - BM;
-            csc[tid - BM] = n < p.N ? p.s_w[n] / 127.0f : 0.0f;
-        }
+        if (tid < BM) rsc[tid] = sc / 127.0f;
+        else csc[tid - BM] = sc / 127.0f;
         __syncthreads();
         uint16_t* ys = (uint16_t*)(smem + kScaleBytes + w * kYStageBytes);
 #pragma unroll
@@ -363,7 +376,14 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
             const uint16_t* xo = p.XO + am * p.xo_pitch + h * 8;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const v16f F = outlier_product(xo, wn0 + 32 * j + rl);
+                v16f F = v16f{};
+                if (nsub > 0) {
+                    F = mfma16<DT>(xo0[i], wo0[j], F);
+                    const int64_t n = wn0 + 32 * j + rl;
+                    const uint16_t* wo = p.WO + (n < p.N ? n : p.N - 1) * p.wo_pitch + h * 8;
+                    for (int ch = 1; ch < nsub; ++ch)
+                        F = mfma16<DT>(*(const u32x4*)(xo + ch * 16), *(const u32x4*)(wo + ch * 16), F);
+                }
                 const float c = csc[wn * (32 * NJ) + 32 * j + rl];
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
