@@ -36,6 +36,13 @@
 //   Tiles are assigned so that the workgroups the dispatcher places on one XCD (ids
 //   congruent mod 8) take a contiguous run of tiles in grouped order (8 row-tiles per
 //   group): the 32 tiles running together on an XCD share A and B panels in its L2.
+//   Persistent: one workgroup per compute unit works through its XCD's run, strided by
+//   the XCD's workgroup count.  Its K stages run back to back across tile boundaries --
+//   the loads of a tile's last stages already fetch the next tile's first operands --,
+//   and a tile's epilogue (outlier product, dequantization, Y through the two LDS slots
+//   its last stage freed) runs while those are in flight.  Against one workgroup per tile,
+//   that removes the pipeline fill (about 2.5 us) and the workgroup launch (about 1.3 us)
+//   from every tile boundary.
 #include <type_traits>
 
 #include "common.hpp"
@@ -59,16 +66,18 @@ constexpr int kSlotsA = kLeadA ? 3 : 2;                  // 5 x 32 KB: the whole
 constexpr int kSlotsB = kLeadA ? 2 : 3;
 constexpr int kSlotBytesB = BN * BK;
 constexpr int kSubSteps = BK / 32;                       // 32-deep MFMA steps per stage
-constexpr int kGroupM = 8;
-// epilogue staging (reuses the operand slots): the tile's row and column factors, then per
-// wave its 128 x 64 outputs, rows padded to 144 bytes (16-byte aligned)
+constexpr int kGroupM = 8;                               // row tiles per group of the tile order
+// epilogue staging, in the A and B slots the tile's last stage freed: the tile's row and
+// column factors, then per wave one 32 x 64 slice of its outputs at a time, rows padded to
+// 144 bytes (16-byte aligned)
 constexpr int kScaleBytes = 2 * 256 * 4;
 constexpr int kYPitch = 72;  // 16-bit elements
-constexpr int kYStageBytes = 128 * kYPitch * 2;                               // row tiles per group of the tile order
+constexpr int kYQuarterBytes = 32 * kYPitch * 2;
 constexpr int kXcds = 8;
 static_assert(kSlotsA * kTileBytes + kSlotsB * kSlotBytesB <= 160 * 1024, "LDS");
 static_assert(kLoadsA == 4 && kLoadsB == 4, "the waits below count 4 loads per operand and wave");
-static_assert(kScaleBytes + kWaves * kYStageBytes <= kSlotsA * kTileBytes + kSlotsB * kSlotBytesB, "epilogue LDS");
+static_assert(kScaleBytes + 4 * kYQuarterBytes <= kTileBytes && 4 * kYQuarterBytes <= kSlotBytesB, "epilogue LDS");
+static_assert(!kLeadA && kSlotsA == 2 && kSlotsB == 3, "the stage loop rotates 2 A slots and 3 B slots, B two ahead");
 static_assert(BM == 256 && BN == 256, "the factor tables take one row and one column per thread");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -129,74 +138,96 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3;
 
-    // ---- tile of this workgroup (XCD-contiguous runs, grouped order)
+    // ---- tiles of this workgroup: the XCD-contiguous run of tiles (grouped order) of the
+    // XCD the dispatcher places it on (ids congruent mod 8), strided by the number of
+    // workgroups on that XCD
     const int T = p.tiles_m * p.tiles_n;
-    const int bid = blockIdx.x;
+    const int bid = blockIdx.x, nwg = gridDim.x;
     const int xcd = bid % kXcds, local = bid / kXcds;
     const int per = T / kXcds, rem = T % kXcds;
-    const int t = xcd * per + (xcd < rem ? xcd : rem) + local;
-    const int in_group = kGroupM * p.tiles_n;
-    const int first_m = (t / in_group) * kGroupM;
-    const int gm = p.tiles_m - first_m < kGroupM ? p.tiles_m - first_m : kGroupM;
-    const int tm = first_m + (t % in_group) % gm;
-    const int tn = (t % in_group) / gm;
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int x_start = xcd * per + (xcd < rem ? xcd : rem), x_cnt = per + (xcd < rem ? 1 : 0);
+    const int on_xcd = (nwg - xcd + kXcds - 1) / kXcds;
+    const int my_tiles = local < x_cnt ? (x_cnt - local + on_xcd - 1) / on_xcd : 0;
+    if (my_tiles == 0) return;  // the same for every wave of the workgroup
+    auto tile_origin = [&](int i, int64_t& m0, int64_t& n0) {
+        const int t = x_start + local + i * on_xcd;
+        const int in_group = kGroupM * p.tiles_n;
+        const int first_m = (t / in_group) * kGroupM;
+        const int gm = p.tiles_m - first_m < kGroupM ? p.tiles_m - first_m : kGroupM;
+        m0 = (int64_t)(first_m + (t % in_group) % gm) * BM;
+        n0 = (int64_t)((t % in_group) / gm) * BN;
+    };
 
-    // ---- loader: wave w fills LDS slots [1024*(4w+j), +1024) of each operand, j = 0..3:
-    // row r = 8*(4w + j) + lane/8 (one 128-byte line per row), physical chunk lane%8,
-    // logical chunk (lane%8) ^ swz(r).
+    // ---- per-lane offsets of the stage loop: loader (wave w fills LDS slots
+    // [1024*(4w+j), +1024) of each operand, j = 0..3: row r = 8*(4w + j) + lane/8 of the
+    // tile, one 128-byte line per row, physical chunk lane%8, logical chunk
+    // (lane%8) ^ swz(r)) and MFMA operand reads (32x32x32: lane holds row lane%32, 16 k at
+    // 16*(lane/32); fragment i of sub-step u reads row 32*i + lane%32 of the wave's
+    // 128-row panel, logical chunk 2u + lane/32).  They are recomputed after every
+    // epilogue from an opaque copy of the lane index, so that they are not held through it.
     const int wu = __builtin_amdgcn_readfirstlane(w);
     uint32_t a_off[kLoadsA], b_off[kLoadsB];
-#pragma unroll
-    for (int j = 0; j < kLoadsA; ++j) {
-        const int r = kRowsPerLoad * (kLoadsA * wu + j) + lane / kChunks;
-        const int c = (lane % kChunks) ^ swz(r);
-        const int64_t m = m0 + r < p.M ? m0 + r : p.M - 1;
-        a_off[j] = (uint32_t)((m - m0) * p.xq_pitch + c * 16);
-    }
-#pragma unroll
-    for (int j = 0; j < kLoadsB; ++j) {
-        const int r = kRowsPerLoad * (kLoadsB * wu + j) + lane / kChunks;
-        const int c = (lane % kChunks) ^ swz(r);
-        const int64_t n = n0 + r < p.N ? n0 + r : p.N - 1;
-        b_off[j] = (uint32_t)((n - n0) * p.K + c * 16);
-    }
-    const int8_t* a_tile = p.Xq + m0 * p.xq_pitch;
-    const int8_t* b_tile = p.Wq + n0 * p.K;
-    const int nk = (int)ceil_div(p.K, BK);
-    // The resources span the tile's rows (at most 256 of them: offsets fit 32 bits for any
-    // K the library accepts).  In a partial last stage the chunks past K of a B row read the
-    // next row's first bytes, or nothing (zero) past the last row: their A side is the zero
-    // padding of Xq, so they add exact zeros.
-    const int64_t rows_a = p.M - m0 < BM ? p.M - m0 : BM, rows_b = p.N - n0 < BN ? p.N - n0 : BN;
-    const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(a_tile, rows_a * p.xq_pitch);
-    const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(b_tile, rows_b * p.K);
-
-    auto slot_a = [&](int kt) { return smem + (kt % kSlotsA) * kTileBytes; };
-    auto slot_b = [&](int kt) { return smem + kSlotsA * kTileBytes + (kt % kSlotsB) * kSlotBytesB; };
-    auto issue_a = [&](int kt) {
-        int8_t* As = slot_a(kt);
-        const int kb = kt * BK;
-#pragma unroll
-        for (int j = 0; j < kLoadsA; ++j) load_lds16(rsa, a_off[j], kb, As + (kLoadsA * wu + j) * 1024);
-    };
-    auto issue_b = [&](int kt) {
-        int8_t* Bs = slot_b(kt);
-        const int kb = kt * BK;
-#pragma unroll
-        for (int j = 0; j < kLoadsB; ++j) load_lds16(rsb, b_off[j], kb, Bs + (kLoadsB * wu + j) * 1024);
-    };
-
-    // ---- MFMA operand reads (32x32x32: lane holds row lane%32, 16 k at 16*(lane/32)):
-    // fragment i of sub-step u reads row 32*i + lane%32 of the wave's 128-row panel,
-    // logical chunk 2u + lane/32.  Read in the order the MFMAs consume them.
-    const int rl = lane & 31, h = lane >> 5;
     int rd[kSubSteps];
+    auto lane_offsets = [&](int ln) {
 #pragma unroll
-    for (int u = 0; u < kSubSteps; ++u) rd[u] = rl * BK + (((2 * u + h) ^ swz(rl)) << 4);
-    auto read_frags = [&](int kt, int u, v4i (&fa)[4], v4i (&fb)[NJ]) {
-        const int8_t* As = slot_a(kt) + wm * 128 * BK + rd[u];
-        const int8_t* Bs = slot_b(kt) + wn * (32 * NJ) * BK + rd[u];
+        for (int j = 0; j < kLoadsA; ++j) {
+            const int r = kRowsPerLoad * (kLoadsA * wu + j) + ln / kChunks;
+            a_off[j] = (uint32_t)(r * p.xq_pitch + (((ln % kChunks) ^ swz(r)) << 4));
+        }
+#pragma unroll
+        for (int j = 0; j < kLoadsB; ++j) {
+            const int r = kRowsPerLoad * (kLoadsB * wu + j) + ln / kChunks;
+            b_off[j] = (uint32_t)(r * p.K + (((ln % kChunks) ^ swz(r)) << 4));
+        }
+        const int rl = ln & 31, h = ln >> 5;
+#pragma unroll
+        for (int u = 0; u < kSubSteps; ++u) rd[u] = rl * BK + (((2 * u + h) ^ swz(rl)) << 4);
+    };
+    lane_offsets(lane);
+    const int nk = (int)ceil_div(p.K, BK);  // >= 1 (K = 0 never reaches this kernel)
+
+    // ---- operand resources.  A tile's resources span its rows (at most 256 of them:
+    // offsets fit 32 bits for any K the library accepts); rows past M or N lie past the
+    // resource and read zero.  In a partial last stage the chunks past K of a B row read
+    // the next row's first bytes, or nothing (zero) past the last row: their A side is the
+    // zero padding of Xq, so they add exact zeros.  Loads run up to two stages ahead, across
+    // tile boundaries: the resources of this tile and the next two are held.  Past the
+    // workgroup's last tile a resource is empty: every stage issues its loads, and those
+    // land zeros in slots no stage reads.
+    auto tile_rsrc = [&](int i, __amdgpu_buffer_rsrc_t& ra, __amdgpu_buffer_rsrc_t& rb) {
+        int64_t m0 = 0, n0 = 0, rows_a = 0, rows_b = 0;
+        if (i < my_tiles) {
+            tile_origin(i, m0, n0);
+            rows_a = p.M - m0 < BM ? p.M - m0 : BM;
+            rows_b = p.N - n0 < BN ? p.N - n0 : BN;
+        }
+        ra = buffer_rsrc(p.Xq + m0 * p.xq_pitch, rows_a * p.xq_pitch);
+        rb = buffer_rsrc(p.Wq + n0 * p.K, rows_b * p.K);
+    };
+    __amdgpu_buffer_rsrc_t ra0, rb0, ra1, rb1, ra2, rb2;
+    tile_rsrc(0, ra0, rb0);
+    tile_rsrc(1, ra1, rb1);
+    tile_rsrc(2, ra2, rb2);
+
+    // The workgroup's stages run back to back over its tiles: global stage s sits in A slot
+    // s % 2 and B slot s % 3.  `d` = tiles ahead of the current one.
+    auto slot_a = [&](int sa) { return smem + sa * kTileBytes; };
+    auto slot_b = [&](int sb) { return smem + kSlotsA * kTileBytes + sb * kSlotBytesB; };
+    auto issue_a = [&](int sa, int kt, int d) {
+        const __amdgpu_buffer_rsrc_t rs = d == 0 ? ra0 : (d == 1 ? ra1 : ra2);
+        int8_t* As = slot_a(sa);
+#pragma unroll
+        for (int j = 0; j < kLoadsA; ++j) load_lds16(rs, a_off[j], kt * BK, As + (kLoadsA * wu + j) * 1024);
+    };
+    auto issue_b = [&](int sb, int kt, int d) {
+        const __amdgpu_buffer_rsrc_t rs = d == 0 ? rb0 : (d == 1 ? rb1 : rb2);
+        int8_t* Bs = slot_b(sb);
+#pragma unroll
+        for (int j = 0; j < kLoadsB; ++j) load_lds16(rs, b_off[j], kt * BK, Bs + (kLoadsB * wu + j) * 1024);
+    };
+    auto read_frags = [&](int sa, int sb, int u, v4i (&fa)[4], v4i (&fb)[NJ]) {
+        const int8_t* As = slot_a(sa) + wm * 128 * BK + rd[u];
+        const int8_t* Bs = slot_b(sb) + wn * (32 * NJ) * BK + rd[u];
         fa[0] = *(const v4i*)As;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) fb[j] = *(const v4i*)(Bs + j * 32 * BK);
@@ -205,11 +236,6 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
     };
 
     v16i acc[4][NJ];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = v16i{};
-
     auto mfma_rows = [&](const v4i (&fa)[4], const v4i (&fb)[NJ], int i0, int i1) {
 #pragma unroll
         for (int i = i0; i < i1; ++i)
@@ -218,36 +244,77 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
                 acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
     };
 
-    // One K stage.  Sub-steps 0..2 run their 8 MFMAs while the 6 LDS reads of the next
-    // sub-step (and, in 0 and 1, the global loads of stage kt+1 of the short-lead operand
-    // and stage kt+2 of the long-lead one, into the slots stage kt-1 freed) are
-    // interleaved, front-loaded so they have most of the sub-step to land.  Sub-step 3 runs
-    // 2 MFMAs, waits for stage kt+1 and meets the other waves at the barrier, then reads
-    // stage kt+1's first operands under its other 6.  Each sub-step is fenced
-    // (sched_barrier) so that the interleave stays inside it.
-    // STEADY: stage kt+2 exists (every stage but the last two).
+    // ---- the epilogue's global reads, issued in a tile's last stage (whose closing wait
+    // then covers them): this thread's entry of the factor tables (waves 0-3: the rows'
+    // s_x, waves 4-7: the columns' s_w) at its top, and the first 16 outlier columns of the
+    // wave's rows and columns after its barrier (in the registers the next stage's first
+    // operands take elsewhere).  Unconditional buffer loads: with no outlier column the
+    // resources are empty and the loads return zeros.
+    const int32_t nO = *p.n_out;
+    const int nsub = (nO + 15) >> 4;  // 16-deep MFMA steps over the padded outlier columns
+    float sc = 0.0f;
+    u32x4 xo0[4], wo0[NJ];
+    auto epilogue_reads = [&](int ti, bool outlier_part) {
+        int lx = lane, tx = tid;
+        asm volatile("" : "+v"(lx), "+v"(tx));
+        const int rl = lx & 31, h = lx >> 5, tid = tx;
+        const int w = __builtin_amdgcn_readfirstlane(tx >> 6), wm = w >> 2, wn = w & 3;
+        int64_t m0, n0;
+        tile_origin(ti, m0, n0);
+        if (outlier_part) {
+            const int64_t rows = nsub > 0 ? (p.M - m0 < BM ? p.M - m0 : BM) : 0;
+            const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(p.XO + m0 * p.xo_pitch, rows * p.xo_pitch * 2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                xo0[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rx, (uint32_t)(((wm * 128 + 32 * i + rl) * p.xo_pitch + h * 8) * 2), 0, 0));
+        } else {
+            const int64_t cols = nsub > 0 ? (p.N - n0 < BN ? p.N - n0 : BN) : 0;
+            const __amdgpu_buffer_rsrc_t rw = buffer_rsrc(p.WO + n0 * p.wo_pitch, cols * p.wo_pitch * 2);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                wo0[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       rw, (uint32_t)(((wn * (32 * NJ) + 32 * j + rl) * p.wo_pitch + h * 8) * 2), 0, 0));
+            // factor tables: rows m0 + tid (waves 0-3) or columns n0 + tid - 256 (waves 4-7)
+            const bool rows_side = w < 4;
+            const int64_t base = rows_side ? m0 : n0, lim = rows_side ? p.M : p.N;
+            const int64_t cnt = lim - base < BM ? lim - base : BM;
+            const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(rows_side ? (const void*)(p.s_x + m0) : (const void*)(p.s_w + n0), cnt * 4);
+            sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)((tid & (BM - 1)) * 4), 0, 0));
+        }
+    };
+
+    // One K stage (global stage s in slots sa, sb; stage kt of its tile).  Sub-steps 0..2
+    // run their 8 MFMAs while the 6 LDS reads of the next sub-step (and, in 0 and 1, the
+    // global loads of stage s+1 of the short-lead operand and stage s+2 of the long-lead
+    // one, into the slots stage s-1 freed) are interleaved, front-loaded so they have most
+    // of the sub-step to land.  Sub-step 3 runs 2 MFMAs, waits for stage s+1 and meets the
+    // other waves at the barrier, then reads stage s+1's first operands under its other 6
+    // -- except in a tile's last stage (LAST), where the epilogue comes first.  Each
+    // sub-step is fenced (sched_barrier) so that the interleave stays inside it.
     v4i fa[2][4], fb[2][NJ];  // operand sets of the current / next sub-step
-    auto stage = [&](int kt, auto steady_tag) {
-        constexpr bool STEADY = decltype(steady_tag)::value;
-        const bool next = STEADY || kt + 1 < nk;
+    auto stage = [&](int sa, int sb, int kt, int ti, auto last_tag) {
+        constexpr bool LAST = decltype(last_tag)::value;
+        // (readfirstlane: the compiler then knows these, and so the resources, are uniform)
+        const int ka = kt + 1 < nk ? kt + 1 : kt + 1 - nk;
+        const int da = __builtin_amdgcn_readfirstlane(kt + 1 < nk ? 0 : 1);
+        const int db = __builtin_amdgcn_readfirstlane(kt + 2 < nk ? 0 : (kt + 2 < 2 * nk ? 1 : 2));
+        const int kb = kt + 2 - db * nk;
+        if constexpr (LAST && !ACC_OUT) {
+            epilogue_reads(ti, false);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int u = 0; u < kSubSteps - 1; ++u) {
             const int cur = u & 1, nxt = cur ^ 1;
-            const bool loads = STEADY && u < 2;
             // this sub-step's operands were read a sub-step ago: a free wait that keeps the
             // compiler's own waits (it counts the direct-to-LDS loads as LDS traffic) out
             __builtin_amdgcn_s_waitcnt(0xC07F);
-            if (u == 0 && next) {
-                if (kLeadA) issue_b(kt + 1);
-                else issue_a(kt + 1);
-            }
-            if (u == 1 && STEADY) {
-                if (kLeadA) issue_a(kt + 2);
-                else issue_b(kt + 2);
-            }
-            read_frags(kt, u + 1, fa[nxt], fb[nxt]);
+            if (u == 0) issue_a(sa ^ 1, ka, da);
+            if (u == 1) issue_b(sb == 0 ? 2 : sb - 1, kb, db);
+            read_frags(sa, sb, u + 1, fa[nxt], fb[nxt]);
             mfma_rows(fa[cur], fb[cur], 0, 4);
-            if (loads) {
+            if (u < 2) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
@@ -271,143 +338,172 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
         }
         mfma_rows(fa[1], fb[1], 0, 1);
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (STEADY) LLMINT8_WAIT_BARRIER(4);  // the stage kt+2 loads may stay in flight
-        else LLMINT8_WAIT_BARRIER(0);
-        if (next) read_frags(kt + 1, 0, fa[0], fb[0]);
+        LLMINT8_WAIT_BARRIER(4);  // the stage s+2 loads may stay in flight
+        if constexpr (!LAST) read_frags(sa ^ 1, sb == 2 ? 0 : sb + 1, 0, fa[0], fb[0]);
+        else if constexpr (!ACC_OUT) epilogue_reads(ti, true);
         mfma_rows(fa[1], fb[1], 1, 4);
         __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    if (nk > 0) {
-        // prologue: A[0], B[0] (and B[1]) in flight; wait for the first two groups
-        issue_a(0);
-        issue_b(0);
-        if (nk > 1) {
-            if (kLeadA) issue_a(1);
-            else issue_b(1);
-            LLMINT8_WAIT_BARRIER(4);
-        } else {
-            LLMINT8_WAIT_BARRIER(0);
-        }
-        read_frags(0, 0, fa[0], fb[0]);
-        int kt = 0;
-        for (; kt + 2 < nk; ++kt) stage(kt, std::true_type{});
-        for (; kt < nk; ++kt) stage(kt, std::false_type{});
-    }
-
-    // ---- 16-bit outlier product and epilogue, one 32-row slice at a time
-    // (lane holds column lane%32 and rows 8*(e/4) + 4*(lane/32) + e%4, e = 0..15, of each
-    // 32 x 32 tile)
-    const int32_t nO = *p.n_out;
-    const int nsub = (nO + 15) >> 4;  // 16-deep MFMA steps over the padded outlier columns
-    const int64_t wm0 = m0 + wm * 128, wn0 = n0 + wn * (32 * NJ);
-    auto outlier_product = [&](const uint16_t* xo, int64_t n) {
-        const int64_t bn = n < p.N ? n : p.N - 1;
-        const uint16_t* wo = p.WO + bn * p.wo_pitch + h * 8;
-        v16f F = v16f{};
-        for (int ch = 0; ch < nsub; ++ch)
-            F = mfma16<DT>(*(const u32x4*)(xo + ch * 16), *(const u32x4*)(wo + ch * 16), F);
-        return F;
-    };
-    if constexpr (ACC_OUT) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int64_t row0 = wm0 + 32 * i + 4 * h;
-            int64_t am = wm0 + 32 * i + rl;
-            am = am < p.M ? am : p.M - 1;
-            const uint16_t* xo = p.XO + am * p.xo_pitch + h * 8;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int64_t n = wn0 + 32 * j + rl;
-                const v16f F = outlier_product(xo, n);
-                if (n >= p.N) continue;
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int64_t m = row0 + 8 * (e >> 2) + (e & 3);
-                    if (m >= p.M) continue;
-                    p.C_acc[m * p.N + n] = acc[i][j][e];
-                    p.F_acc[m * p.N + n] = F[e];
-                }
-            }
-        }
-    } else {
-        // Every global read of the epilogue is issued first, together, so that their latencies
-        // overlap (and the wait for the last operand loads): this thread's entry of the
-        // factor tables and the first 16 outlier columns of the wave's rows and columns.
-        const int64_t fm = m0 + tid, fn = n0 + tid - BM;
-        const float sc = tid < BM ? (fm < p.M ? p.s_x[fm] : 0.0f) : (fn < p.N ? p.s_w[fn] : 0.0f);
-        u32x4 xo0[4], wo0[NJ];
-        if (nsub > 0) {
+    // ---- epilogue of tile ti: 16-bit outlier product, dequantization, Y.  The LDS slots of
+    // the stage just consumed (A sa, B sb) are free: no wave reads them past that stage's
+    // barrier, and the loads in flight go to the other slots.
+    auto epilogue = [&](int ti, int sa, int sb) {
+        // lane-derived values made opaque here, so that the compiler computes the
+        // epilogue's addresses in it instead of holding them through the main loop
+        int lx = lane, tx = tid;
+        asm volatile("" : "+v"(lx), "+v"(tx));
+        const int rl = lx & 31, h = lx >> 5, lane = lx, tid = tx;
+        const int w = __builtin_amdgcn_readfirstlane(tx >> 6), wm = w >> 2, wn = w & 3;
+        int64_t m0, n0;
+        tile_origin(ti, m0, n0);
+        const int64_t wm0 = m0 + wm * 128, wn0 = n0 + wn * (32 * NJ);
+        if constexpr (ACC_OUT) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int64_t am = wm0 + 32 * i + rl < p.M ? wm0 + 32 * i + rl : p.M - 1;
-                xo0[i] = *(const u32x4*)(p.XO + am * p.xo_pitch + h * 8);
-            }
+                const int64_t row0 = wm0 + 32 * i + 4 * h;
+                int64_t am = wm0 + 32 * i + rl;
+                am = am < p.M ? am : p.M - 1;
+                const uint16_t* xo = p.XO + am * p.xo_pitch + h * 8;
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                const int64_t bn = wn0 + 32 * j + rl < p.N ? wn0 + 32 * j + rl : p.N - 1;
-                wo0[j] = *(const u32x4*)(p.WO + bn * p.wo_pitch + h * 8);
-            }
-        }
-        // The operand slots are free once every wave is past its last reads and no load is in
-        // flight: the LDS then holds the tile's dequantization factors and, per wave, its
-        // 128 x 64 outputs, which leave as 16-byte row segments (full lines).
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        float* rsc = (float*)smem;  // r_i = s_x[i]/127 of the tile's rows
-        float* csc = rsc + BM;      // c_n = s_w[n]/127 of its columns
-        if (tid < BM) rsc[tid] = sc / 127.0f;
-        else csc[tid - BM] = sc / 127.0f;
-        __syncthreads();
-        uint16_t* ys = (uint16_t*)(smem + kScaleBytes + w * kYStageBytes);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rb = wm * 128 + 32 * i + 4 * h;  // tile row of e = 0
-            float r[16];
-#pragma unroll
-            for (int a = 0; a < 4; ++a) {
-                const v4f t = *(const v4f*)(rsc + rb + 8 * a);
-#pragma unroll
-                for (int b = 0; b < 4; ++b) r[4 * a + b] = t[b];
-            }
-            int64_t am = wm0 + 32 * i + rl;
-            am = am < p.M ? am : p.M - 1;
-            const uint16_t* xo = p.XO + am * p.xo_pitch + h * 8;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) {
-                v16f F = v16f{};
-                if (nsub > 0) {
-                    F = mfma16<DT>(xo0[i], wo0[j], F);
+                for (int j = 0; j < NJ; ++j) {
                     const int64_t n = wn0 + 32 * j + rl;
-                    const uint16_t* wo = p.WO + (n < p.N ? n : p.N - 1) * p.wo_pitch + h * 8;
-                    for (int ch = 1; ch < nsub; ++ch)
+                    const int64_t bn = n < p.N ? n : p.N - 1;
+                    const uint16_t* wo = p.WO + bn * p.wo_pitch + h * 8;
+                    v16f F = v16f{};
+                    for (int ch = 0; ch < nsub; ++ch)
                         F = mfma16<DT>(*(const u32x4*)(xo + ch * 16), *(const u32x4*)(wo + ch * 16), F);
-                }
-                const float c = csc[wn * (32 * NJ) + 32 * j + rl];
+                    if (n >= p.N) continue;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float yi = __fmul_rn(__fmul_rn((float)acc[i][j][e], r[e]), c);
-                    const float y = __fadd_rn(yi, p.f_scaled ? __fmul_rn(c, F[e]) : F[e]);
-                    ys[(32 * i + 8 * (e >> 2) + 4 * h + (e & 3)) * kYPitch + 32 * j + rl] = from_f32<DT>(y);
+                    for (int e = 0; e < 16; ++e) {
+                        const int64_t m = row0 + 8 * (e >> 2) + (e & 3);
+                        if (m >= p.M) continue;
+                        p.C_acc[m * p.N + n] = acc[i][j][e];
+                        p.F_acc[m * p.N + n] = F[e];
+                    }
+                }
+            }
+        } else {
+            float* rsc = (float*)slot_a(sa);  // r_i = s_x[i]/127 of the tile's rows
+            float* csc = rsc + BM;            // c_n = s_w[n]/127 of its columns
+            rsc[tid] = sc / 127.0f;           // (csc[tid - 256] for waves 4-7)
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_s_barrier();
+            // per wave, a 32 x 64 staging area (rows padded to 144 bytes): waves 0-3 in the
+            // free A slot after the factor tables, waves 4-7 in the free B slot
+            uint16_t* ys = (uint16_t*)(w < 4 ? slot_a(sa) + kScaleBytes + w * kYQuarterBytes
+                                             : slot_b(sb) + (w - 4) * kYQuarterBytes);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rb = wm * 128 + 32 * i + 4 * h;  // tile row of e = 0
+                // the slice's 16-bit outlier products: the first 16 columns from the
+                // prefetched operands, the rest one 16-column step (both column tiles) per
+                // round trip
+                v16f F[NJ];
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) F[j] = mfma16<DT>(xo0[i], wo0[j], v16f{});
+                if (nsub > 1) {
+                    int64_t am = wm0 + 32 * i + rl;
+                    am = am < p.M ? am : p.M - 1;
+                    const uint16_t* xo = p.XO + am * p.xo_pitch + h * 8;
+                    const uint16_t* wo[NJ];
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        const int64_t n = wn0 + 32 * j + rl;
+                        wo[j] = p.WO + (n < p.N ? n : p.N - 1) * p.wo_pitch + h * 8;
+                    }
+                    for (int ch = 1; ch < nsub; ++ch) {
+                        const u32x4 xa = *(const u32x4*)(xo + ch * 16);
+                        u32x4 wa[NJ];
+#pragma unroll
+                        for (int j = 0; j < NJ; ++j) wa[j] = *(const u32x4*)(wo[j] + ch * 16);
+#pragma unroll
+                        for (int j = 0; j < NJ; ++j) F[j] = mfma16<DT>(xa, wa[j], F[j]);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const float c = csc[wn * (32 * NJ) + 32 * j + rl];
+                    // the outlier term's factor: c_n, or 1 (an exact product) when W_O holds
+                    // 16-bit rows of W
+                    const float cf = p.f_scaled ? c : 1.0f;
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        // row factors: four at a time from the table, for each column tile
+                        const float re = ((const v4f*)(rsc + rb + 8 * (e >> 2)))[0][e & 3];
+                        const float yi = __fmul_rn(__fmul_rn((float)acc[i][j][e], re), c);
+                        const float y = __fadd_rn(yi, __fmul_rn(cf, F[j][e]));
+                        ys[(8 * (e >> 2) + 4 * h + (e & 3)) * kYPitch + 32 * j + rl] = from_f32<DT>(y);
+                    }
+                }
+                // all the prefetched outlier operands are in before the first stores (else
+                // the compiler's wait for a later slice's would also wait for the stores)
+                if (i == 0) asm volatile("" ::"v"(xo0[1]), "v"(xo0[2]), "v"(xo0[3]));
+                // read the slice back as 16-byte row segments (one wave's LDS accesses
+                // complete in order) and store them (full lines)
+#pragma unroll
+                for (int it = 0; it < 4; ++it) {
+                    const int row = it * 8 + (lane >> 3), ch = lane & 7;
+                    const u32x4 v = *(const u32x4*)(ys + row * kYPitch + ch * 8);
+                    const int64_t m = wm0 + 32 * i + row, n = wn0 + ch * 8;
+                    if (m < p.M && n < p.N) *(u32x4*)(p.Y + m * p.N + n) = v;
                 }
             }
         }
-        // read back the wave's own rows (one wave's LDS accesses complete in order)
-#pragma unroll 4
-        for (int it = 0; it < 16; ++it) {
-            const int row = it * 8 + (lane >> 3), ch = lane & 7;
-            const u32x4 v = *(const u32x4*)(ys + row * kYPitch + ch * 8);
-            const int64_t m = wm0 + row, n = wn0 + ch * 8;
-            if (m < p.M && n < p.N) *(u32x4*)(p.Y + m * p.N + n) = v;
+    };
+
+    // ---- prologue: global stages 0 and (of the long-lead operand) 1 in flight
+    issue_a(0, 0, 0);
+    issue_b(0, 0, 0);
+    issue_b(1, nk > 1 ? 1 : 0, nk > 1 ? 0 : 1);
+    LLMINT8_WAIT_BARRIER(4);
+    read_frags(0, 0, 0, fa[0], fb[0]);
+    int sa = 0, sb = 0;
+    for (int ti = 0; ti < my_tiles; ++ti) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[i][j] = v16i{};
+        for (int kt = 0; kt + 1 < nk; ++kt) {
+            stage(sa, sb, kt, ti, std::false_type{});
+            sa ^= 1;
+            sb = sb == 2 ? 0 : sb + 1;
+        }
+        stage(sa, sb, nk - 1, ti, std::true_type{});
+        epilogue(ti, sa, sb);
+        sa ^= 1;
+        sb = sb == 2 ? 0 : sb + 1;
+        if (ti + 1 < my_tiles) {
+            ra0 = ra1;
+            rb0 = rb1;
+            ra1 = ra2;
+            rb1 = rb2;
+            tile_rsrc(ti + 3, ra2, rb2);
+            int lx = lane;
+            asm volatile("" : "+v"(lx));
+            lane_offsets(lx);
+            // every wave is done with its staging area (the next stage's loads go there)
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_s_barrier();
+            read_frags(sa, sb, 0, fa[0], fb[0]);
         }
     }
+    // no load into this workgroup's LDS may outlive it
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <int DT, bool ACC_OUT>
 hipError_t launch_one(const Params& p, hipStream_t stream) {
-    const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
-    gemm_kernel<DT, ACC_OUT><<<grid, 64 * kWaves, 0, stream>>>(p);
+    // persistent: one workgroup per compute unit (its LDS admits one), at most one per tile
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int64_t T = (int64_t)p.tiles_m * p.tiles_n;
+    const int64_t wgs = T < cus ? T : (cus > 0 ? cus : 1);
+    gemm_kernel<DT, ACC_OUT><<<(unsigned)wgs, 64 * kWaves, 0, stream>>>(p);
     return hipGetLastError();
 }
 
@@ -415,6 +511,13 @@ hipError_t launch_one(const Params& p, hipStream_t stream) {
 
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     if (a.M == 0 || a.N == 0) return hipSuccess;
+    if (a.K == 0) {
+        // the empty sum: C = 0, F = 0, Y = +0 (the kernel assumes at least one K stage)
+        const int64_t mn = a.M * a.N;
+        if (a.Y) return launch_fill_zero((float*)a.Y, mn / 2, stream);  // N is a multiple of 8
+        hipError_t e = launch_fill_zero((float*)a.C_acc, mn, stream);
+        return e == hipSuccess ? launch_fill_zero(a.F_acc, mn, stream) : e;
+    }
     Params p;
     p.Xq = a.Xq;
     p.xq_pitch = a.xq_pitch;

@@ -52,6 +52,33 @@ def test_edge_shapes(M, K, N, dt):
     parity.run_case(x, w, 6.0)
 
 
+@pytest.mark.parametrize("K,dt", [(128, "fp16"), (256, "bf16"), (400, "fp16"), (336, "bf16")])
+def test_several_tiles_per_workgroup(K, dt):
+    # 17 x 21 = 357 tiles of 256 x 256 on 256 workgroups: some take two tiles, and the
+    # operand loads run one (K = 128: one stage per tile) or two tiles ahead; ragged in M,
+    # N and K (400 and 336: a partial last stage).  Rows sampled in the first, a middle
+    # and the last row tile, C compared exactly.
+    M, N = 4200, 5256
+    _banner(f"several tiles per workgroup {M}x{K}x{N} {dt}")
+    x, w = _case(M, K, N, dt, n_out=4, seed=K)
+    rng = np.random.default_rng(K)
+    rows = np.unique(np.concatenate([[0, 255, 256, 2047, 4095, 4096, M - 1], rng.integers(0, M, 5)]))
+    st = parity.run_case(x, w, 6.0, rows=rows)
+    assert st["n_outliers"] >= 4
+
+
+def test_k_zero_on_the_tiled_path():
+    # M > 64 takes the tiled kernel's launcher: K = 0 is the empty sum (Y = +0, C = F = 0)
+    _banner("K=0, M=300, N=264")
+    X = torch.zeros(300, 0, dtype=torch.float16, device="cuda")
+    Wq = torch.zeros(264, 0, dtype=torch.int8, device="cuda")
+    s_w = torch.zeros(264, device="cuda")
+    Y = lm.int8_matmul(X, Wq, s_w, 6.0, Y=torch.full((300, 264), 5.0, dtype=torch.float16, device="cuda"))
+    C, F, _ = lm.int8_matmul_accumulators(X, Wq, 6.0)
+    torch.cuda.synchronize()
+    assert not Y.view(torch.int16).any() and not C.any() and not F.view(torch.int32).any()
+
+
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
 def test_threshold_exactly_tau_is_not_an_outlier(dt):
     _banner(f"x == tau {dt}")
