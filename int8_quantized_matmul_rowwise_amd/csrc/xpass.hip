@@ -192,11 +192,13 @@ hipError_t launch_compact(int64_t M, int64_t K, const uint32_t* partial, uint32_
 namespace llmint8 {
 
 
+// One wave per workgroup: the few workgroups a small X has then spread over more compute
+// units (K = 8192: 16 instead of 4).
 template <int DT>
-__global__ __launch_bounds__(256) void detect_direct_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
-                                                            float tau, uint32_t* __restrict__ bitmap) {
-    const int lane = threadIdx.x & 63;
-    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;  // 8-column chunk
+__global__ __launch_bounds__(64) void detect_direct_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                           float tau, uint32_t* __restrict__ bitmap) {
+    const int lane = threadIdx.x;
+    const int64_t c = (int64_t)blockIdx.x * 64 + threadIdx.x;  // 8-column chunk
     const int64_t nch = K / 8;
     uint32_t mask = 0;
     if (c < nch) {
@@ -438,6 +440,135 @@ __global__ __launch_bounds__(256) void code_rows_kernel(const uint16_t* __restri
     if (WRITE_O && g == 0 && tid == 0) *n_out = total;
 }
 
+// The whole small-batch X pass in one workgroup, for M * K <= kOneMaxElems (64 KB of X:
+// one compute unit keeps too few loads in flight for more -- 256 KB took 30 us this way,
+// against 9 us for the two launches): X is read once, into registers (up to kOneChunks
+// 8-column chunks per thread, chunk i of the
+// row-major X at X + 8 i), and every later step works on them and on LDS: detection (the
+// chunks' outlier bits ORed into an LDS bitmap), the list O and the per-word ranks (a
+// block scan of the words' popcounts, one word per thread: K <= 32768), the row maxima
+// over the non-outlier columns (per row in LDS, one atomic per wave when the wave's 64
+// chunks lie in one row) and the coding.  The same per-chunk arithmetic as the two-launch
+// path, so the results are the same bits.  All indices fit 32 bits (M <= 64, K <= 32768).
+constexpr int kOneChunks = 4;
+constexpr int64_t kOneMaxElems = 1024 * kOneChunks * 8;
+
+template <int DT>
+__global__ __launch_bounds__(1024) void xpass_one_kernel(const uint16_t* __restrict__ X, int M, int K, float tau,
+                                                         uint32_t* __restrict__ bitmap, int32_t* __restrict__ O,
+                                                         int32_t* __restrict__ n_out, int8_t* __restrict__ Xq,
+                                                         int xq_pitch, float* __restrict__ s_x,
+                                                         uint16_t* __restrict__ XO, int xo_pitch) {
+    __shared__ uint32_t bits[1024];
+    __shared__ int32_t wrank[1024];
+    __shared__ uint32_t rmax[kSmallM];
+    __shared__ int32_t wsum[16];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int C = K / 8, items = M * C, Kw = (K + 31) / 32;
+    // chunk tid + 1024 u is row r[u], chunk c[u] of it (stepped without divisions)
+    int r[kOneChunks], c[kOneChunks];
+    {
+        const int q = 1024 / C, rm = 1024 % C;
+        int rr = tid / C, cc = tid % C;
+#pragma unroll
+        for (int u = 0; u < kOneChunks; ++u) {
+            r[u] = rr;
+            c[u] = cc;
+            rr += q;
+            cc += rm;
+            if (cc >= C) {
+                cc -= C;
+                ++rr;
+            }
+        }
+    }
+    u32x4 v[kOneChunks];
+#pragma unroll
+    for (int u = 0; u < kOneChunks; ++u) {
+        const int i = tid + 1024 * u;
+        v[u] = i < items ? *(const u32x4*)(X + 8 * i) : u32x4{0u, 0u, 0u, 0u};
+    }
+    bits[tid] = 0;
+    if (tid < kSmallM) rmax[tid] = 0;
+    __syncthreads();
+    // detection: |x| > tau, compared in fp32
+#pragma unroll
+    for (int u = 0; u < kOneChunks; ++u) {
+        if (tid + 1024 * u >= items) continue;
+        uint32_t mask = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            mask |= (__builtin_fabsf(to_f32<DT>((uint16_t)(v[u][j >> 1] >> (16 * (j & 1))))) > tau ? 1u : 0u) << j;
+        if (mask) atomicOr(&bits[c[u] >> 2], mask << (8 * (c[u] & 3)));
+    }
+    __syncthreads();
+    // O in ascending column order, n_O, and each word's rank of its first outlier column
+    const uint32_t word = tid < Kw ? bits[tid] : 0u;
+    const int32_t cnt = __popc(word);
+    int32_t incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t t = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += t;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int32_t pos = incl - cnt, total = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+        pos += q < wv ? wsum[q] : 0;
+        total += wsum[q];
+    }
+    if (tid < Kw) {
+        wrank[tid] = pos;
+        bitmap[tid] = word;
+        for (uint32_t wd = word, t = (uint32_t)pos; wd; wd &= wd - 1) O[t++] = 32 * tid + __ffs(wd) - 1;
+    }
+    if (tid == 0) *n_out = total;
+    auto obits = [&](int cc) { return (bits[cc >> 2] >> (8 * (cc & 3))) & 0xffu; };
+    // row maxima of the magnitudes (15-bit patterns) over the non-outlier columns
+#pragma unroll
+    for (int u = 0; u < kOneChunks; ++u) {
+        if (1024 * u + 64 * wv >= items) continue;  // the wave's first chunk (wave-uniform)
+        const bool valid = tid + 1024 * u < items;
+        uint32_t m = 0;
+        if (valid) {
+            const u16x2 mb = absmax_bits(u16x2{0, 0}, v[u], obits(c[u]), true);
+            m = mb[0] > mb[1] ? mb[0] : mb[1];
+        }
+        // the wave's 64 chunks in one row: reduce in the wave (patterns below 2^15 are exact
+        // floats); chunks past the end have rows >= M, so a partial wave takes the other way
+        const int r0 = __builtin_amdgcn_readfirstlane(r[u]);
+        if (r0 == __shfl(r[u], 63, kWave)) {
+            m = (uint32_t)wave_max((float)m);
+            if (lane == 0) atomicMax(&rmax[r0], m);
+        } else if (valid) {
+            atomicMax(&rmax[r[u]], m);
+        }
+    }
+    __syncthreads();
+    // codes, outlier values at their ranks, scales and padding
+#pragma unroll
+    for (int u = 0; u < kOneChunks; ++u) {
+        if (tid + 1024 * u >= items) continue;
+        const int rr = r[u], cc = c[u];
+        const float inv = inv_scale(to_f32<DT>((uint16_t)rmax[rr]));
+        const uint32_t o = obits(cc);
+        *(u32x2*)(Xq + rr * xq_pitch + 8 * cc) = code_chunk<DT>(v[u], o, inv, true);
+        if (o) {
+            int32_t t = wrank[cc >> 2] + __popc(bits[cc >> 2] & ((1u << (8 * (cc & 3))) - 1u));
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if ((o >> j) & 1u) XO[rr * xo_pitch + t++] = (uint16_t)(v[u][j >> 1] >> (16 * (j & 1)));
+        }
+    }
+    if (tid < M) s_x[tid] = to_f32<DT>((uint16_t)rmax[tid]);
+    const int pad_c = (xq_pitch - K) / 8, pad_o = ((total + 31) & ~31) - total;
+    for (int e = tid; e < M * pad_c; e += 1024)
+        *(u32x2*)(Xq + (e / pad_c) * xq_pitch + K + 8 * (e % pad_c)) = u32x2{0u, 0u};
+    for (int e = tid; e < M * pad_o; e += 1024) XO[(e / pad_o) * xo_pitch + total + e % pad_o] = 0;
+}
+
 template <int DT, int HOLD, bool WRITE_O>
 static hipError_t code_rows_launch1(const XPassArgs& a, const uint32_t* bitmap, int32_t* O, int32_t* n_out,
                                     int64_t n_wo, hipStream_t stream) {
@@ -479,12 +610,24 @@ hipError_t launch_code_rows(const XPassArgs& a, const uint32_t* bitmap, int32_t*
     return code_rows_launch<BF16, false>(a, bitmap, O, n_out, n_wo, stream);
 }
 
-// Small-batch path: direct detect, then the row coding also writes O and n_O.
+// Small-batch path: one workgroup for at most kOneMaxElems elements, else direct detect,
+// then the row coding, which also writes O and n_O.
 hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, uint32_t* bitmap, hipStream_t stream) {
+    if (a.M > 0 && a.K > 0 && a.M * a.K <= kOneMaxElems) {
+        if (a.dt == F16)
+            xpass_one_kernel<F16><<<1, 1024, 0, stream>>>((const uint16_t*)a.X, (int)a.M, (int)a.K, a.tau, bitmap, O,
+                                                          n_out, a.Xq, (int)a.xq_pitch, a.s_x, (uint16_t*)a.XO,
+                                                          (int)a.xo_pitch);
+        else
+            xpass_one_kernel<BF16><<<1, 1024, 0, stream>>>((const uint16_t*)a.X, (int)a.M, (int)a.K, a.tau, bitmap, O,
+                                                           n_out, a.Xq, (int)a.xq_pitch, a.s_x, (uint16_t*)a.XO,
+                                                           (int)a.xo_pitch);
+        return hipGetLastError();
+    }
     if (a.K > 0) {
-        const unsigned g1 = (unsigned)ceil_div(a.K / 8, 256);
-        if (a.dt == F16) detect_direct_kernel<F16><<<g1, 256, 0, stream>>>((const uint16_t*)a.X, a.M, a.K, a.tau, bitmap);
-        else detect_direct_kernel<BF16><<<g1, 256, 0, stream>>>((const uint16_t*)a.X, a.M, a.K, a.tau, bitmap);
+        const unsigned g1 = (unsigned)ceil_div(a.K / 8, 64);
+        if (a.dt == F16) detect_direct_kernel<F16><<<g1, 64, 0, stream>>>((const uint16_t*)a.X, a.M, a.K, a.tau, bitmap);
+        else detect_direct_kernel<BF16><<<g1, 64, 0, stream>>>((const uint16_t*)a.X, a.M, a.K, a.tau, bitmap);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -45,7 +45,12 @@ def test_ragged_medium(dt):
 
 @pytest.mark.parametrize("M,K,N,dt", [(1, 16, 8, "fp16"), (1, 4096, 264, "bf16"), (16, 8192, 512, "bf16"),
                                       (64, 1040, 264, "fp16"), (65, 1040, 264, "bf16"), (33, 32784, 24, "fp16"),
-                                      (257, 272, 264, "fp16"), (513, 128, 8, "bf16"), (7, 32, 1032, "fp16")])
+                                      (257, 272, 264, "fp16"), (513, 128, 8, "bf16"), (7, 32, 1032, "fp16"),
+                                      # small batches: one-workgroup X pass (M*K <= 32768) with waves that
+                                      # straddle rows (K = 800: 100 chunks per row), at and just past its
+                                      # size limit, and the two-launch X pass
+                                      (40, 800, 136, "bf16"), (64, 512, 264, "fp16"), (64, 528, 264, "fp16"),
+                                      (40, 3200, 136, "bf16"), (64, 4096, 264, "bf16")])
 def test_edge_shapes(M, K, N, dt):
     _banner(f"edge {M}x{K}x{N} {dt}")
     x, w = _case(M, K, N, dt, n_out=2, seed=M + K + N)
