@@ -18,6 +18,10 @@
 // and s_w for the tile's rows and columns, loaded straight into LDS at the group's first
 // stage, before the stage's operand loads, so the counted wait and barrier that cover
 // stage kt+1 cover them too; two slots alternate between groups.
+// Persistent: one workgroup per compute unit works through its XCD's run of tiles; the K
+// stages run back to back across tile boundaries (a tile's last stages already load the
+// next tile's first operands), and a tile's epilogue stages Y through the slots of the
+// stage it consumed last while those loads are in flight.
 #include <type_traits>
 
 #include "common.hpp"
@@ -46,9 +50,9 @@ constexpr int kSubSteps = BK / 32;
 constexpr int kGroupM = 8;
 constexpr int kXcds = 8;
 constexpr int kYPitch = 32 * NJ + 8;             // epilogue staging row, 16-bit elements
-constexpr int kYStageBytes = 32 * MI * kYPitch * 2;
+constexpr int kYHalfBytes = 32 * kYPitch * 2;      // one 32-row half of a wave's outputs
 static_assert(kOperandBytes + kScaleBytes <= 160 * 1024, "LDS");
-static_assert(kWaves * kYStageBytes <= kOperandBytes, "epilogue LDS");
+static_assert(6 * kYHalfBytes <= kTileBytesA && 2 * kYHalfBytes <= kTileBytesB, "epilogue LDS");
 static_assert(kLoadsA + kLoadsB == 6, "the barrier's wait leaves the 6 loads of stage kt+2 in flight");
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -93,64 +97,86 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_group_kernel(GroupParams p) 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 1, wn = w & 1;
 
+    // ---- tiles of this workgroup: the XCD-contiguous run of tiles (grouped order) of the
+    // XCD the dispatcher places it on (ids congruent mod 8), strided by the number of
+    // workgroups on that XCD
     const int T = p.tiles_m * p.tiles_n;
-    const int bid = blockIdx.x;
+    const int bid = blockIdx.x, nwg = gridDim.x;
     const int xcd = bid % kXcds, local = bid / kXcds;
     const int per = T / kXcds, rem = T % kXcds;
-    const int t = xcd * per + (xcd < rem ? xcd : rem) + local;
-    const int in_group = kGroupM * p.tiles_n;
-    const int first_m = (t / in_group) * kGroupM;
-    const int gm = p.tiles_m - first_m < kGroupM ? p.tiles_m - first_m : kGroupM;
-    const int tm = first_m + (t % in_group) % gm;
-    const int tn = (t % in_group) / gm;
-    const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
+    const int x_start = xcd * per + (xcd < rem ? xcd : rem), x_cnt = per + (xcd < rem ? 1 : 0);
+    const int on_xcd = (nwg - xcd + kXcds - 1) / kXcds;
+    const int my_tiles = local < x_cnt ? (x_cnt - local + on_xcd - 1) / on_xcd : 0;
+    if (my_tiles == 0) return;  // the same for every wave of the workgroup
+    auto tile_origin = [&](int i, int64_t& m0, int64_t& n0) LLMINT8_INLINE {
+        const int t = x_start + local + i * on_xcd;
+        const int in_group = kGroupM * p.tiles_n;
+        const int first_m = (t / in_group) * kGroupM;
+        const int gm = p.tiles_m - first_m < kGroupM ? p.tiles_m - first_m : kGroupM;
+        m0 = (int64_t)(first_m + (t % in_group) % gm) * BM;
+        n0 = (int64_t)((t % in_group) / gm) * BN;
+    };
 
+    // ---- per-lane offsets, relative to a tile's first row: operand rows (one 128-byte
+    // line each, swizzled chunks) and the factor entries; rows past M or N lie past the
+    // resources and read zero
     const int wu = __builtin_amdgcn_readfirstlane(w);
     uint32_t a_off[kLoadsA], b_off[kLoadsB];
 #pragma unroll
     for (int j = 0; j < kLoadsA; ++j) {
         const int r = kRowsPerLoad * (kLoadsA * wu + j) + lane / kChunks;
-        const int c = (lane % kChunks) ^ swz(r);
-        const int64_t m = m0 + r < p.M ? m0 + r : p.M - 1;
-        a_off[j] = (uint32_t)((m - m0) * p.K + c * 16);
+        a_off[j] = (uint32_t)(r * p.K + (((lane % kChunks) ^ swz(r)) << 4));
     }
 #pragma unroll
     for (int j = 0; j < kLoadsB; ++j) {
         const int r = kRowsPerLoad * (kLoadsB * wu + j) + lane / kChunks;
-        const int c = (lane % kChunks) ^ swz(r);
-        const int64_t n = n0 + r < p.N ? n0 + r : p.N - 1;
-        b_off[j] = (uint32_t)((n - n0) * p.K + c * 16);
+        b_off[j] = (uint32_t)(r * p.K + (((lane % kChunks) ^ swz(r)) << 4));
     }
-    const int8_t* a_tile = p.Xq + m0 * p.K;
-    const int8_t* b_tile = p.Wq + n0 * p.K;
     const int nk = (int)(p.K / BK);  // K is a multiple of G >= 128
-    const int64_t rows_a = p.M - m0 < BM ? p.M - m0 : BM, rows_b = p.N - n0 < BN ? p.N - n0 : BN;
-    const __amdgpu_buffer_rsrc_t rsa = buffer_rsrc(a_tile, rows_a * p.K);
-    const __amdgpu_buffer_rsrc_t rsb = buffer_rsrc(b_tile, rows_b * p.K);
+    // Loads run two stages ahead, across tile boundaries: the resources of this tile and
+    // the next two are held; past the workgroup's last tile they are empty (every stage
+    // issues its loads, which then land zeros in slots no stage reads).
+    auto tile_rsrc = [&](int i, __amdgpu_buffer_rsrc_t& ra, __amdgpu_buffer_rsrc_t& rb) LLMINT8_INLINE {
+        int64_t m0 = 0, n0 = 0, rows_a = 0, rows_b = 0;
+        if (i < my_tiles) {
+            tile_origin(i, m0, n0);
+            rows_a = p.M - m0 < BM ? p.M - m0 : BM;
+            rows_b = p.N - n0 < BN ? p.N - n0 : BN;
+        }
+        ra = buffer_rsrc(p.Xq + m0 * p.K, rows_a * p.K);
+        rb = buffer_rsrc(p.Wq + n0 * p.K, rows_b * p.K);
+    };
+    __amdgpu_buffer_rsrc_t ra0, rb0, ra1, rb1, ra2, rb2;
+    tile_rsrc(0, ra0, rb0);
+    tile_rsrc(1, ra1, rb1);
+    tile_rsrc(2, ra2, rb2);
 
-    auto slot_a = [&](int kt) LLMINT8_INLINE { return smem + (kt % kSlotsA) * kTileBytesA; };
-    auto slot_b = [&](int kt) LLMINT8_INLINE { return smem + kSlotsA * kTileBytesA + (kt % kSlotsB) * kTileBytesB; };
-    auto issue_a = [&](int kt) LLMINT8_INLINE {
-        int8_t* As = slot_a(kt);
+    // global stage s sits in slot s % 3 of each operand; `d` = tiles ahead of the current one
+    auto slot_a = [&](int ss) LLMINT8_INLINE { return smem + ss * kTileBytesA; };
+    auto slot_b = [&](int ss) LLMINT8_INLINE { return smem + kSlotsA * kTileBytesA + ss * kTileBytesB; };
+    auto issue_ab = [&](int ss, int kt, int d) LLMINT8_INLINE {
+        const __amdgpu_buffer_rsrc_t rs_a = d == 0 ? ra0 : (d == 1 ? ra1 : ra2);
+        const __amdgpu_buffer_rsrc_t rs_b = d == 0 ? rb0 : (d == 1 ? rb1 : rb2);
+        int8_t* As = slot_a(ss);
+        int8_t* Bs = slot_b(ss);
 #pragma unroll
-        for (int j = 0; j < kLoadsA; ++j) load_lds16(rsa, a_off[j], kt * BK, As + (kLoadsA * wu + j) * 1024);
-    };
-    auto issue_b = [&](int kt) LLMINT8_INLINE {
-        int8_t* Bs = slot_b(kt);
+        for (int j = 0; j < kLoadsA; ++j) load_lds16(rs_a, a_off[j], kt * BK, As + (kLoadsA * wu + j) * 1024);
 #pragma unroll
-        for (int j = 0; j < kLoadsB; ++j) load_lds16(rsb, b_off[j], kt * BK, Bs + (kLoadsB * wu + j) * 1024);
+        for (int j = 0; j < kLoadsB; ++j) load_lds16(rs_b, b_off[j], kt * BK, Bs + (kLoadsB * wu + j) * 1024);
     };
-    // the factors of group g, one 64-entry load per wave: waves 0..3 the r of the tile's
-    // 256 rows, waves 4 and 5 the s_w of its 128 columns, waves 6 and 7 the same columns
-    // again (same values to the same place, so that every wave issues the same loads); rows
-    // and columns past the matrix read the last one (unused)
+    // the factors of group g of the current tile, one 64-entry load per wave: waves 0..3 the
+    // r of the tile's 256 rows, waves 4 and 5 the s_w of its 128 columns, waves 6 and 7 the
+    // same columns again (same values to the same place, so that every wave issues the same
+    // loads)
     const int cw = wu & 1;
-    const uint32_t r_off = (uint32_t)(((m0 + 64 * (wu & 3) + lane < p.M ? m0 + 64 * (wu & 3) + lane : p.M - 1) - m0) * 4);
-    const uint32_t c_off = (uint32_t)(((n0 + 64 * cw + lane < p.N ? n0 + 64 * cw + lane : p.N - 1) - n0) * p.ng * 4);
+    const uint32_t r_off = (uint32_t)((64 * (wu & 3) + lane) * 4);
+    const uint32_t c_off = (uint32_t)((64 * cw + lane) * p.ng * 4);
+    int64_t cm0 = 0, cn0 = 0;  // the current tile's origin
+    tile_origin(0, cm0, cn0);
     auto issue_scales = [&](int g) LLMINT8_INLINE {
-        // buffer resources over this group's factors of the tile (32-bit offsets)
-        const __amdgpu_buffer_rsrc_t rs = wu < 4 ? buffer_rsrc(p.rg + (int64_t)g * p.M + m0, rows_a * 4)
-                                                 : buffer_rsrc(p.s_w + n0 * p.ng + g, rows_b * p.ng * 4);
+        const int64_t rows_a = p.M - cm0 < BM ? p.M - cm0 : BM, rows_b = p.N - cn0 < BN ? p.N - cn0 : BN;
+        const __amdgpu_buffer_rsrc_t rs = wu < 4 ? buffer_rsrc(p.rg + (int64_t)g * p.M + cm0, rows_a * 4)
+                                                 : buffer_rsrc(p.s_w + cn0 * p.ng + g, rows_b * p.ng * 4);
         float* dst = wu < 4 ? rbuf + (g & 1) * BM + 64 * wu : cbuf + (g & 1) * BN + 64 * cw;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)dst, 4, (int)(wu < 4 ? r_off : c_off), 0, 0, 0);
     };
@@ -159,9 +185,9 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_group_kernel(GroupParams p) 
     int rd[kSubSteps];
 #pragma unroll
     for (int u = 0; u < kSubSteps; ++u) rd[u] = rl * BK + (((2 * u + h) ^ swz(rl)) << 4);
-    auto read_frags = [&](int kt, int u, v4i (&fa)[MI], v4i (&fb)[NJ]) LLMINT8_INLINE {
-        const int8_t* As = slot_a(kt) + wm * (32 * MI) * BK + rd[u];
-        const int8_t* Bs = slot_b(kt) + wn * (32 * NJ) * BK + rd[u];
+    auto read_frags = [&](int ss, int u, v4i (&fa)[MI], v4i (&fb)[NJ]) LLMINT8_INLINE {
+        const int8_t* As = slot_a(ss) + wm * (32 * MI) * BK + rd[u];
+        const int8_t* Bs = slot_b(ss) + wn * (32 * NJ) * BK + rd[u];
         fa[0] = *(const v4i*)As;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) fb[j] = *(const v4i*)(Bs + j * 32 * BK);
@@ -171,10 +197,6 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_group_kernel(GroupParams p) 
 
     v16i acc[MI][NJ];
     v16f accf[MI][NJ];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) accf[i][j] = v16f{};
     // ZERO: the group's first products, which start from 0 instead of the previous group's
     // partial (so the partials are never cleared)
     auto mfma_rows = [&](const v4i (&fa)[MI], const v4i (&fb)[NJ], int i0, int i1, auto zero_tag) LLMINT8_INLINE {
@@ -213,30 +235,29 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_group_kernel(GroupParams p) 
         }
     };
 
-    // One K stage: sub-steps 0..2 run their 8 MFMAs under the next sub-step's 6 LDS reads
-    // and, in sub-step 0 of a group's first stage, the loads of the group's factors, in
-    // sub-step 1 the global loads of stage kt+2 (both operands, into the slots stage kt-1
-    // freed); sub-step 3 runs 2 MFMAs, waits for stage kt+1 and meets the other waves at the
-    // barrier, then reads stage kt+1's first operands under its other 6.  STEADY: stage kt+2
-    // exists.  FIRST: the group's first stage.
+    // One K stage (global stage in slot ss, stage kt of its tile): sub-steps 0..2 run their 8
+    // MFMAs under the next sub-step's 6 LDS reads and, in sub-step 0 of a group's first
+    // stage, the loads of the group's factors, in sub-step 1 the global loads two stages
+    // ahead (both operands, into the slots the previous stage freed); sub-step 3 runs 2
+    // MFMAs, waits for the next stage and meets the other waves at the barrier, then reads
+    // the next stage's first operands under its other 6.  FIRST: the group's first stage.
     v4i fa[2][MI], fb[2][NJ];
-    auto stage = [&](int kt, int g, auto steady_tag, auto first_tag) LLMINT8_INLINE {
-        constexpr bool STEADY = decltype(steady_tag)::value;
+    auto stage = [&](int ss, int kt, int g, auto first_tag) LLMINT8_INLINE {
         constexpr bool FIRST = decltype(first_tag)::value;
-        const bool next = STEADY || kt + 1 < nk;
+        // (readfirstlane: the compiler then knows this, and so the resources, are uniform)
+        const int d = __builtin_amdgcn_readfirstlane(kt + 2 < nk ? 0 : (kt + 2 < 2 * nk ? 1 : 2));
+        const int k2 = kt + 2 - d * nk;
+        const int s1 = ss == 2 ? 0 : ss + 1, s2 = ss == 0 ? 2 : ss - 1;
 #pragma unroll
         for (int u = 0; u < kSubSteps - 1; ++u) {
             const int cur = u & 1, nxt = cur ^ 1;
             __builtin_amdgcn_s_waitcnt(0xC07F);
             if (u == 0 && FIRST) issue_scales(g);
-            if (u == 1 && STEADY) {
-                issue_a(kt + 2);
-                issue_b(kt + 2);
-            }
-            read_frags(kt, u + 1, fa[nxt], fb[nxt]);
+            if (u == 1) issue_ab(s2, k2, d);
+            read_frags(ss, u + 1, fa[nxt], fb[nxt]);
             if (u == 0) mfma_rows(fa[cur], fb[cur], 0, MI, std::integral_constant<bool, FIRST>{});
             else mfma_rows(fa[cur], fb[cur], 0, MI, std::false_type{});
-            if (u == 1 && STEADY) {
+            if (u == 1) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     if (q < 2) __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);
@@ -255,56 +276,76 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_group_kernel(GroupParams p) 
         }
         mfma_rows(fa[1], fb[1], 0, 1, std::false_type{});
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (STEADY) LLMINT8_GROUP_WAIT_BARRIER(6);  // stage kt+2 may stay in flight
-        else LLMINT8_GROUP_WAIT_BARRIER(0);
-        if (next) read_frags(kt + 1, 0, fa[0], fb[0]);
+        LLMINT8_GROUP_WAIT_BARRIER(6);  // the loads two stages ahead may stay in flight
+        read_frags(s1, 0, fa[0], fb[0]);
         mfma_rows(fa[1], fb[1], 1, MI, std::false_type{});
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
-    auto run_stage = [&](int kt, int g, auto first_tag) LLMINT8_INLINE {
-        if (kt + 2 < nk) stage(kt, g, std::true_type{}, first_tag);
-        else stage(kt, g, std::false_type{}, first_tag);
+
+    // ---- epilogue of the current tile: Y = RN_T(sums), one 32-row half per wave at a time,
+    // staged in the A and B slots of the stage just consumed (A: waves 0-5, B: waves 6, 7),
+    // written as 16-byte row segments
+    auto epilogue = [&](int ss) LLMINT8_INLINE {
+        uint16_t* ys = (uint16_t*)(w < 6 ? slot_a(ss) + w * kYHalfBytes : slot_b(ss) + (w - 6) * kYHalfBytes);
+        const int64_t wm0 = cm0 + wm * (32 * MI), wn0 = cn0 + wn * (32 * NJ);
+        constexpr int kLanesPerRow = 32 * NJ / 8;  // 16-byte segments per staged row
+        constexpr int kRowsPerIter = 64 / kLanesPerRow;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    ys[(8 * (e >> 2) + 4 * h + (e & 3)) * kYPitch + 32 * j + rl] = from_f32<DT>(accf[i][j][e]);
+#pragma unroll
+            for (int it = 0; it < 32 / kRowsPerIter; ++it) {
+                const int row = it * kRowsPerIter + lane / kLanesPerRow, ch = lane % kLanesPerRow;
+                const u32x4 v = *(const u32x4*)(ys + row * kYPitch + ch * 8);
+                const int64_t m = wm0 + 32 * i + row, n = wn0 + ch * 8;
+                if (m < p.M && n < p.N) *(u32x4*)(p.Y + m * p.N + n) = v;
+            }
+        }
     };
 
-    // prologue: stages 0 and 1 in flight; wait for stage 0
-    issue_a(0);
-    issue_b(0);
-    if (nk > 1) {
-        issue_a(1);
-        issue_b(1);
-        LLMINT8_GROUP_WAIT_BARRIER(6);
-    } else {
-        LLMINT8_GROUP_WAIT_BARRIER(0);
-    }
+    // prologue: global stages 0 and 1 in flight; wait for stage 0
+    issue_ab(0, 0, 0);
+    issue_ab(1, nk > 1 ? 1 : 0, nk > 1 ? 0 : 1);
+    LLMINT8_GROUP_WAIT_BARRIER(6);
     read_frags(0, 0, fa[0], fb[0]);
-    for (int g = 0, kt = 0; g < (int)p.ng; ++g) {
-        run_stage(kt++, g, std::true_type{});
-        for (int s = 1; s < p.gs; ++s) run_stage(kt++, g, std::false_type{});
-        fold(g);
+    int ss = 0;
+    for (int ti = 0; ti < my_tiles; ++ti) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) accf[i][j] = v16f{};
+        int kt = 0;
+        for (int g = 0; g < (int)p.ng; ++g) {
+            stage(ss, kt++, g, std::true_type{});
+            ss = ss == 2 ? 0 : ss + 1;
+            for (int s = 1; s < p.gs; ++s) {
+                stage(ss, kt++, g, std::false_type{});
+                ss = ss == 2 ? 0 : ss + 1;
+            }
+            fold(g);
+        }
+        // the stage just consumed sits in the slot before ss; no wave reads it any more
+        epilogue(ss == 0 ? 2 : ss - 1);
+        if (ti + 1 < my_tiles) {
+            ra0 = ra1;
+            rb0 = rb1;
+            ra1 = ra2;
+            rb1 = rb2;
+            tile_rsrc(ti + 3, ra2, rb2);
+            tile_origin(ti + 1, cm0, cn0);
+            // every wave is done with its staging area (the next stage's loads go there)
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_s_barrier();
+        }
     }
-
-    // ---- epilogue: Y = RN_T(sums), staged per wave in LDS, written as 16-byte row segments
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    uint16_t* ys = (uint16_t*)(smem + w * kYStageBytes);
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                ys[(32 * i + 8 * (e >> 2) + 4 * h + (e & 3)) * kYPitch + 32 * j + rl] = from_f32<DT>(accf[i][j][e]);
-    const int64_t wm0 = m0 + wm * (32 * MI), wn0 = n0 + wn * (32 * NJ);
-    constexpr int kLanesPerRow = 32 * NJ / 8;        // 16-byte segments per staged row
-    constexpr int kRowsPerIter = 64 / kLanesPerRow;
-#pragma unroll 4
-    for (int it = 0; it < 32 * MI / kRowsPerIter; ++it) {
-        const int row = it * kRowsPerIter + lane / kLanesPerRow, ch = lane % kLanesPerRow;
-        const u32x4 v = *(const u32x4*)(ys + row * kYPitch + ch * 8);
-        const int64_t m = wm0 + row, n = wn0 + ch * 8;
-        if (m < p.M && n < p.N) *(u32x4*)(p.Y + m * p.N + n) = v;
-    }
+    // no load into this workgroup's LDS may outlive it
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ---- X pass: the group-wise codes of X.  Row groups never cross rows (G divides K), so X
@@ -455,7 +496,13 @@ hipError_t launch_gemm_group(int dt, const int8_t* Xq, const float* rg, const in
     p.Y = (uint16_t*)Y;
     p.tiles_m = (int)ceil_div(M, BM);
     p.tiles_n = (int)ceil_div(N, BN);
-    const unsigned grid = (unsigned)(p.tiles_m * p.tiles_n);
+    // persistent: one workgroup per compute unit (its LDS admits one), at most one per tile
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int64_t T = (int64_t)p.tiles_m * p.tiles_n;
+    const unsigned grid = (unsigned)(T < cus ? T : (cus > 0 ? cus : 1));
     if (dt == F16) gemm_group_kernel<F16><<<grid, 64 * kWaves, 0, stream>>>(p);
     else gemm_group_kernel<BF16><<<grid, 64 * kWaves, 0, stream>>>(p);
     return hipGetLastError();

@@ -69,6 +69,19 @@ def test_group_parity(dt, M, K, N, G):
     _run(x, w, dt, G)
 
 
+@pytest.mark.parametrize("K,G,dt", [(128, 128, "fp16"), (256, 128, "bf16"), (384, 128, "fp16")])
+def test_group_several_tiles_per_workgroup(K, G, dt):
+    # 17 x 17 = 289 tiles of 256 x 128 on 256 workgroups: some take two tiles, and the
+    # operand loads run one (K = 128: one stage per tile) or two tiles ahead; ragged in M
+    # and N; rows sampled in the first, a middle and the last row tile
+    M, N = 4200, 2056
+    print(f"\n[case] group several tiles per workgroup {dt} {M}x{K}x{N} G={G}", flush=True)
+    x, w = _case(M, K, N, dt, seed=K + 1)
+    rng = np.random.default_rng(K)
+    rows = np.unique(np.concatenate([[0, 255, 256, 2047, 4095, 4096, M - 1], rng.integers(0, M, 5)]))
+    _run(x, w, dt, G, rows=rows)
+
+
 def test_group_equals_vectorwise_at_one_group():
     # G = K: one scale per row and column, the vector-wise code; with no outlier above the
     # threshold the vector-wise path's Y is RN_T(RN32(RN32(C * r) * c)), the same as one group
