@@ -40,7 +40,7 @@ int check_shape(int64_t M, int64_t K, int64_t N, int dtype) {
 int check_threshold(float t) { return (isnan(t) || t < 0.0f) ? LLMINT8_EINVAL : LLMINT8_OK; }
 
 struct Layout {
-    size_t xq, xq_pitch, s_x, n_outliers, outliers, xo, xo_pitch, wo, bitmap, partial, total;
+    size_t xq, xq_pitch, s_x, n_outliers, outliers, xo, xo_pitch, wo, bitmap, partial, pmax, total;
 };
 
 Layout make_layout(int64_t M, int64_t K, int64_t N) {
@@ -66,6 +66,8 @@ Layout make_layout(int64_t M, int64_t K, int64_t N) {
     off = align_up(off + 4 * kw);
     L.partial = off;
     off = align_up(off + 4 * kw * (size_t)detect_row_blocks(M));
+    L.pmax = off;  // small batches: per row and 512-column slab, the slab's row maximum
+    off = align_up(off + (small_batch(M, K) ? 4 * m * (size_t)ceil_div(K, 512) : 0));
     L.total = off;
     return L;
 }
@@ -95,7 +97,7 @@ int run_xpass(const void* X, int64_t M, int64_t K, int dtype, float tau, const i
     a.s_x = (float*)(ws + L.s_x);
     a.XO = ws + L.xo;
     a.xo_pitch = (int64_t)L.xo_pitch;
-    if (small_batch(M, K)) return hip_status(launch_xpass_small(a, O, nO, bitmap, st));
+    if (small_batch(M, K)) return hip_status(launch_xpass_small(a, O, nO, bitmap, (uint32_t*)(ws + L.pmax), st));
     hipError_t e = launch_detect(dtype, X, M, K, tau, partial, st);
     if (e == hipSuccess) e = launch_compact(M, K, partial, bitmap, O, nO, st);
     if (e == hipSuccess) {

@@ -53,7 +53,10 @@ struct XPassArgs {
 };
 hipError_t launch_code_rows(const XPassArgs& a, const uint32_t* bitmap, int32_t* O, int32_t* n_out,
                             hipStream_t stream);
-hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, uint32_t* bitmap, hipStream_t stream);
+// pmax (M x ceil(K/512) words of scratch): per row and 512-column slab, the slab's
+// maximum over its non-outlier columns
+hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, uint32_t* bitmap, uint32_t* pmax,
+                              hipStream_t stream);
 
 // ---- products + epilogue
 struct GemmArgs {

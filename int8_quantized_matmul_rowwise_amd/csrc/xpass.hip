@@ -184,48 +184,11 @@ hipError_t launch_compact(int64_t M, int64_t K, const uint32_t* partial, uint32_
 }  // namespace llmint8
 
 // ---------------------------------------------------------------------------
-// Row coding (both paths) and the small-batch detection.  A small batch (M <= kSmallM
-// rows, K <= kSmallK) takes two launches: detect_direct -- one thread per 8-column chunk
-// scans all M rows and writes its bits of the bitmap directly (no row blocks, hence no
-// partials and no compaction launch) -- then code_rows, whose workgroup 0 also writes O
-// and n_O.  The tiled path runs detect (row-block partials), compact, then code_rows.
+// Row coding of the tiled path (after detect and compact), and the small-batch X pass
+// (M <= kSmallM rows, K <= kSmallK): one workgroup for at most 64 KB of X, else two
+// launches over 512-column slabs.
 namespace llmint8 {
 
-
-// One wave per workgroup: the few workgroups a small X has then spread over more compute
-// units (K = 8192: 16 instead of 4).
-template <int DT>
-__global__ __launch_bounds__(64) void detect_direct_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
-                                                           float tau, uint32_t* __restrict__ bitmap) {
-    const int lane = threadIdx.x;
-    const int64_t c = (int64_t)blockIdx.x * 64 + threadIdx.x;  // 8-column chunk
-    const int64_t nch = K / 8;
-    uint32_t mask = 0;
-    if (c < nch) {
-        const uint16_t* col = X + c * 8;
-        int64_t r = 0;
-        for (; r + 8 <= M; r += 8) {
-            u32x4 v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = *(const u32x4*)(col + (r + u) * K);
-#pragma unroll
-            for (int u = 0; u < 8; ++u)
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    mask |= (__builtin_fabsf(to_f32<DT>((uint16_t)(v[u][j >> 1] >> (16 * (j & 1))))) > tau ? 1u : 0u) << j;
-        }
-        for (; r < M; ++r) {
-            const u32x4 v = *(const u32x4*)(col + r * K);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                mask |= (__builtin_fabsf(to_f32<DT>((uint16_t)(v[j >> 1] >> (16 * (j & 1))))) > tau ? 1u : 0u) << j;
-        }
-    }
-    uint32_t word = mask << (8 * (lane & 3));
-    word |= __shfl_xor(word, 1, kWave);
-    word |= __shfl_xor(word, 2, kWave);
-    if ((lane & 3) == 0 && c < nch) bitmap[c >> 2] = word;  // K % 16 == 0: a word's chunks exist together
-}
 
 // ---- per-chunk arithmetic of the row coding (a chunk: 8 consecutive 16-bit elements in
 // four dwords; o: its 8 outlier bits; any: some lane of the wave has o != 0, wave-uniform)
@@ -290,9 +253,8 @@ __device__ __forceinline__ u32x2 code_chunk(const u32x4& x, uint32_t o, float in
 // gives the rank t of every outlier column.  HOLD > 0: a row stays in registers (HOLD
 // 16-byte chunks per thread, K <= 2048 * HOLD) between its max and its coding, else each
 // row is read twice.  (A second register set, to load the next row while one is coded,
-// costs more in occupancy than it gains.)  WRITE_O: the workgroup of row 0 writes O and
-// n_O (the small-batch path has no compaction launch).
-template <int DT, int HOLD, bool WRITE_O>
+// costs more in occupancy than it gains.)
+template <int DT, int HOLD>
 __global__ __launch_bounds__(256) void code_rows_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                         const uint32_t* __restrict__ bitmap, int32_t* __restrict__ O,
                                                         int32_t* __restrict__ n_out, int8_t* __restrict__ Xq,
@@ -410,11 +372,7 @@ __global__ __launch_bounds__(256) void code_rows_kernel(const uint16_t* __restri
                 int32_t r = wrank[c >> 2] + __popc(bits[c >> 2] & ((1u << (8 * (c & 3))) - 1u));
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    if ((o >> j) & 1u) {
-                        xo[r] = (uint16_t)(x[j >> 1] >> (16 * (j & 1)));
-                        if (WRITE_O && i == 0) O[r] = (int32_t)(8 * c + j);
-                        ++r;
-                    }
+                    if ((o >> j) & 1u) xo[r++] = (uint16_t)(x[j >> 1] >> (16 * (j & 1)));
                 }
             }
         };
@@ -437,7 +395,6 @@ __global__ __launch_bounds__(256) void code_rows_kernel(const uint16_t* __restri
         if (HOLD > 0 && i != g) load_row(va, i);
         process(va, i, par);
     }
-    if (WRITE_O && g == 0 && tid == 0) *n_out = total;
 }
 
 // The whole small-batch X pass in one workgroup, for M * K <= kOneMaxElems (64 KB of X:
@@ -569,7 +526,172 @@ __global__ __launch_bounds__(1024) void xpass_one_kernel(const uint16_t* __restr
     for (int e = tid; e < M * pad_o; e += 1024) XO[(e / pad_o) * xo_pitch + total + e % pad_o] = 0;
 }
 
-template <int DT, int HOLD, bool WRITE_O>
+// The small-batch X pass past kOneMaxElems, in two wide launches over 512-column slabs
+// (64 chunks of 8 columns).  M <= 64 rows, so the workgroup of a slab sees every row of its
+// columns: which of them are outlier columns is known there exactly, and so are its rows'
+// maxima over the other columns.
+//   detect_slab (one workgroup of 16 waves per slab, 1 to 4 rows per wave held in
+//     registers): the slab's bitmap words and, per row, the slab's largest magnitude
+//     pattern over its non-outlier columns (pmax);
+//   code_slab (one workgroup per slab and 4 rows, a wave per row): the rows' maxima (max
+//     over the slabs' pmax), the slab's outlier ranks (popcounts of the words before it, a
+//     scan within it), its part of O, n_O (slab 0), then the codes, X_O and the padding.
+// Both read X (the second time mostly from the cache); together they replace a detection
+// launch with too few threads to hide its latency and a one-workgroup-per-row coding.
+
+// A raw buffer resource over [base, base + bytes): loads past the end read 0, so the slab
+// kernels issue every load unconditionally and their waits count exactly.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+template <int DT, int RPW>
+__global__ __launch_bounds__(1024) void detect_slab_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                           float tau, uint32_t* __restrict__ bitmap,
+                                                           uint32_t* __restrict__ pmax, int64_t nslab) {
+    // 16 waves; lane: chunk c of the slab; wave w: rows w, w + 16, ... (RPW of them, M <=
+    // 16 RPW).  Rows past M repeat the last row, which changes neither the outlier bits nor
+    // a stored maximum.
+    __shared__ uint32_t omask[64];
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t c = (int64_t)blockIdx.x * 64 + lane, C = K / 8;
+    const bool live = c < C;
+    const uint16_t* col = X + (live ? c : C - 1) * 8;
+    u32x4 v[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int64_t r = w + 16 * i;
+        v[i] = *(const u32x4*)(col + (r < M ? r : M - 1) * K);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load in flight before the first use
+    if (threadIdx.x < 64) omask[threadIdx.x] = 0;
+    __syncthreads();
+    // the chunk's outlier bits: |x| > tau in any row, compared in fp32
+    uint32_t mask = 0;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            mask |= (__builtin_fabsf(to_f32<DT>((uint16_t)(v[i][j >> 1] >> (16 * (j & 1))))) > tau ? 1u : 0u) << j;
+    if (mask && live) atomicOr(&omask[lane], mask);
+    __syncthreads();
+    mask = omask[lane];
+    if (w == 0) {
+        uint32_t word = mask << (8 * (lane & 3));
+        word |= __shfl_xor(word, 1, kWave);
+        word |= __shfl_xor(word, 2, kWave);
+        // a word's first chunk exists whenever the word does (K % 8 == 0)
+        if ((lane & 3) == 0 && live) bitmap[c >> 2] = word;
+    }
+    // per row, the slab's maximum magnitude pattern over the non-outlier columns
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const u16x2 mb = absmax_bits(u16x2{0, 0}, v[i], mask, true);
+        uint32_t m = live ? (mb[0] > mb[1] ? mb[0] : mb[1]) : 0u;
+        m = (uint32_t)wave_max((float)m);  // patterns below 2^15 are exact floats
+        const int64_t r = w + 16 * i;
+        if (lane == 0 && r < M) pmax[r * nslab + blockIdx.x] = m;
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void code_slab_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
+                                                        const uint32_t* __restrict__ bitmap,
+                                                        const uint32_t* __restrict__ pmax, int64_t nslab,
+                                                        int32_t* __restrict__ O, int32_t* __restrict__ n_out,
+                                                        int8_t* __restrict__ Xq, int64_t xq_pitch,
+                                                        float* __restrict__ s_x, uint16_t* __restrict__ XO,
+                                                        int64_t xo_pitch) {
+    __shared__ float inv_s[4];
+    __shared__ int32_t wr[16];
+    __shared__ uint32_t wb[16];
+    __shared__ int32_t tot;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int64_t sl = blockIdx.x, C = K / 8, Cp = xq_pitch / 8, Kw = ceil_div(K, 32);
+    const int64_t c = sl * 64 + lane, r = (int64_t)blockIdx.y * 4 + w;  // this thread's chunk and row
+    const bool live = c < C, row = r < M;
+    // every load first (rows past M and chunks past K read 0): the chunk, row r's slab
+    // partials (nslab <= 64), and in wave 0 the bitmap (Kw <= 1024 words)
+    const __amdgpu_buffer_rsrc_t xr = span_rsrc(X + (row ? r : 0) * K, row ? 2 * K : 0);
+    const __amdgpu_buffer_rsrc_t pr = span_rsrc(pmax + (row ? r : 0) * nslab, row ? 4 * nslab : 0);
+    const __amdgpu_buffer_rsrc_t br = span_rsrc(bitmap, 4 * Kw);
+    const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)(16 * c), 0, 0));
+    uint32_t m = __builtin_amdgcn_raw_buffer_load_b32(pr, (uint32_t)(4 * lane), 0, 0);
+    uint32_t bw[16], wd = 0;
+    if (w == 0) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) bw[q] = __builtin_amdgcn_raw_buffer_load_b32(br, (uint32_t)(4 * (lane + 64 * q)), 0, 0);
+        wd = __builtin_amdgcn_raw_buffer_load_b32(br, (uint32_t)(4 * (16 * sl + lane)), 0, 0);
+    }
+    // wave w: row r's maximum over the slabs' partials, and its factor
+    {
+        m = lane < nslab ? m : 0u;
+        m = (uint32_t)wave_max((float)m);
+        if (lane == 0) {
+            const float sv = to_f32<DT>((uint16_t)m);
+            inv_s[w] = inv_scale(sv);
+            if (row && sl == 0) s_x[r] = sv;
+        }
+    }
+    // wave 0: outlier columns before the slab and in all, the slab's 16 word ranks, its part
+    // of O, and n_O
+    if (w == 0) {
+        int32_t before = 0, all = 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int32_t pc = __popc(bw[q]);
+            all += pc;
+            before += lane + 64 * q < 16 * sl ? pc : 0;
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            all += __shfl_xor(all, off, kWave);
+            before += __shfl_xor(before, off, kWave);
+        }
+        const int64_t wi = 16 * sl + lane;
+        wd = lane < 16 ? wd : 0u;
+        const int32_t cnt = __popc(wd);
+        int32_t incl = cnt;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const int32_t t = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += t;
+        }
+        if (lane < 16) {
+            wr[lane] = before + incl - cnt;
+            wb[lane] = wd;
+            if (blockIdx.y == 0) {
+                int32_t t = before + incl - cnt;
+                for (uint32_t b = wd; b; b &= b - 1) O[t++] = (int32_t)(32 * wi + __ffs(b) - 1);
+            }
+        }
+        if (lane == 0) {
+            tot = all;
+            if (sl == 0 && blockIdx.y == 0) *n_out = all;
+        }
+    }
+    __syncthreads();
+    const int32_t total = tot, P = (total + 31) & ~31;
+    if (row) {
+        if (live) {
+            wd = wb[(c >> 2) - 16 * sl];
+            const uint32_t o = (wd >> (8 * (c & 3))) & 0xffu;
+            *(u32x2*)(Xq + r * xq_pitch + 8 * c) = code_chunk<DT>(v, o, inv_s[w], o != 0u);
+            if (o) {
+                int32_t t = wr[(c >> 2) - 16 * sl] + __popc(wd & ((1u << (8 * (c & 3))) - 1u));
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if ((o >> j) & 1u) XO[r * xo_pitch + t++] = (uint16_t)(v[j >> 1] >> (16 * (j & 1)));
+            }
+        } else if (c < Cp) {
+            *(u32x2*)(Xq + r * xq_pitch + 8 * c) = u32x2{0u, 0u};
+        }
+        if (sl == 0)
+            for (int32_t t = total + lane; t < P; t += 64) XO[r * xo_pitch + t] = 0;
+    }
+}
+
+template <int DT, int HOLD>
 static hipError_t code_rows_launch1(const XPassArgs& a, const uint32_t* bitmap, int32_t* O, int32_t* n_out,
                                     int64_t n_wo, hipStream_t stream) {
     // persistent row workgroups: as many as fit on the device at once (at most M)
@@ -578,13 +700,13 @@ static hipError_t code_rows_launch1(const XPassArgs& a, const uint32_t* bitmap, 
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, code_rows_kernel<DT, HOLD, WRITE_O>, 256, lds);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, code_rows_kernel<DT, HOLD>, 256, lds);
     if (e != hipSuccess) return e;
     int64_t groups = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     groups = groups < a.M ? groups : a.M;
     const unsigned grid = (unsigned)(n_wo + groups);
     if (grid == 0) return hipSuccess;
-    code_rows_kernel<DT, HOLD, WRITE_O><<<grid, 256, lds, stream>>>(
+    code_rows_kernel<DT, HOLD><<<grid, 256, lds, stream>>>(
         (const uint16_t*)a.X, a.M, a.K, bitmap, O, n_out, a.Xq, a.xq_pitch, a.s_x, (uint16_t*)a.XO, a.xo_pitch, a.Wq,
         a.N, (uint16_t*)a.WO, n_wo, groups);
     return hipGetLastError();
@@ -592,13 +714,13 @@ static hipError_t code_rows_launch1(const XPassArgs& a, const uint32_t* bitmap, 
 
 // The register hold is sized to the row (16-byte chunks per thread of 256): fewer
 // registers per thread leave room for more workgroups per CU.
-template <int DT, bool WRITE_O>
+template <int DT>
 static hipError_t code_rows_launch(const XPassArgs& a, const uint32_t* bitmap, int32_t* O, int32_t* n_out,
                                    int64_t n_wo, hipStream_t stream) {
-    if (a.K <= 2048 * 4) return code_rows_launch1<DT, 4, WRITE_O>(a, bitmap, O, n_out, n_wo, stream);
-    if (a.K <= 2048 * 8) return code_rows_launch1<DT, 8, WRITE_O>(a, bitmap, O, n_out, n_wo, stream);
-    if (a.K <= 2048 * 16) return code_rows_launch1<DT, 16, WRITE_O>(a, bitmap, O, n_out, n_wo, stream);
-    return code_rows_launch1<DT, 0, WRITE_O>(a, bitmap, O, n_out, n_wo, stream);
+    if (a.K <= 2048 * 4) return code_rows_launch1<DT, 4>(a, bitmap, O, n_out, n_wo, stream);
+    if (a.K <= 2048 * 8) return code_rows_launch1<DT, 8>(a, bitmap, O, n_out, n_wo, stream);
+    if (a.K <= 2048 * 16) return code_rows_launch1<DT, 16>(a, bitmap, O, n_out, n_wo, stream);
+    return code_rows_launch1<DT, 0>(a, bitmap, O, n_out, n_wo, stream);
 }
 
 // Big path: after detect + compact (which wrote the bitmap, O and n_O).
@@ -606,33 +728,49 @@ hipError_t launch_code_rows(const XPassArgs& a, const uint32_t* bitmap, int32_t*
                             hipStream_t stream) {
     const int64_t n_wo = a.Wq ? ceil_div(a.N, 64) : 0;
     if (a.M + n_wo == 0) return hipSuccess;
-    if (a.dt == F16) return code_rows_launch<F16, false>(a, bitmap, O, n_out, n_wo, stream);
-    return code_rows_launch<BF16, false>(a, bitmap, O, n_out, n_wo, stream);
+    if (a.dt == F16) return code_rows_launch<F16>(a, bitmap, O, n_out, n_wo, stream);
+    return code_rows_launch<BF16>(a, bitmap, O, n_out, n_wo, stream);
 }
 
-// Small-batch path: one workgroup for at most kOneMaxElems elements, else direct detect,
-// then the row coding, which also writes O and n_O.
-hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, uint32_t* bitmap, hipStream_t stream) {
-    if (a.M > 0 && a.K > 0 && a.M * a.K <= kOneMaxElems) {
+// Small-batch path (M > 0): one workgroup for at most kOneMaxElems elements, else the
+// slab detection and the slab coding.  K = 0 takes the coding launch alone (one slab
+// workgroup per 4 rows), which writes s_x = 0 and n_O = 0.
+hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, uint32_t* bitmap, uint32_t* pmax,
+                              hipStream_t stream) {
+    const uint16_t* x = (const uint16_t*)a.X;
+    if (a.K > 0 && a.M * a.K <= kOneMaxElems) {
         if (a.dt == F16)
-            xpass_one_kernel<F16><<<1, 1024, 0, stream>>>((const uint16_t*)a.X, (int)a.M, (int)a.K, a.tau, bitmap, O,
-                                                          n_out, a.Xq, (int)a.xq_pitch, a.s_x, (uint16_t*)a.XO,
-                                                          (int)a.xo_pitch);
+            xpass_one_kernel<F16><<<1, 1024, 0, stream>>>(x, (int)a.M, (int)a.K, a.tau, bitmap, O, n_out, a.Xq,
+                                                          (int)a.xq_pitch, a.s_x, (uint16_t*)a.XO, (int)a.xo_pitch);
         else
-            xpass_one_kernel<BF16><<<1, 1024, 0, stream>>>((const uint16_t*)a.X, (int)a.M, (int)a.K, a.tau, bitmap, O,
-                                                           n_out, a.Xq, (int)a.xq_pitch, a.s_x, (uint16_t*)a.XO,
-                                                           (int)a.xo_pitch);
+            xpass_one_kernel<BF16><<<1, 1024, 0, stream>>>(x, (int)a.M, (int)a.K, a.tau, bitmap, O, n_out, a.Xq,
+                                                           (int)a.xq_pitch, a.s_x, (uint16_t*)a.XO, (int)a.xo_pitch);
         return hipGetLastError();
     }
-    if (a.K > 0) {
-        const unsigned g1 = (unsigned)ceil_div(a.K / 8, 64);
-        if (a.dt == F16) detect_direct_kernel<F16><<<g1, 64, 0, stream>>>((const uint16_t*)a.X, a.M, a.K, a.tau, bitmap);
-        else detect_direct_kernel<BF16><<<g1, 64, 0, stream>>>((const uint16_t*)a.X, a.M, a.K, a.tau, bitmap);
+    const int64_t nslab = ceil_div(a.K / 8, 64);
+    if (nslab > 0) {
+        const unsigned g1 = (unsigned)nslab;
+        if (a.dt == F16) {
+            if (a.M <= 16) detect_slab_kernel<F16, 1><<<g1, 1024, 0, stream>>>(x, a.M, a.K, a.tau, bitmap, pmax, nslab);
+            else if (a.M <= 32) detect_slab_kernel<F16, 2><<<g1, 1024, 0, stream>>>(x, a.M, a.K, a.tau, bitmap, pmax, nslab);
+            else detect_slab_kernel<F16, 4><<<g1, 1024, 0, stream>>>(x, a.M, a.K, a.tau, bitmap, pmax, nslab);
+        } else {
+            if (a.M <= 16) detect_slab_kernel<BF16, 1><<<g1, 1024, 0, stream>>>(x, a.M, a.K, a.tau, bitmap, pmax, nslab);
+            else if (a.M <= 32) detect_slab_kernel<BF16, 2><<<g1, 1024, 0, stream>>>(x, a.M, a.K, a.tau, bitmap, pmax, nslab);
+            else detect_slab_kernel<BF16, 4><<<g1, 1024, 0, stream>>>(x, a.M, a.K, a.tau, bitmap, pmax, nslab);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (a.dt == F16) return code_rows_launch<F16, true>(a, bitmap, O, n_out, 0, stream);
-    return code_rows_launch<BF16, true>(a, bitmap, O, n_out, 0, stream);
+    const int64_t gx = ceil_div(a.xq_pitch / 8, 64);
+    const dim3 g2((unsigned)(gx > 0 ? gx : 1), (unsigned)ceil_div(a.M, 4));
+    if (a.dt == F16)
+        code_slab_kernel<F16><<<g2, 256, 0, stream>>>(x, a.M, a.K, bitmap, pmax, nslab, O, n_out, a.Xq, a.xq_pitch,
+                                                      a.s_x, (uint16_t*)a.XO, a.xo_pitch);
+    else
+        code_slab_kernel<BF16><<<g2, 256, 0, stream>>>(x, a.M, a.K, bitmap, pmax, nslab, O, n_out, a.Xq, a.xq_pitch,
+                                                       a.s_x, (uint16_t*)a.XO, a.xo_pitch);
+    return hipGetLastError();
 }
 
 }  // namespace llmint8

@@ -48,9 +48,11 @@ def test_ragged_medium(dt):
                                       (257, 272, 264, "fp16"), (513, 128, 8, "bf16"), (7, 32, 1032, "fp16"),
                                       # small batches: one-workgroup X pass (M*K <= 32768) with waves that
                                       # straddle rows (K = 800: 100 chunks per row), at and just past its
-                                      # size limit, and the two-launch X pass
+                                      # size limit, and the two slab launches past it (16, 32 and 64 rows
+                                      # held per lane; K not a multiple of the 512-column slab)
                                       (40, 800, 136, "bf16"), (64, 512, 264, "fp16"), (64, 528, 264, "fp16"),
-                                      (40, 3200, 136, "bf16"), (64, 4096, 264, "bf16")])
+                                      (40, 3200, 136, "bf16"), (64, 4096, 264, "bf16"), (24, 2064, 136, "fp16"),
+                                      (32, 16400, 40, "bf16"), (17, 1552, 8, "fp16")])
 def test_edge_shapes(M, K, N, dt):
     _banner(f"edge {M}x{K}x{N} {dt}")
     x, w = _case(M, K, N, dt, n_out=2, seed=M + K + N)
@@ -153,6 +155,12 @@ def test_empty_batch_and_empty_features():
     Y = lm.int8_matmul(X, Wq0, s0, 6.0, Y=torch.full((5, 16), 7.0, dtype=torch.bfloat16, device="cuda"))
     torch.cuda.synchronize()
     assert torch.all(Y == 0) and not torch.signbit(Y.float()).any()
+    # the X pass of an empty feature dimension: no outlier columns, every row scale 0
+    ws = torch.full((lm.int8_matmul_workspace_bytes(5, 0, 16),), 0x55, dtype=torch.uint8, device="cuda")
+    lm.int8_matmul_prepare(X, Wq0, 6.0, workspace=ws)
+    torch.cuda.synchronize()
+    v = lm.workspace_views(ws, 5, 0, 16, X.dtype)
+    assert v["n_outliers"] == 0 and torch.all(v["s_x"] == 0)
     Y = lm.int8_matmul(torch.randn(4, 32).half().cuda(), torch.zeros(0, 32, dtype=torch.int8, device="cuda"),
                        torch.zeros(0, device="cuda"), 6.0)
     assert Y.shape == (4, 0)
