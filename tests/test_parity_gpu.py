@@ -98,6 +98,36 @@ def test_threshold_exactly_tau_is_not_an_outlier(dt):
 
 
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
+@pytest.mark.parametrize("M", [4, 80])  # small-batch slab detection and the tiled path's detection
+def test_detection_threshold_sweep(dt, M):
+    """The outlier set against the oracle with every finite magnitude in one column each
+    (random signs, spread over the rows) and thresholds at 0, the smallest subnormal, a
+    representable value, a value strictly between two representable ones, the largest
+    finite value and +inf."""
+    top = 0x7C00 if dt == "fp16" else 0x7F80  # +inf's pattern; every magnitude below is finite
+    K = 32768
+    rng = np.random.default_rng(11)
+    mags = np.arange(top, dtype=np.uint32)
+    signs = rng.integers(0, 2, top).astype(np.uint32) << 15
+    Xb = np.zeros((M, K), np.uint16)
+    Xb[mags % M, mags] = (mags | signs).astype(np.uint16)
+    X = workloads.from_bits(Xb, dt).cuda()
+    Wq = torch.zeros((8, K), dtype=torch.int8, device="cuda")
+    six = float(f32_of(bits_of(np.array([6.0]), dt), dt)[0])
+    between = float(np.nextafter(np.float32(six), np.float32(7.0)))  # not representable in 16 bits
+    largest = float(f32_of(np.array([top - 1], np.uint16), dt)[0])
+    tiny = float(f32_of(np.array([1], np.uint16), dt)[0])
+    for tau in (0.0, tiny, six, between, largest, float("inf")):
+        _banner(f"detection sweep {dt} M={M} tau={tau!r}")
+        ws = lm.int8_matmul_prepare(X, Wq, tau)
+        torch.cuda.synchronize()
+        v = lm.workspace_views(ws, M, K, 8, X.dtype)
+        O = oracle.outlier_columns(Xb, dt, tau)
+        assert v["n_outliers"] == O.size, (tau, v["n_outliers"], O.size)
+        assert np.array_equal(v["outliers"].cpu().numpy(), O), tau
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
 @pytest.mark.parametrize("M", [40, 130])  # small-batch path and tiled path
 def test_tau_zero_every_column_is_an_outlier(dt, M):
     # the degenerate 16-bit path: n_O = K (nine 32-wide chunks), C = 0, s_x = 0
