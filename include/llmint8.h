@@ -141,7 +141,7 @@ int int8_matmul_products(int64_t M, int64_t K, int dtype, const int8_t* Wq, cons
  *   wo        dtype [N][xo_pitch]   Wq[:, O] cast to dtype (same padding); written only by
  *                                   the tiled path (M > 64 or K > 32768) -- the small-batch
  *                                   product kernel gathers these values itself
- *   scratch   internal (outlier flags)                                              */
+ *   scratch   internal (outlier flags; for small batches also per-row partial maxima) */
 typedef struct {
     size_t xq, xq_pitch, s_x, n_outliers, outliers, xo, xo_pitch, wo, scratch, total;
 } llmint8_workspace_layout;
