@@ -52,7 +52,10 @@ def test_ragged_medium(dt):
                                       # held per lane; K not a multiple of the 512-column slab)
                                       (40, 800, 136, "bf16"), (64, 512, 264, "fp16"), (64, 528, 264, "fp16"),
                                       (40, 3200, 136, "bf16"), (64, 4096, 264, "bf16"), (24, 2064, 136, "fp16"),
-                                      (32, 16400, 40, "bf16"), (17, 1552, 8, "fp16")])
+                                      (32, 16400, 40, "bf16"), (17, 1552, 8, "fp16"),
+                                      # two rows at the largest small-batch K; a ragged last slab and a
+                                      # half-filled last bitmap word (K % 32 = 16)
+                                      (2, 32768, 8, "bf16"), (5, 7440, 24, "fp16")])
 def test_edge_shapes(M, K, N, dt):
     _banner(f"edge {M}x{K}x{N} {dt}")
     x, w = _case(M, K, N, dt, n_out=2, seed=M + K + N)
