@@ -58,17 +58,18 @@ KERNELS = {
     "gemm_small_kernel": [CSRC + "gemm_small.hip", CSRC + "common.hpp"],
     "gemm_group_kernel": [CSRC + "gemm_group.hip", CSRC + "common.hpp"],
 }
-SMALL_M, SMALL_K = 64, 32768  # the library's small-batch switch (M <= 64 and K <= 32768)
 
 
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def product_kernel(M: int, K: int, group: int = 0) -> str:
+def product_kernel(M: int, K: int, N: int, group: int = 0) -> str:
+    """The product kernel the library runs for these sizes (it reports its own choice)."""
     if group:
         return "gemm_group_kernel"
-    return "gemm_small_kernel" if (M <= SMALL_M and K <= SMALL_K) else "gemm_kernel"
+    import int8_quantized_matmul_rowwise_amd as lm
+    return "gemm_small_kernel" if lm.int8_matmul_workspace_layout(M, K, N)["small_batch"] else "gemm_kernel"
 
 
 def workload_tag(wl, group: int = 0) -> str:
@@ -203,7 +204,7 @@ def _per_dispatch(rows, counter: str, match) -> list:
 
 
 def traffic_summary(fetch_dir: str, write_dir: str, wl, copy_mib: int, group: int = 0) -> int:
-    kernel = product_kernel(wl.M, wl.K, group)
+    kernel = product_kernel(wl.M, wl.K, wl.N, group)
     tag = workload_tag(wl, group)
     gflag = f" --group {group}" if group else ""
     copy_bytes = copy_mib * 1024 * 1024
@@ -265,7 +266,7 @@ def trace_summary(trace_dir: str, bench_json: str, wl, cmd: str, group: int = 0)
         raise SystemExit(f"no kernel_stats.csv under {trace_dir}")
     with open(files[0], newline="") as fh:
         rows = list(csv.DictReader(fh))
-    kernel = product_kernel(wl.M, wl.K, group)
+    kernel = product_kernel(wl.M, wl.K, wl.N, group)
     tag = workload_tag(wl, group)
     lines = [f"# Kernel trace, workload {tag} ({wl.M}x{wl.K}x{wl.N} {wl.dtype})", "",
              "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
@@ -390,7 +391,7 @@ def group_bench(args, wl) -> int:
     lm.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    kernel = product_kernel(wl.M, wl.K, G)
+    kernel = product_kernel(wl.M, wl.K, wl.N, G)
     tag = workload_tag(wl, G)
     log(f"workload {tag}: X {wl.M}x{wl.K} {wl.dtype}, W {wl.K}x{wl.N}, groups of {G}; product kernel {kernel}")
     x, w, _, _ = workloads.make_workload(wl.name)
@@ -522,7 +523,7 @@ def main() -> int:
     lm.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    kernel = product_kernel(wl.M, wl.K)
+    kernel = product_kernel(wl.M, wl.K, wl.N)
     log(f"workload {wl.name}: X {wl.M}x{wl.K} {wl.dtype}, W {wl.K}x{wl.N}, tau {wl.tau}; product kernel {kernel}")
     x, w, cols, _ = workloads.make_workload(wl.name)
     X = x.to(dev)

@@ -139,11 +139,14 @@ int int8_matmul_products(int64_t M, int64_t K, int dtype, const int8_t* Wq, cons
  *   xo        dtype [M][xo_pitch]   X[:, O] (first n_O columns; zero up to the next
  *                                   multiple of 32)
  *   wo        dtype [N][xo_pitch]   Wq[:, O] cast to dtype (same padding); written only by
- *                                   the tiled path (M > 64 or K > 32768) -- the small-batch
- *                                   product kernel gathers these values itself
- *   scratch   internal (outlier flags; for small batches also per-row partial maxima) */
+ *                                   the tiled path -- the small-batch product kernel
+ *                                   gathers these values itself
+ *   scratch   internal (outlier flags; for small batches also per-row partial maxima)
+ *   total     bytes (int8_matmul_workspace_bytes)
+ *   small_batch  1 when these sizes take the small-batch path (M <= 64, K <= 32768 and
+ *             N small enough that streaming Wq once beats the tiled kernel), else 0 */
 typedef struct {
-    size_t xq, xq_pitch, s_x, n_outliers, outliers, xo, xo_pitch, wo, scratch, total;
+    size_t xq, xq_pitch, s_x, n_outliers, outliers, xo, xo_pitch, wo, scratch, total, small_batch;
 } llmint8_workspace_layout;
 
 int int8_matmul_workspace_layout(int64_t M, int64_t K, int64_t N, llmint8_workspace_layout* out);

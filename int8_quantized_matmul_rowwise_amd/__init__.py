@@ -42,7 +42,7 @@ class LLMInt8Error(RuntimeError):
 
 class WorkspaceLayout(ctypes.Structure):
     _fields_ = [(n, _SZ) for n in ("xq", "xq_pitch", "s_x", "n_outliers", "outliers", "xo", "xo_pitch", "wo",
-                                   "scratch", "total")]
+                                   "scratch", "total", "small_batch")]
 
 
 _SIGNATURES = {

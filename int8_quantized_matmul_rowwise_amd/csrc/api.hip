@@ -67,7 +67,7 @@ Layout make_layout(int64_t M, int64_t K, int64_t N) {
     L.partial = off;
     off = align_up(off + 4 * kw * (size_t)detect_row_blocks(M));
     L.pmax = off;  // small batches: per row and 512-column slab, the slab's row maximum
-    off = align_up(off + (small_batch(M, K) ? 4 * m * (size_t)ceil_div(K, 512) : 0));
+    off = align_up(off + (small_batch(M, K, N) ? 4 * m * (size_t)ceil_div(K, 512) : 0));
     L.total = off;
     return L;
 }
@@ -97,7 +97,7 @@ int run_xpass(const void* X, int64_t M, int64_t K, int dtype, float tau, const i
     a.s_x = (float*)(ws + L.s_x);
     a.XO = ws + L.xo;
     a.xo_pitch = (int64_t)L.xo_pitch;
-    if (small_batch(M, K)) return hip_status(launch_xpass_small(a, O, nO, bitmap, (uint32_t*)(ws + L.pmax), st));
+    if (small_batch(M, K, N)) return hip_status(launch_xpass_small(a, O, nO, bitmap, (uint32_t*)(ws + L.pmax), st));
     hipError_t e = launch_detect(dtype, X, M, K, tau, partial, st);
     if (e == hipSuccess) e = launch_compact(M, K, partial, bitmap, O, nO, st);
     if (e == hipSuccess) {
@@ -183,7 +183,7 @@ int products_common(int64_t M, int64_t K, int dtype, const int8_t* Wq, const flo
     g.Y = Y;
     g.C_acc = C;
     g.F_acc = F;
-    if (small_batch(M, K)) return hip_status(launch_gemm_small(g, (hipStream_t)stream));
+    if (small_batch(M, K, N)) return hip_status(launch_gemm_small(g, (hipStream_t)stream));
     return hip_status(launch_gemm(g, (hipStream_t)stream));
 }
 
@@ -280,6 +280,7 @@ LLMINT8_API int int8_matmul_workspace_layout(int64_t M, int64_t K, int64_t N, ll
     out->wo = L.wo;
     out->scratch = L.bitmap;
     out->total = L.total;
+    out->small_batch = small_batch(M, K, N) ? 1 : 0;
     return LLMINT8_OK;
 }
 

@@ -110,8 +110,8 @@ def run_case(X: torch.Tensor, W: torch.Tensor, tau: float, rows=None, device="cu
         P = v["XO"].shape[1]
         xo = to_bits(v["XO"])
         assert np.array_equal(xo[:, :n_o], XO_o) and not xo[:, n_o:].any(), "X[:,O] gather differs"
-        small_batch = M <= 64 and K <= 32768  # that path gathers Wq[:,O] inside its product kernel
-        if N > 0 and not small_batch:
+        # the small-batch path gathers Wq[:,O] inside its product kernel
+        if N > 0 and not lm.int8_matmul_workspace_layout(M, K, N)["small_batch"]:
             wo = to_bits(v["WO"])
             ref = bits_of(Wq_o[:, O].astype(np.float32), dt)
             assert np.array_equal(wo[:, :n_o], ref) and not wo[:, n_o:].any(), "Wq[:,O] gather differs"

@@ -55,7 +55,9 @@ def test_ragged_medium(dt):
                                       (32, 16400, 40, "bf16"), (17, 1552, 8, "fp16"),
                                       # two rows at the largest small-batch K; a ragged last slab and a
                                       # half-filled last bitmap word (K % 32 = 16)
-                                      (2, 32768, 8, "bf16"), (5, 7440, 24, "fp16")])
+                                      (2, 32768, 8, "bf16"), (5, 7440, 24, "fp16"),
+                                      # small batches with N wide enough that they take the tiled kernel
+                                      (24, 1024, 36864, "fp16"), (48, 512, 28672, "bf16")])
 def test_edge_shapes(M, K, N, dt):
     _banner(f"edge {M}x{K}x{N} {dt}")
     x, w = _case(M, K, N, dt, n_out=2, seed=M + K + N)
