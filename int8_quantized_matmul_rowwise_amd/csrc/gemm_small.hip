@@ -2,13 +2,14 @@
 // decode shape).  The same arithmetic as the tiled kernel (exact int32 C = Xq Wq^T on i8
 // MFMA, fp32 F = X[:,O] Wq[:,O]^T on 16-bit MFMA, the same epilogue op sequence), laid
 // out for an HBM-bound product: the weight is read once, so every workgroup streams its
-// own 16 rows of Wq (16 output columns) straight from HBM into registers -- no LDS
-// staging, nothing to reuse -- and the four waves of a workgroup split K, each keeping
-// two batches of K steps in flight (the next batch is loaded before the current one's
-// MFMAs).  Two 64-deep steps of a wave cover one 128-byte line of each Wq row.  Partial
-// int32 sums are combined exactly through LDS.  Each workgroup gathers the 16-bit outlier
-// operands Wq[n, O[t]] of its own columns, at kernel start so that the scattered loads
-// overlap the weight stream.
+// own 16 or 32 rows of Wq (output columns) straight from HBM into registers -- no LDS
+// staging -- and the waves of a workgroup split K, each keeping two batches of K steps in
+// flight (the next batch is loaded before the current one's MFMAs).  Two 64-deep steps of
+// a wave cover one 128-byte line of each Wq row.  Every workgroup re-reads all of Xq from
+// the cache; with 32 columns per workgroup each X operand load feeds two MFMAs, which
+// halves those re-reads (they grow with M).  Partial int32 sums are combined exactly
+// through LDS.  Each workgroup gathers the 16-bit outlier operands Wq[n, O[t]] of its own
+// columns, at kernel start so that the scattered loads overlap the weight stream.
 // "LLM.int8(): 8-bit Matrix Multiplication for Transformers at Scale", abstract.
 #include "common.hpp"
 #include "launch.hpp"
@@ -17,8 +18,6 @@ namespace llmint8 {
 
 namespace {
 
-constexpr int kCols = 16;   // output columns per workgroup
-constexpr int kWaves = 4;   // waves per workgroup, splitting K
 
 struct SmallParams {
     const int8_t* Xq;
@@ -46,19 +45,28 @@ __device__ __forceinline__ v4f mfma16x16(const u32x4& a, const u32x4& b, const v
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
-// MG: groups of 16 rows of X (ceil(M/16)).  Batches of PAIRS step pairs per wave, two
-// register sets: the next batch's loads are issued before the current batch's MFMAs, so
-// the weight stream never waits for the arithmetic.
-template <int DT, int MG, bool ACC_OUT>
-__global__ __launch_bounds__(256) void gemm_small_kernel(SmallParams p) {
-    constexpr int PAIRS = MG == 1 ? 4 : (MG == 2 ? 2 : 1);
+// MG: groups of 16 rows of X (ceil(M/16)); NC: groups of 16 output columns per
+// workgroup (each X operand load feeds NC MFMAs, so Xq is re-read from the cache N / (16
+// NC) times instead of N / 16).  Batches of PAIRS step pairs per wave, two register sets:
+// the next batch's loads are issued before the current batch's MFMAs, so the weight
+// stream never waits for the arithmetic.  WAVES waves split K; waves g * NC + c (g < MG,
+// c < NC) finish the row group g of column group c: MG * NC <= WAVES.
+template <int DT, int MG, int NC, int WAVES, bool ACC_OUT>
+__global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(SmallParams p) {
+    static_assert(MG * NC <= WAVES, "one finishing wave per row and column group");
+    constexpr int kWaves = WAVES;
+    constexpr int PAIRS = MG == 1 ? 4 : (MG * NC == 2 ? 2 : 1);
     constexpr int U = 2 * PAIRS;  // 64-deep steps per batch
-    __shared__ v4i red[kWaves][MG][64];
+    __shared__ v4i red[kWaves][MG][NC][64];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int li = lane & 15, q = lane >> 4;  // 16x16x64 operands: row/column li, 16 k at 16*q
-    const int64_t n0 = (int64_t)blockIdx.x * kCols;
-    const int64_t n = n0 + li < p.N ? n0 + li : p.N - 1;
-    const int8_t* brow = p.Wq + n * p.K;
+    const int64_t n0 = (int64_t)blockIdx.x * 16 * NC;
+    const int8_t* brow[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int64_t n = n0 + 16 * c + li < p.N ? n0 + 16 * c + li : p.N - 1;
+        brow[c] = p.Wq + n * p.K;
+    }
     const int8_t* arow[MG];
 #pragma unroll
     for (int g = 0; g < MG; ++g) {
@@ -68,48 +76,56 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(SmallParams p) {
     const int64_t nsteps = ceil_div(p.K, 64);
 
     // The outlier operands of the epilogue (first 32 outlier columns), gathered now so that
-    // their scattered loads overlap the weight stream: Wq[n, O[t]] for t = 8q + e, and the
-    // row's X[:,O] chunk.
+    // their scattered loads overlap the weight stream: for the finishing wave of (g, c),
+    // Wq[n, O[t]] for t = 8q + e, and the row's X[:,O] chunk.
     const int32_t nO = *p.n_out;
+    const int fg = w / NC, fc = w % NC;  // this wave's row and column group when it finishes
+    const int64_t fn = n0 + 16 * fc + li < p.N ? n0 + 16 * fc + li : p.N - 1;
     uint32_t wo0[4] = {0u, 0u, 0u, 0u};
     u32x4 xo0 = {0u, 0u, 0u, 0u};
-    if (w < MG && nO > 0) {
-        const int64_t am = w * 16 + li < p.M ? w * 16 + li : p.M - 1;
+    if (w < MG * NC && nO > 0) {
+        const int64_t am = fg * 16 + li < p.M ? fg * 16 + li : p.M - 1;
         xo0 = *(const u32x4*)(p.XO + am * p.xo_pitch + q * 8);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int t = q * 8 + e;
             const uint16_t hv = t >= nO ? (uint16_t)0
-                                : p.WO ? p.WO[n * p.wo_pitch + t] : from_f32<DT>((float)brow[p.O[t]]);
+                                : p.WO ? p.WO[fn * p.wo_pitch + t] : from_f32<DT>((float)p.Wq[fn * p.K + p.O[t]]);
             wo0[e >> 1] |= (uint32_t)hv << (16 * (e & 1));
         }
     }
 
-    v4i acc[MG];
+    v4i acc[MG][NC];
 #pragma unroll
-    for (int g = 0; g < MG; ++g) acc[g] = v4i{0, 0, 0, 0};
+    for (int g = 0; g < MG; ++g)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[g][c] = v4i{0, 0, 0, 0};
     // wave w takes step pairs w, w+4, w+8, ...; batch j of the wave holds pairs
     // w + kWaves * (PAIRS * j + i), i < PAIRS
     const int64_t stride = (int64_t)kWaves * PAIRS;
-    auto load = [&](int64_t p0, v4i (&b)[U], v4i (&a)[U][MG]) {
+    auto load = [&](int64_t p0, v4i (&b)[U][NC], v4i (&a)[U][MG]) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t st = 2 * (p0 + (int64_t)kWaves * (u >> 1)) + (u & 1);
             const int64_t k = st * 64 + q * 16;
             const bool in = st < nsteps;
-            b[u] = (in && k < p.K) ? *(const v4i*)(brow + k) : v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) b[u][c] = (in && k < p.K) ? *(const v4i*)(brow[c] + k) : v4i{0, 0, 0, 0};
 #pragma unroll
             for (int g = 0; g < MG; ++g) a[u][g] = in ? *(const v4i*)(arow[g] + k) : v4i{0, 0, 0, 0};
         }
     };
-    auto compute = [&](const v4i (&b)[U], const v4i (&a)[U][MG]) {
+    auto compute = [&](const v4i (&b)[U][NC], const v4i (&a)[U][MG]) {
 #pragma unroll
         for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int g = 0; g < MG; ++g) acc[g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][g], b[u], acc[g], 0, 0, 0);
+            for (int g = 0; g < MG; ++g)
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+                    acc[g][c] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u][g], b[u][c], acc[g][c], 0, 0, 0);
     };
     {
-        v4i b0[U], a0[U][MG], b1[U], a1[U][MG];
+        v4i b0[U][NC], a0[U][MG], b1[U][NC], a1[U][MG];
         int64_t p0 = w;
         if (2 * p0 < nsteps) load(p0, b0, a0);
         while (2 * p0 < nsteps) {
@@ -124,13 +140,19 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(SmallParams p) {
         }
     }
 #pragma unroll
-    for (int g = 0; g < MG; ++g) red[w][g][lane] = acc[g];
+    for (int g = 0; g < MG; ++g)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) red[w][g][c][lane] = acc[g][c];
     __syncthreads();
-    if (w >= MG) return;
+    if (w >= MG * NC) return;
 
-    // ---- wave g: rows 16g.., exact sum of the four partials, outlier product, epilogue
-    const int g = w;
-    const v4i c = red[0][g][lane] + red[1][g][lane] + red[2][g][lane] + red[3][g][lane];
+    // ---- wave (g, c): rows 16g.., columns n0 + 16c.., exact sum of the four partials,
+    // outlier product, epilogue
+    const int g = fg, c = fc;
+    const int64_t n = fn;
+    v4i cs = red[0][g][c][lane];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) cs += red[i][g][c][lane];
     v4f F = v4f{0.f, 0.f, 0.f, 0.f};
     if (nO > 0) F = mfma16x16<DT>(xo0, u32x4{wo0[0], wo0[1], wo0[2], wo0[3]}, F);
     {
@@ -143,38 +165,58 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(SmallParams p) {
             for (int e = 0; e < 8; ++e) {
                 const int t = t0 + q * 8 + e;
                 const uint16_t h = t >= nO ? (uint16_t)0
-                                   : p.WO ? p.WO[n * p.wo_pitch + t] : from_f32<DT>((float)brow[p.O[t]]);
+                                   : p.WO ? p.WO[n * p.wo_pitch + t] : from_f32<DT>((float)p.Wq[n * p.K + p.O[t]]);
                 bv[e >> 1] |= (uint32_t)h << (16 * (e & 1));
             }
             F = mfma16x16<DT>(av, bv, F);
         }
     }
-    if (n0 + li >= p.N) return;
+    if (n0 + 16 * c + li >= p.N) return;
     const float cn = p.s_w[n] / 127.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {  // lane holds rows 4q + e of the group, column li
         const int64_t m = g * 16 + 4 * q + e;
         if (m >= p.M) continue;
         if constexpr (ACC_OUT) {
-            p.C_acc[m * p.N + n] = c[e];
+            p.C_acc[m * p.N + n] = cs[e];
             p.F_acc[m * p.N + n] = F[e];
         } else {
             const float r = p.s_x[m] / 127.0f;
-            const float yi = __fmul_rn(__fmul_rn((float)c[e], r), cn);
+            const float yi = __fmul_rn(__fmul_rn((float)cs[e], r), cn);
             const float y = __fadd_rn(yi, p.WO ? F[e] : __fmul_rn(cn, F[e]));
             p.Y[m * p.N + n] = from_f32<DT>(y);
         }
     }
 }
 
+// Two column groups per workgroup when that still gives every compute unit a workgroup
+// (and, for one row group, two: with one the single 16-column layout is faster), with 8
+// waves for 3 or 4 row groups; else one column group and 4 waves.  Measured on MI355X,
+// N x K = 36864 x 12288, 28672 x 8192, 16384 x 4096 and 8192 x 8192, M = 16 to 64.
 template <int DT, bool ACC_OUT>
 hipError_t launch_mg(const SmallParams& p, hipStream_t stream) {
-    const unsigned grid = (unsigned)ceil_div(p.N, kCols);
-    switch (ceil_div(p.M, 16)) {
-        case 1: gemm_small_kernel<DT, 1, ACC_OUT><<<grid, 256, 0, stream>>>(p); break;
-        case 2: gemm_small_kernel<DT, 2, ACC_OUT><<<grid, 256, 0, stream>>>(p); break;
-        case 3: gemm_small_kernel<DT, 3, ACC_OUT><<<grid, 256, 0, stream>>>(p); break;
-        default: gemm_small_kernel<DT, 4, ACC_OUT><<<grid, 256, 0, stream>>>(p); break;
+    const int64_t mg = ceil_div(p.M, 16);
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const int64_t wg2 = ceil_div(p.N, 32);
+    if (wg2 >= cus && (mg > 1 || wg2 >= 2 * (int64_t)cus)) {
+        const unsigned grid = (unsigned)wg2;
+        switch (mg) {
+            case 1: gemm_small_kernel<DT, 1, 2, 4, ACC_OUT><<<grid, 256, 0, stream>>>(p); break;
+            case 2: gemm_small_kernel<DT, 2, 2, 4, ACC_OUT><<<grid, 256, 0, stream>>>(p); break;
+            case 3: gemm_small_kernel<DT, 3, 2, 8, ACC_OUT><<<grid, 512, 0, stream>>>(p); break;
+            default: gemm_small_kernel<DT, 4, 2, 8, ACC_OUT><<<grid, 512, 0, stream>>>(p); break;
+        }
+        return hipGetLastError();
+    }
+    const unsigned grid = (unsigned)ceil_div(p.N, 16);
+    switch (mg) {
+        case 1: gemm_small_kernel<DT, 1, 1, 4, ACC_OUT><<<grid, 256, 0, stream>>>(p); break;
+        case 2: gemm_small_kernel<DT, 2, 1, 4, ACC_OUT><<<grid, 256, 0, stream>>>(p); break;
+        case 3: gemm_small_kernel<DT, 3, 1, 4, ACC_OUT><<<grid, 256, 0, stream>>>(p); break;
+        default: gemm_small_kernel<DT, 4, 1, 4, ACC_OUT><<<grid, 256, 0, stream>>>(p); break;
     }
     return hipGetLastError();
 }

@@ -31,20 +31,20 @@ hipError_t launch_compact(int64_t M, int64_t K, const uint32_t* partial, uint32_
                           int32_t* n_out, hipStream_t stream);
 
 // Small-batch path (slab X pass, split-N product kernel), for M <= kSmallM and K <= kSmallK
-// where it beats the tiled path.  The split-N kernel streams Wq once at about 5.4 TB/s,
-// and every row of X adds about 3.8 % to that time (its re-reads of Xq from the cache);
-// the tiled kernel, with at most one 256-row tile, takes about K * 10.5 ns per round of
-// 256-column tiles over the compute units.  Measured on MI355X (256 CUs), from M = 8 to 64
-// on N x K = 36864 x 12288, 28672 x 8192, 16384 x 4096, 8192 x 8192 and 4096 x 4096:
-// N * (1 + 0.038 M) / 5.4 TB/s < K * 10.5 ns * rounds, i.e. the test below, picks the
-// faster path in each case but one (28672 x 8192 at M = 32: 86 us tiled, 83 small).
+// where it beats the tiled path.  The split-N kernel streams Wq once at about 5 TB/s, and
+// every row of X adds about 2.2 % to that time (its re-reads of Xq from the cache); the
+// tiled kernel, with one 256-row tile, takes about K * 10.5 ns per round of 256-column
+// tiles over the compute units, whatever M.  Measured on MI355X (256 CUs), M = 16 to 64
+// on N x K = 36864 x 12288, 28672 x 8192, 16384 x 4096 and 8192 x 8192:
+// N * (1 + 0.022 M) / 5 TB/s < K * 10.5 ns * rounds, the test below, picks the faster
+// path in each of those cases.
 constexpr int64_t kSmallM = 64;
 constexpr int64_t kSmallK = 32768;
 constexpr int64_t kRoutingCUs = 256;
 inline bool small_batch(int64_t M, int64_t K, int64_t N) {
     if (M > kSmallM || K > kSmallK) return false;
     const int64_t rounds = ((N + 255) / 256 + kRoutingCUs - 1) / kRoutingCUs;
-    return N * (1000 + 38 * M) < 56700000 * (rounds > 0 ? rounds : 1);
+    return N * (1000 + 22 * M) < 52500000 * (rounds > 0 ? rounds : 1);
 }
 
 struct XPassArgs {

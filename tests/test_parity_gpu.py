@@ -57,7 +57,11 @@ def test_ragged_medium(dt):
                                       # half-filled last bitmap word (K % 32 = 16)
                                       (2, 32768, 8, "bf16"), (5, 7440, 24, "fp16"),
                                       # small batches with N wide enough that they take the tiled kernel
-                                      (24, 1024, 36864, "fp16"), (48, 512, 28672, "bf16")])
+                                      (24, 1024, 36864, "fp16"), (48, 512, 28672, "bf16"),
+                                      # the small-batch kernel with two 16-column groups per workgroup
+                                      # (1, 2 and 4 row groups; 4 and 8 waves; a ragged last group)
+                                      (16, 2048, 16384, "fp16"), (32, 1024, 8192, "fp16"),
+                                      (64, 512, 16384, "bf16"), (40, 800, 8200, "bf16")])
 def test_edge_shapes(M, K, N, dt):
     _banner(f"edge {M}x{K}x{N} {dt}")
     x, w = _case(M, K, N, dt, n_out=2, seed=M + K + N)
