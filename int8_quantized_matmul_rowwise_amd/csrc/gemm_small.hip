@@ -45,6 +45,36 @@ __device__ __forceinline__ v4f mfma16x16(const u32x4& a, const u32x4& b, const v
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
+// The W side of the outlier product for column n and outlier ranks t = t0 + 8q + e (e < 8),
+// packed two per dword: the caller's exact row W_O[n, t], else (T)Wq[n, O[t]]; 0 for t >=
+// n_O.  Every load is issued unconditionally (ranks past n_O read the last outlier's
+// entries, then are zeroed), so the eight O loads share one round trip and the eight
+// gathers the next, instead of two dependent trips per outlier.
+template <int DT>
+__device__ __forceinline__ void gather_w_side(const SmallParams& p, int64_t n, int t0, int q, int32_t nO,
+                                              uint32_t (&out)[4]) {
+    uint16_t h[8];
+    if (p.WO) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = t0 + q * 8 + e;
+            h[e] = p.WO[n * p.wo_pitch + (t < nO ? t : nO - 1)];
+        }
+    } else {
+        int32_t col[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = t0 + q * 8 + e;
+            col[e] = p.O[t < nO ? t : nO - 1];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = from_f32<DT>((float)p.Wq[n * p.K + col[e]]);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        out[e >> 1] |= (uint32_t)(t0 + q * 8 + e < nO ? h[e] : (uint16_t)0) << (16 * (e & 1));
+}
+
 // MG: groups of 16 rows of X (ceil(M/16)); NC: groups of 16 output columns per
 // workgroup (each X operand load feeds NC MFMAs, so Xq is re-read from the cache N / (16
 // NC) times instead of N / 16).  Batches of PAIRS step pairs per wave, two register sets:
@@ -86,13 +116,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(SmallParams p) {
     if (w < MG * NC && nO > 0) {
         const int64_t am = fg * 16 + li < p.M ? fg * 16 + li : p.M - 1;
         xo0 = *(const u32x4*)(p.XO + am * p.xo_pitch + q * 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int t = q * 8 + e;
-            const uint16_t hv = t >= nO ? (uint16_t)0
-                                : p.WO ? p.WO[fn * p.wo_pitch + t] : from_f32<DT>((float)p.Wq[fn * p.K + p.O[t]]);
-            wo0[e >> 1] |= (uint32_t)hv << (16 * (e & 1));
-        }
+        gather_w_side<DT>(p, fn, 0, q, nO, wo0);
     }
 
     v4i acc[MG][NC];
@@ -160,15 +184,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(SmallParams p) {
         const uint16_t* xo = p.XO + am * p.xo_pitch + q * 8;
         for (int t0 = 32; t0 < nO; t0 += 32) {
             const u32x4 av = *(const u32x4*)(xo + t0);  // zero-padded to a multiple of 32
-            u32x4 bv = {0u, 0u, 0u, 0u};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int t = t0 + q * 8 + e;
-                const uint16_t h = t >= nO ? (uint16_t)0
-                                   : p.WO ? p.WO[n * p.wo_pitch + t] : from_f32<DT>((float)p.Wq[n * p.K + p.O[t]]);
-                bv[e >> 1] |= (uint32_t)h << (16 * (e & 1));
-            }
-            F = mfma16x16<DT>(av, bv, F);
+            uint32_t bw[4] = {0u, 0u, 0u, 0u};
+            gather_w_side<DT>(p, n, t0, q, nO, bw);
+            F = mfma16x16<DT>(av, u32x4{bw[0], bw[1], bw[2], bw[3]}, F);
         }
     }
     if (n0 + 16 * c + li >= p.N) return;
