@@ -39,7 +39,7 @@ hipError_t launch_compact(int64_t M, int64_t K, const uint32_t* partial, uint32_
 // N * (1 + 0.022 M) / 5 TB/s < K * 10.5 ns * rounds, the test below, picks the faster
 // path in each of those cases.
 constexpr int64_t kSmallM = 64;
-constexpr int64_t kSmallK = 32768;
+constexpr int64_t kSmallK = 65536;
 constexpr int64_t kRoutingCUs = 256;
 inline bool small_batch(int64_t M, int64_t K, int64_t N) {
     if (M > kSmallM || K > kSmallK) return false;

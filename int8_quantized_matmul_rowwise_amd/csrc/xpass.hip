@@ -610,22 +610,28 @@ __global__ __launch_bounds__(256) void code_slab_kernel(const uint16_t* __restri
     const int64_t sl = blockIdx.x, C = K / 8, Cp = xq_pitch / 8, Kw = ceil_div(K, 32);
     const int64_t c = sl * 64 + lane, r = (int64_t)blockIdx.y * 4 + w;  // this thread's chunk and row
     const bool live = c < C, row = r < M;
-    // every load first (rows past M and chunks past K read 0): the chunk, row r's slab
-    // partials (nslab <= 64), and in wave 0 the bitmap (Kw <= 1024 words)
+    // every load first (rows past M, slabs past nslab and chunks past K read 0): the chunk,
+    // row r's slab partials (nslab <= 64 kParts), and in wave 0 the bitmap (Kw <= 64 kWords)
+    constexpr int kParts = (int)(kSmallK / 512 / 64), kWords = (int)(kSmallK / 32 / 64);
     const __amdgpu_buffer_rsrc_t xr = span_rsrc(X + (row ? r : 0) * K, row ? 2 * K : 0);
     const __amdgpu_buffer_rsrc_t pr = span_rsrc(pmax + (row ? r : 0) * nslab, row ? 4 * nslab : 0);
     const __amdgpu_buffer_rsrc_t br = span_rsrc(bitmap, 4 * Kw);
     const u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, (uint32_t)(16 * c), 0, 0));
-    uint32_t m = __builtin_amdgcn_raw_buffer_load_b32(pr, (uint32_t)(4 * lane), 0, 0);
-    uint32_t bw[16], wd = 0;
+    uint32_t pm[kParts];
+#pragma unroll
+    for (int i = 0; i < kParts; ++i) pm[i] = __builtin_amdgcn_raw_buffer_load_b32(pr, (uint32_t)(4 * (lane + 64 * i)), 0, 0);
+    uint32_t bw[kWords], wd = 0;
     if (w == 0) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) bw[q] = __builtin_amdgcn_raw_buffer_load_b32(br, (uint32_t)(4 * (lane + 64 * q)), 0, 0);
+        for (int q = 0; q < kWords; ++q)
+            bw[q] = __builtin_amdgcn_raw_buffer_load_b32(br, (uint32_t)(4 * (lane + 64 * q)), 0, 0);
         wd = __builtin_amdgcn_raw_buffer_load_b32(br, (uint32_t)(4 * (16 * sl + lane)), 0, 0);
     }
     // wave w: row r's maximum over the slabs' partials, and its factor
     {
-        m = lane < nslab ? m : 0u;
+        uint32_t m = 0;
+#pragma unroll
+        for (int i = 0; i < kParts; ++i) m = pm[i] > m ? pm[i] : m;
         m = (uint32_t)wave_max((float)m);
         if (lane == 0) {
             const float sv = to_f32<DT>((uint16_t)m);
@@ -638,7 +644,7 @@ __global__ __launch_bounds__(256) void code_slab_kernel(const uint16_t* __restri
     if (w == 0) {
         int32_t before = 0, all = 0;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
+        for (int q = 0; q < kWords; ++q) {
             const int32_t pc = __popc(bw[q]);
             all += pc;
             before += lane + 64 * q < 16 * sl ? pc : 0;

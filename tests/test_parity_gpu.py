@@ -61,7 +61,10 @@ def test_ragged_medium(dt):
                                       # the small-batch kernel with two 16-column groups per workgroup
                                       # (1, 2 and 4 row groups; 4 and 8 waves; a ragged last group)
                                       (16, 2048, 16384, "fp16"), (32, 1024, 8192, "fp16"),
-                                      (64, 512, 16384, "bf16"), (40, 800, 8200, "bf16")])
+                                      (64, 512, 16384, "bf16"), (40, 800, 8200, "bf16"),
+                                      # the small-batch path at its largest K, with a ragged K, and the
+                                      # tiled path just past it
+                                      (2, 65536, 8, "bf16"), (16, 40976, 24, "fp16"), (8, 65552, 16, "fp16")])
 def test_edge_shapes(M, K, N, dt):
     _banner(f"edge {M}x{K}x{N} {dt}")
     x, w = _case(M, K, N, dt, n_out=2, seed=M + K + N)
