@@ -143,7 +143,7 @@ int int8_matmul_products(int64_t M, int64_t K, int dtype, const int8_t* Wq, cons
  *                                   gathers these values itself
  *   scratch   internal (outlier flags; for small batches also per-row partial maxima)
  *   total     bytes (int8_matmul_workspace_bytes)
- *   small_batch  1 when these sizes take the small-batch path (M <= 64, K <= 65536 and
+ *   small_batch  1 when these sizes take the small-batch path (M <= 128, K <= 65536 and
  *             N small enough that streaming Wq once beats the tiled kernel), else 0 */
 typedef struct {
     size_t xq, xq_pitch, s_x, n_outliers, outliers, xo, xo_pitch, wo, scratch, total, small_batch;

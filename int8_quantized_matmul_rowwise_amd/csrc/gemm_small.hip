@@ -218,6 +218,16 @@ hipError_t launch_mg(const SmallParams& p, hipStream_t stream) {
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
+    if (mg > 4) {  // 65 to 128 rows: one column group, 8 waves
+        const unsigned grid = (unsigned)ceil_div(p.N, 16);
+        switch (mg) {
+            case 5: gemm_small_kernel<DT, 5, 1, 8, ACC_OUT><<<grid, 512, 0, stream>>>(p); break;
+            case 6: gemm_small_kernel<DT, 6, 1, 8, ACC_OUT><<<grid, 512, 0, stream>>>(p); break;
+            case 7: gemm_small_kernel<DT, 7, 1, 8, ACC_OUT><<<grid, 512, 0, stream>>>(p); break;
+            default: gemm_small_kernel<DT, 8, 1, 8, ACC_OUT><<<grid, 512, 0, stream>>>(p); break;
+        }
+        return hipGetLastError();
+    }
     const int64_t wg2 = ceil_div(p.N, 32);
     if (wg2 >= cus && (mg > 1 || wg2 >= 2 * (int64_t)cus)) {
         const unsigned grid = (unsigned)wg2;

@@ -32,19 +32,21 @@ hipError_t launch_compact(int64_t M, int64_t K, const uint32_t* partial, uint32_
 
 // Small-batch path (slab X pass, split-N product kernel), for M <= kSmallM and K <= kSmallK
 // where it beats the tiled path.  The split-N kernel streams Wq once at about 5 TB/s, and
-// every row of X adds about 2.2 % to that time (its re-reads of Xq from the cache); the
-// tiled kernel, with one 256-row tile, takes about K * 10.5 ns per round of 256-column
-// tiles over the compute units, whatever M.  Measured on MI355X (256 CUs), M = 16 to 64
-// on N x K = 36864 x 12288, 28672 x 8192, 16384 x 4096 and 8192 x 8192:
-// N * (1 + 0.022 M) / 5 TB/s < K * 10.5 ns * rounds, the test below, picks the faster
-// path in each of those cases.
-constexpr int64_t kSmallM = 64;
+// every row of X adds to that time (its re-reads of Xq from the cache): about 2.2 % per
+// row up to 64 rows (two column groups per workgroup), about 5 % beyond (one); the tiled
+// kernel, with one 256-row tile, takes about K * 10.5 ns per round of 256-column tiles
+// over the compute units, whatever M.  Measured on MI355X (256 CUs), M = 16 to 128 on
+// N x K = 36864 x 12288, 28672 x 8192, 16384 x 53248, 16384 x 4096, 14336 x 4096,
+// 8192 x 8192 and 4096 x 4096: N * (1 + c M) / 5 TB/s < K * 10.5 ns * rounds, the test
+// below, picks the faster path in each of those cases, or one within 2 %.
+constexpr int64_t kSmallM = 128;
 constexpr int64_t kSmallK = 65536;
 constexpr int64_t kRoutingCUs = 256;
 inline bool small_batch(int64_t M, int64_t K, int64_t N) {
     if (M > kSmallM || K > kSmallK) return false;
     const int64_t rounds = ((N + 255) / 256 + kRoutingCUs - 1) / kRoutingCUs;
-    return N * (1000 + 22 * M) < 52500000 * (rounds > 0 ? rounds : 1);
+    const int64_t c = M <= 64 ? 22 : 50;  // per mille of the Wq stream time per row
+    return N * (1000 + c * M) < 52500000 * (rounds > 0 ? rounds : 1);
 }
 
 struct XPassArgs {

@@ -406,7 +406,7 @@ __global__ __launch_bounds__(256) void code_rows_kernel(const uint16_t* __restri
 // block scan of the words' popcounts, one word per thread: K <= 32768), the row maxima
 // over the non-outlier columns (per row in LDS, one atomic per wave when the wave's 64
 // chunks lie in one row) and the coding.  The same per-chunk arithmetic as the two-launch
-// path, so the results are the same bits.  All indices fit 32 bits (M <= 64, K <= 32768).
+// path, so the results are the same bits.  All indices fit 32 bits (M * K <= 32768).
 constexpr int kOneChunks = 4;
 constexpr int64_t kOneMaxElems = 1024 * kOneChunks * 8;
 
@@ -527,10 +527,10 @@ __global__ __launch_bounds__(1024) void xpass_one_kernel(const uint16_t* __restr
 }
 
 // The small-batch X pass past kOneMaxElems, in two wide launches over 512-column slabs
-// (64 chunks of 8 columns).  M <= 64 rows, so the workgroup of a slab sees every row of its
+// (64 chunks of 8 columns).  M <= 128 rows, so the workgroup of a slab sees every row of its
 // columns: which of them are outlier columns is known there exactly, and so are its rows'
 // maxima over the other columns.
-//   detect_slab (one workgroup of 16 waves per slab, 1 to 4 rows per wave held in
+//   detect_slab (one workgroup of 16 waves per slab, 1 to 8 rows per wave held in
 //     registers): the slab's bitmap words and, per row, the slab's largest magnitude
 //     pattern over its non-outlier columns (pmax);
 //   code_slab (one workgroup per slab and 4 rows, a wave per row): the rows' maxima (max
@@ -759,11 +759,13 @@ hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, ui
         if (a.dt == F16) {
             if (a.M <= 16) detect_slab_kernel<F16, 1><<<g1, 1024, 0, stream>>>(x, a.M, a.K, a.tau, bitmap, pmax, nslab);
             else if (a.M <= 32) detect_slab_kernel<F16, 2><<<g1, 1024, 0, stream>>>(x, a.M, a.K, a.tau, bitmap, pmax, nslab);
-            else detect_slab_kernel<F16, 4><<<g1, 1024, 0, stream>>>(x, a.M, a.K, a.tau, bitmap, pmax, nslab);
+            else if (a.M <= 64) detect_slab_kernel<F16, 4><<<g1, 1024, 0, stream>>>(x, a.M, a.K, a.tau, bitmap, pmax, nslab);
+            else detect_slab_kernel<F16, 8><<<g1, 1024, 0, stream>>>(x, a.M, a.K, a.tau, bitmap, pmax, nslab);
         } else {
             if (a.M <= 16) detect_slab_kernel<BF16, 1><<<g1, 1024, 0, stream>>>(x, a.M, a.K, a.tau, bitmap, pmax, nslab);
             else if (a.M <= 32) detect_slab_kernel<BF16, 2><<<g1, 1024, 0, stream>>>(x, a.M, a.K, a.tau, bitmap, pmax, nslab);
-            else detect_slab_kernel<BF16, 4><<<g1, 1024, 0, stream>>>(x, a.M, a.K, a.tau, bitmap, pmax, nslab);
+            else if (a.M <= 64) detect_slab_kernel<BF16, 4><<<g1, 1024, 0, stream>>>(x, a.M, a.K, a.tau, bitmap, pmax, nslab);
+            else detect_slab_kernel<BF16, 8><<<g1, 1024, 0, stream>>>(x, a.M, a.K, a.tau, bitmap, pmax, nslab);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -64,7 +64,10 @@ def test_ragged_medium(dt):
                                       (64, 512, 16384, "bf16"), (40, 800, 8200, "bf16"),
                                       # the small-batch path at its largest K, with a ragged K, and the
                                       # tiled path just past it
-                                      (2, 65536, 8, "bf16"), (16, 40976, 24, "fp16"), (8, 65552, 16, "fp16")])
+                                      (2, 65536, 8, "bf16"), (16, 40976, 24, "fp16"), (8, 65552, 16, "fp16"),
+                                      # 65 to 128 rows on the small-batch path (5 to 8 row groups), one
+                                      # of them through the one-workgroup X pass
+                                      (80, 1024, 512, "fp16"), (128, 2048, 264, "bf16"), (100, 304, 136, "fp16")])
 def test_edge_shapes(M, K, N, dt):
     _banner(f"edge {M}x{K}x{N} {dt}")
     x, w = _case(M, K, N, dt, n_out=2, seed=M + K + N)
@@ -168,7 +171,7 @@ def test_zero_rows_and_zero_weight_columns():
 
 
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
-@pytest.mark.parametrize("M", [13, 70])  # small-batch path and tiled path
+@pytest.mark.parametrize("M", [13, 70, 140])  # small-batch path (one and five row groups) and tiled path
 def test_lattice_closed_form_exact_on_gpu(dt, M):
     # power-of-two lattice: every step is exact, so Y must equal RN_T(exact) bitwise,
     # outlier part included (its sums are exact integers in any order)
@@ -318,14 +321,15 @@ def _sweep_rows(dt, width=None):
 def test_row_quantizer_exhaustive_sweep(dt, layout):
     """X side: s_x and every code bitwise against the oracle, tau = inf (no outliers),
     through each row-coding configuration: rows longer than the register hold (read
-    twice), rows held in registers at each hold size (K <= 32768, 16384, 8192; M > 64),
-    and the small-batch launch (M <= 64)."""
+    twice), rows held in registers at each hold size (K <= 32768, 16384, 8192; M > 128),
+    and the small-batch launch (64 rows)."""
     width = {"two_reads": None, "hold16": 32768, "hold8": 16384, "hold4": 8192, "small_batch": 32768}[layout]
     Xb = _sweep_rows(dt, width)
     if layout == "small_batch":
         Xb = Xb[:64]
-    elif Xb.shape[0] <= 64:
-        Xb = np.concatenate([Xb, Xb[::-1]])  # past the small-batch switch
+    else:
+        while Xb.shape[0] <= 128:  # past the small-batch switch
+            Xb = np.concatenate([Xb, Xb[::-1]])
     M, K = Xb.shape
     _banner(f"row quantizer sweep {dt} {layout}: {M} x {K}")
     X = workloads.from_bits(Xb, dt).cuda()
