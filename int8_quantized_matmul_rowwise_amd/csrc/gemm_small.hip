@@ -1,5 +1,5 @@
-// Products and epilogue of the LLM.int8() matmul for a small batch (M <= 64 tokens: the
-// decode shape).  The same arithmetic as the tiled kernel (exact int32 C = Xq Wq^T on i8
+// Products and epilogue of the LLM.int8() matmul for a small batch (M <= 128 tokens: the
+// decode shapes).  The same arithmetic as the tiled kernel (exact int32 C = Xq Wq^T on i8
 // MFMA, fp32 F = X[:,O] Wq[:,O]^T on 16-bit MFMA, the same epilogue op sequence), laid
 // out for an HBM-bound product: the weight is read once, so every workgroup streams its
 // own 16 or 32 rows of Wq (output columns) straight from HBM into registers -- no LDS
@@ -207,10 +207,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(SmallParams p) {
     }
 }
 
-// Two column groups per workgroup when that still gives every compute unit a workgroup
-// (and, for one row group, two: with one the single 16-column layout is faster), with 8
-// waves for 3 or 4 row groups; else one column group and 4 waves.  Measured on MI355X,
-// N x K = 36864 x 12288, 28672 x 8192, 16384 x 4096 and 8192 x 8192, M = 16 to 64.
+// Up to 4 row groups: two column groups per workgroup when that still gives every compute
+// unit a workgroup (and, for one row group, two: with one the single 16-column layout is
+// faster), with 8 waves for 3 or 4 row groups; else one column group and 4 waves.  5 to 8
+// row groups: one column group and 8 waves.  Measured on MI355X, N x K = 36864 x 12288,
+// 28672 x 8192, 16384 x 4096, 14336 x 4096, 8192 x 8192 and 4096 x 4096, M = 16 to 128.
 template <int DT, bool ACC_OUT>
 hipError_t launch_mg(const SmallParams& p, hipStream_t stream) {
     const int64_t mg = ceil_div(p.M, 16);
