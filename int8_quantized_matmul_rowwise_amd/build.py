@@ -18,7 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libllmint8.so")
-SOURCES = ["api.hip", "xpass.hip", "weight.hip", "gemm.hip", "gemm_small.hip", "codec.hip", "gemm_group.hip"]
+SOURCES = ["api.hip", "xpass.hip", "weight.hip", "gemm.hip", "gemm_small.hip", "codec.hip", "gemm_group.hip",
+           "gemm_group_small.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

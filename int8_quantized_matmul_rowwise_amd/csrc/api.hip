@@ -519,7 +519,9 @@ int group_common(const void* X, int64_t M, int64_t K, int dtype, int64_t group, 
     float* rg = (float*)(ws + L.rg);
     hipError_t e = hipSuccess;
     if (xpass) e = launch_group_xpass(dtype, X, M, K, group, Xq, s_x, rg, st);
-    if (e == hipSuccess && products && N > 0) e = launch_gemm_group(dtype, Xq, rg, Wq, w_scale, M, N, K, group, Y, st);
+    if (e == hipSuccess && products && N > 0)
+        e = group_small_batch(M, K, N, group) ? launch_gemm_group_small(dtype, Xq, rg, Wq, w_scale, M, N, K, group, Y, st)
+                                              : launch_gemm_group(dtype, Xq, rg, Wq, w_scale, M, N, K, group, Y, st);
     return hip_status(e);
 }
 

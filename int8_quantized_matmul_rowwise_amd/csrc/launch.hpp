@@ -118,5 +118,10 @@ hipError_t launch_group_xpass(int dt, const void* X, int64_t M, int64_t K, int64
 // Y (M x N, 16-bit) = the group-wise product (per-group int32 partials folded into fp32)
 hipError_t launch_gemm_group(int dt, const int8_t* Xq, const float* rg, const int8_t* Wq, const float* s_w, int64_t M,
                              int64_t N, int64_t K, int64_t G, void* Y, hipStream_t stream);
+// Small batches of the group-wise path (M <= 64, K / G <= 64, where small_batch holds):
+// the split-N group kernel.
+bool group_small_batch(int64_t M, int64_t K, int64_t N, int64_t G);
+hipError_t launch_gemm_group_small(int dt, const int8_t* Xq, const float* rg, const int8_t* Wq, const float* s_w,
+                                   int64_t M, int64_t N, int64_t K, int64_t G, void* Y, hipStream_t stream);
 
 }  // namespace llmint8

@@ -62,6 +62,11 @@ def _case(M, K, N, dt, seed, n_outliers=3):
     (64, 8192, 128, 4096),    # the largest group
     (513, 3072, 392, 1024),   # three groups of 1024 (the group size the pages' GPTQ snippet uses)
     (1, 128, 8, 128),         # one row, one group, one 8-column segment
+    # small batches (the split-N group kernel): 16-step groups, 2-step groups split over two
+    # of the four waves, three row groups with a ragged last column group
+    (16, 8192, 512, 1024),
+    (48, 2048, 264, 128),
+    (33, 1536, 8200, 512),
 ])
 def test_group_parity(dt, M, K, N, G):
     print(f"\n[case] group {dt} {M}x{K}x{N} G={G}", flush=True)
