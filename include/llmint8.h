@@ -42,6 +42,20 @@
  *     X, W, Wq, Y and the workspace must be 16-byte aligned; w_scale 4-byte aligned.
  *   - Non-finite inputs, and nonzero vectors whose absmax is below 2^-120 (where
  *     127/s overflows fp32; bf16 only), are outside the contract.
+ *   - Environment (read on every call, host side only):
+ *       LLMINT8_LOG=1        prints each call's sizes, dtype, threshold, path (tiled or
+ *                            small batch) and each launch ("stage") to stderr.
+ *       LLMINT8_FAULT=<stage> test switch, a dry run: nothing is enqueued; each stage the
+ *                            call reaches before the named one is taken as done and the
+ *                            named one as failed, so the call returns LLMINT8_EHIP and
+ *                            reports nothing as done (int8_matmul_stats leaves its host
+ *                            output unwritten).  A call whose path lacks that stage returns
+ *                            LLMINT8_OK without having enqueued anything.  Stage names are
+ *                            the ones LLMINT8_LOG prints (detect, compact, code_rows,
+ *                            xpass_small, gemm, gemm_small, weight, list_bitmap, gather_wo,
+ *                            stats_copy, stats_sync, stats_copy_cols, group_colmax,
+ *                            quantize_weight_groups, group_xpass, gemm_group,
+ *                            gemm_group_small, fill_zero, block_quantize, block_dequantize).
  */
 #ifndef LLMINT8_H
 #define LLMINT8_H

@@ -20,7 +20,8 @@ from typing import Optional, Tuple
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libllmint8.so")
+# LLMINT8_LIB: another build of the same sources (the host-sanitized test build)
+LIB_PATH = os.environ.get("LLMINT8_LIB") or os.path.join(HERE, "libllmint8.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "llmint8.h")
 
 F16, BF16 = 0, 1

@@ -1,7 +1,12 @@
 // C-ABI entry points of llmint8 (declared and documented in include/llmint8.h).
 // Validation happens before anything is enqueued; HIP failures map to LLMINT8_EHIP.
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <atomic>
+#include <mutex>
 
 #include "../../include/llmint8.h"
 #include "common.hpp"
@@ -60,8 +65,9 @@ Layout make_layout(int64_t M, int64_t K, int64_t N) {
     off = align_up(off + 4 * k);
     L.xo = off;
     off = align_up(off + 2 * m * L.xo_pitch);
+    // W_O: the tiled path's gathered Wq[:,O]; the small-batch kernel gathers it itself
     L.wo = off;
-    off = align_up(off + 2 * n * L.xo_pitch);
+    off = align_up(off + (small_batch(M, K, N) ? 0 : 2 * n * L.xo_pitch));
     L.bitmap = off;
     off = align_up(off + 4 * kw);
     L.partial = off;
@@ -72,9 +78,48 @@ Layout make_layout(int64_t M, int64_t K, int64_t N) {
     return L;
 }
 
+// ---- failure injection and logging (host layer only; both read the environment per call)
+//   LLMINT8_FAULT=<stage>  dry run: nothing is enqueued; every stage the call reaches before
+//                          the named one counts as done, the named one as failed, so the
+//                          error path (LLMINT8_EHIP, nothing reported as done) runs on a
+//                          machine without a GPU.  A call whose path does not contain the
+//                          stage returns LLMINT8_OK having enqueued nothing.
+//   LLMINT8_LOG=1          each call's sizes, dtype, threshold and path, and each stage, on
+//                          stderr.
+const char* fault_stage() {
+    const char* f = getenv("LLMINT8_FAULT");
+    return f && *f ? f : nullptr;
+}
+
+bool log_on() {
+    const char* l = getenv("LLMINT8_LOG");
+    return l && *l && strcmp(l, "0") != 0;
+}
+
+const char* dtype_name(int dt) { return dt == LLMINT8_F16 ? "fp16" : "bf16"; }
+
+// tau: NaN where the call takes no threshold
+void log_call(const char* fn, int64_t M, int64_t K, int64_t N, int dt, float tau, const char* path) {
+    if (!log_on()) return;
+    char t[32] = "";
+    if (!isnan(tau)) snprintf(t, sizeof t, " threshold=%g", (double)tau);
+    fprintf(stderr, "[llmint8] %s M=%lld K=%lld N=%lld dtype=%s%s path=%s%s\n", fn, (long long)M, (long long)K,
+            (long long)N, dtype_name(dt), t, path, fault_stage() ? " (dry run)" : "");
+}
+
+// Run one stage of a call: `launch` enqueues it and returns its HIP status.
+template <class Launch>
+hipError_t stage(const char* name, Launch&& launch) {
+    const char* f = fault_stage();
+    const bool fail = f && strcmp(f, name) == 0;
+    if (log_on()) fprintf(stderr, "[llmint8]   stage %s%s\n", name, fail ? ": injected failure" : (f ? ": skipped" : ""));
+    if (f) return fail ? hipErrorLaunchFailure : hipSuccess;
+    return launch();
+}
+
 int hip_status(hipError_t e) {
     if (e == hipSuccess) return LLMINT8_OK;
-    (void)hipGetLastError();
+    if (!fault_stage()) (void)hipGetLastError();  // consume the sticky error (an injected one has none)
     return LLMINT8_EHIP;
 }
 
@@ -97,9 +142,10 @@ int run_xpass(const void* X, int64_t M, int64_t K, int dtype, float tau, const i
     a.s_x = (float*)(ws + L.s_x);
     a.XO = ws + L.xo;
     a.xo_pitch = (int64_t)L.xo_pitch;
-    if (small_batch(M, K, N)) return hip_status(launch_xpass_small(a, O, nO, bitmap, (uint32_t*)(ws + L.pmax), st));
-    hipError_t e = launch_detect(dtype, X, M, K, tau, partial, st);
-    if (e == hipSuccess) e = launch_compact(M, K, partial, bitmap, O, nO, st);
+    if (small_batch(M, K, N))
+        return hip_status(stage("xpass_small", [&] { return launch_xpass_small(a, O, nO, bitmap, (uint32_t*)(ws + L.pmax), st); }));
+    hipError_t e = stage("detect", [&] { return launch_detect(dtype, X, M, K, tau, partial, st); });
+    if (e == hipSuccess) e = stage("compact", [&] { return launch_compact(M, K, partial, bitmap, O, nO, st); });
     if (e == hipSuccess) {
         a.M = M;
         a.K = K;
@@ -114,7 +160,7 @@ int run_xpass(const void* X, int64_t M, int64_t K, int dtype, float tau, const i
         a.xo_pitch = (int64_t)L.xo_pitch;
         a.Wq = Wq;
         a.WO = ws + L.wo;
-        e = launch_code_rows(a, bitmap, O, nO, st);
+        e = stage("code_rows", [&] { return launch_code_rows(a, bitmap, O, nO, st); });
     }
     return hip_status(e);
 }
@@ -134,6 +180,7 @@ int prepare_common(const void* X, int64_t M, int64_t K, int dtype, const int8_t*
         overlap(workspace, L.total, Wq, (size_t)N * (size_t)K))
         return LLMINT8_EINVAL;
     if (M == 0 || !enqueue) return LLMINT8_OK;
+    log_call("x pass", M, K, N, dtype, threshold, small_batch(M, K, N) ? "small_batch" : "tiled");
     return run_xpass(X, M, K, dtype, threshold, N > 0 ? Wq : nullptr, N, (int8_t*)workspace, L,
                      (hipStream_t)stream);
 }
@@ -162,6 +209,8 @@ int products_common(int64_t M, int64_t K, int dtype, const int8_t* Wq, const flo
             return LLMINT8_EINVAL;
     }
     if (M == 0 || N == 0 || !enqueue) return LLMINT8_OK;
+    log_call(acc ? "products (accumulator dump)" : (WO_fixed ? "products (fixed outlier set)" : "products"), M, K, N,
+             dtype, NAN, small_batch(M, K, N) ? "small_batch" : "tiled");
     const int8_t* ws = (const int8_t*)workspace;
     GemmArgs g;
     g.dt = dtype;
@@ -183,8 +232,8 @@ int products_common(int64_t M, int64_t K, int dtype, const int8_t* Wq, const flo
     g.Y = Y;
     g.C_acc = C;
     g.F_acc = F;
-    if (small_batch(M, K, N)) return hip_status(launch_gemm_small(g, (hipStream_t)stream));
-    return hip_status(launch_gemm(g, (hipStream_t)stream));
+    if (small_batch(M, K, N)) return hip_status(stage("gemm_small", [&] { return launch_gemm_small(g, (hipStream_t)stream); }));
+    return hip_status(stage("gemm", [&] { return launch_gemm(g, (hipStream_t)stream); }));
 }
 
 // X pass against a caller's fixed outlier set: its bitmap (as one partial), the
@@ -195,8 +244,8 @@ int run_xpass_fixed(const void* X, int64_t M, int64_t K, int dtype, const int32_
     uint32_t* bitmap = (uint32_t*)(ws + L.bitmap);
     int32_t* O = (int32_t*)(ws + L.outliers);
     int32_t* n_out = (int32_t*)(ws + L.n_outliers);
-    hipError_t e = launch_list_bitmap(K, Ofix, nO, partial, st);
-    if (e == hipSuccess) e = launch_compact(1, K, partial, bitmap, O, n_out, st);
+    hipError_t e = stage("list_bitmap", [&] { return launch_list_bitmap(K, Ofix, nO, partial, st); });
+    if (e == hipSuccess) e = stage("compact", [&] { return launch_compact(1, K, partial, bitmap, O, n_out, st); });
     if (e == hipSuccess) {
         XPassArgs a;
         a.dt = dtype;
@@ -215,7 +264,7 @@ int run_xpass_fixed(const void* X, int64_t M, int64_t K, int dtype, const int32_
         a.xo_pitch = (int64_t)L.xo_pitch;
         a.Wq = nullptr;
         a.WO = nullptr;
-        e = launch_code_rows(a, bitmap, O, n_out, st);
+        e = stage("code_rows", [&] { return launch_code_rows(a, bitmap, O, n_out, st); });
     }
     return hip_status(e);
 }
@@ -259,7 +308,8 @@ LLMINT8_API int int8_quantize_weight(const void* W, int64_t K, int64_t N, int dt
     if (overlap(W, (size_t)K * N * 2, Wq, (size_t)K * N) || overlap(W, (size_t)K * N * 2, w_scale, (size_t)N * 4) ||
         overlap(Wq, (size_t)K * N, w_scale, (size_t)N * 4))
         return LLMINT8_EINVAL;
-    return hip_status(launch_weight(dtype, W, K, N, Wq, w_scale, nullptr, (hipStream_t)stream));
+    log_call("int8_quantize_weight", 0, K, N, dtype, NAN, "weight");
+    return hip_status(stage("weight", [&] { return launch_weight(dtype, W, K, N, Wq, w_scale, nullptr, (hipStream_t)stream); }));
 }
 
 LLMINT8_API size_t int8_matmul_workspace_bytes(int64_t M, int64_t K, int64_t N) {
@@ -317,18 +367,24 @@ LLMINT8_API int int8_matmul_stats(const void* X, int64_t M, int64_t K, int dtype
     }
     hipStream_t st = (hipStream_t)stream;
     int8_t* ws = (int8_t*)workspace;
-    hipError_t e = launch_detect(dtype, X, M, K, threshold, (uint32_t*)(ws + L.partial), st);
+    log_call("int8_matmul_stats", M, K, 0, dtype, threshold, "detect");
+    hipError_t e = stage("detect", [&] { return launch_detect(dtype, X, M, K, threshold, (uint32_t*)(ws + L.partial), st); });
     if (e == hipSuccess)
-        e = launch_compact(M, K, (const uint32_t*)(ws + L.partial), (uint32_t*)(ws + L.bitmap),
-                           (int32_t*)(ws + L.outliers), (int32_t*)(ws + L.n_outliers), st);
+        e = stage("compact", [&] {
+            return launch_compact(M, K, (const uint32_t*)(ws + L.partial), (uint32_t*)(ws + L.bitmap),
+                                  (int32_t*)(ws + L.outliers), (int32_t*)(ws + L.n_outliers), st);
+        });
     int32_t n = 0;
-    if (e == hipSuccess) e = hipMemcpyAsync(&n, ws + L.n_outliers, 4, hipMemcpyDeviceToHost, st);
-    if (e == hipSuccess) e = hipStreamSynchronize(st);
-    if (e == hipSuccess && outlier_cols && n > 0) {
-        e = hipMemcpyAsync(outlier_cols, ws + L.outliers, (size_t)n * 4, hipMemcpyDeviceToDevice, st);
-        if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e == hipSuccess)
+        e = stage("stats_copy", [&] { return hipMemcpyAsync(&n, ws + L.n_outliers, 4, hipMemcpyDeviceToHost, st); });
+    if (e == hipSuccess) e = stage("stats_sync", [&] { return hipStreamSynchronize(st); });
+    if (e == hipSuccess && outlier_cols && (n > 0 || fault_stage())) {
+        e = stage("stats_copy_cols", [&] {
+            hipError_t c = hipMemcpyAsync(outlier_cols, ws + L.outliers, (size_t)n * 4, hipMemcpyDeviceToDevice, st);
+            return c == hipSuccess ? hipStreamSynchronize(st) : c;
+        });
     }
-    if (e != hipSuccess) return hip_status(e);
+    if (e != hipSuccess) return hip_status(e);  // *n_outlier_cols is left as it was
     *n_outlier_cols = n;
     return LLMINT8_OK;
 }
@@ -357,7 +413,8 @@ LLMINT8_API int int8_blockwise_quantize(const float* x, int64_t n, int64_t block
     if (overlap(x, (size_t)n * 4, q, (size_t)n) || overlap(x, (size_t)n * 4, absmax, (size_t)nb * 4) ||
         overlap(q, (size_t)n, absmax, (size_t)nb * 4))
         return LLMINT8_EINVAL;
-    return hip_status(launch_block_quantize(x, n, block, q, absmax, (hipStream_t)stream));
+    log_call("int8_blockwise_quantize", 0, block, n, LLMINT8_F16, NAN, "codec");
+    return hip_status(stage("block_quantize", [&] { return launch_block_quantize(x, n, block, q, absmax, (hipStream_t)stream); }));
 }
 
 LLMINT8_API int int8_blockwise_dequantize(const int8_t* q, const float* absmax, int64_t n, int64_t block, float* x,
@@ -368,7 +425,8 @@ LLMINT8_API int int8_blockwise_dequantize(const int8_t* q, const float* absmax, 
     if (!x || !q || !absmax || !aligned(x, 16) || !aligned(q, 4) || !aligned(absmax, 4)) return LLMINT8_EINVAL;
     if (overlap(x, (size_t)n * 4, q, (size_t)n) || overlap(x, (size_t)n * 4, absmax, (size_t)nb * 4))
         return LLMINT8_EINVAL;
-    return hip_status(launch_block_dequantize(q, absmax, n, block, x, (hipStream_t)stream));
+    log_call("int8_blockwise_dequantize", 0, block, n, LLMINT8_F16, NAN, "codec");
+    return hip_status(stage("block_dequantize", [&] { return launch_block_dequantize(q, absmax, n, block, x, (hipStream_t)stream); }));
 }
 
 // ---- fixed (caller-supplied) outlier dimensions
@@ -402,9 +460,10 @@ LLMINT8_API int int8_quantize_weight_fixed(const void* W, int64_t K, int64_t N, 
         return LLMINT8_EINVAL;
     hipStream_t st = (hipStream_t)stream;
     uint32_t* skip = (uint32_t*)workspace;
-    hipError_t e = launch_list_bitmap(K, outlier_cols, nO, skip, st);
-    if (e == hipSuccess) e = launch_weight(dtype, W, K, N, Wq, w_scale, K > 0 ? skip : nullptr, st);
-    if (e == hipSuccess) e = launch_gather_wo(W, K, N, outlier_cols, nO, P, W_O, st);
+    log_call("int8_quantize_weight_fixed", 0, K, N, dtype, NAN, "weight");
+    hipError_t e = stage("list_bitmap", [&] { return launch_list_bitmap(K, outlier_cols, nO, skip, st); });
+    if (e == hipSuccess) e = stage("weight", [&] { return launch_weight(dtype, W, K, N, Wq, w_scale, K > 0 ? skip : nullptr, st); });
+    if (e == hipSuccess) e = stage("gather_wo", [&] { return launch_gather_wo(W, K, N, outlier_cols, nO, P, W_O, st); });
     return hip_status(e);
 }
 
@@ -433,6 +492,7 @@ LLMINT8_API int int8_matmul_fixed(const void* X, int64_t M, int64_t K, int dtype
               overlap(Y, (size_t)M * (size_t)N * 2, outlier_cols, (size_t)nO * 4)))
         return LLMINT8_EINVAL;
     if (M == 0) return LLMINT8_OK;
+    log_call("fixed x pass", M, K, N, dtype, NAN, "fixed");
     rc = run_xpass_fixed(X, M, K, dtype, outlier_cols, nO, (int8_t*)workspace, L, (hipStream_t)stream);
     if (rc) return rc;
     return products_common(M, K, dtype, Wq, w_scale, N, Y, nullptr, nullptr, workspace, workspace_bytes, stream, true,
@@ -476,8 +536,10 @@ LLMINT8_API int int8_quantize_weight_group(const void* W, int64_t K, int64_t N, 
     if (!W || !Wq || !w_scale || !aligned(W, 16) || !aligned(Wq, 16) || !aligned(w_scale, 4)) return LLMINT8_EINVAL;
     if (overlap(W, wb, Wq, qb) || overlap(W, wb, w_scale, sb) || overlap(Wq, qb, w_scale, sb)) return LLMINT8_EINVAL;
     hipStream_t st = (hipStream_t)stream;
-    hipError_t e = launch_group_colmax(dtype, W, K, N, group, w_scale, st);
-    if (e == hipSuccess) e = launch_quantize_weight_groups(dtype, W, K, N, w_scale, group, Wq, st);
+    log_call("int8_quantize_weight_group", 0, K, N, dtype, NAN, "weight");
+    hipError_t e = stage("group_colmax", [&] { return launch_group_colmax(dtype, W, K, N, group, w_scale, st); });
+    if (e == hipSuccess)
+        e = stage("quantize_weight_groups", [&] { return launch_quantize_weight_groups(dtype, W, K, N, w_scale, group, Wq, st); });
     return hip_status(e);
 }
 
@@ -500,7 +562,9 @@ int group_common(const void* X, int64_t M, int64_t K, int dtype, int64_t group, 
     hipStream_t st = (hipStream_t)stream;
     if (products && N > 0) {
         if (!Y || !aligned(Y, 16)) return LLMINT8_EINVAL;
-        if (K == 0) return hip_status(launch_fill_zero((float*)Y, M * N / 2, st));  // the empty sum; N is even
+        if (K == 0) log_call("int8_matmul_group", M, K, N, dtype, NAN, "empty sum");
+        if (K == 0)  // the empty sum; N is even
+            return hip_status(stage("fill_zero", [&] { return launch_fill_zero((float*)Y, M * N / 2, st); }));
         if (!Wq || !w_scale || !aligned(Wq, 16) || !aligned(w_scale, 4)) return LLMINT8_EINVAL;
     }
     if (K == 0) return LLMINT8_OK;
@@ -518,10 +582,13 @@ int group_common(const void* X, int64_t M, int64_t K, int dtype, int64_t group, 
     float* s_x = (float*)(ws + L.s_x);
     float* rg = (float*)(ws + L.rg);
     hipError_t e = hipSuccess;
-    if (xpass) e = launch_group_xpass(dtype, X, M, K, group, Xq, s_x, rg, st);
+    const bool small = products && N > 0 && group_small_batch(M, K, N, group);
+    log_call(xpass ? (products ? "int8_matmul_group" : "int8_matmul_group_prepare") : "int8_matmul_group_products", M, K,
+             N, dtype, NAN, small ? "group_small_batch" : "group_tiled");
+    if (xpass) e = stage("group_xpass", [&] { return launch_group_xpass(dtype, X, M, K, group, Xq, s_x, rg, st); });
     if (e == hipSuccess && products && N > 0)
-        e = group_small_batch(M, K, N, group) ? launch_gemm_group_small(dtype, Xq, rg, Wq, w_scale, M, N, K, group, Y, st)
-                                              : launch_gemm_group(dtype, Xq, rg, Wq, w_scale, M, N, K, group, Y, st);
+        e = small ? stage("gemm_group_small", [&] { return launch_gemm_group_small(dtype, Xq, rg, Wq, w_scale, M, N, K, group, Y, st); })
+                  : stage("gemm_group", [&] { return launch_gemm_group(dtype, Xq, rg, Wq, w_scale, M, N, K, group, Y, st); });
     return hip_status(e);
 }
 

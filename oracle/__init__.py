@@ -19,6 +19,8 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 LIB = os.path.join(HERE, "liborc.so")
+# LLMINT8_ORACLE_LIB: a prebuilt copy of the oracle (the sanitized test build); used as is
+ALT_LIB = os.environ.get("LLMINT8_ORACLE_LIB")
 DT = {"fp16": 0, "bf16": 1}
 
 _lock = threading.Lock()
@@ -26,13 +28,17 @@ _lib = None
 _SIGS = {}
 
 
-def build() -> str:
-    """Compile the oracle (gcc, no fast-math, no contraction).  Returns the library path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
+def build(out: str = LIB, sanitize: bool = False) -> str:
+    """Compile the oracle (gcc, no fast-math, no contraction).  Returns the library path.
+    sanitize: AddressSanitizer + UndefinedBehaviorSanitizer (test build; load it with the
+    sanitizer runtime preloaded and LLMINT8_ORACLE_LIB pointing at it)."""
+    tmp = out + ".tmp%d" % os.getpid()
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"] \
+        if sanitize else []
     subprocess.check_call(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
-                           "-fPIC", "-shared", "-Wall", "-Wextra", "-o", tmp, SRC, "-lm"])
-    os.replace(tmp, LIB)
-    return LIB
+                           "-fPIC", "-shared", "-Wall", "-Wextra", *san, "-o", tmp, SRC, "-lm"])
+    os.replace(tmp, out)
+    return out
 
 
 _P = ctypes.c_void_p
@@ -44,10 +50,13 @@ def _load():
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(LIB) or os.path.getmtime(LIB) < max(os.path.getmtime(SRC),
-                                                                   os.path.getmtime(os.path.join(HERE, "oracle.h"))):
-            build()
-        lib = ctypes.CDLL(LIB)
+        if ALT_LIB:
+            lib = ctypes.CDLL(ALT_LIB)
+        else:
+            if not os.path.exists(LIB) or os.path.getmtime(LIB) < max(os.path.getmtime(SRC),
+                                                                       os.path.getmtime(os.path.join(HERE, "oracle.h"))):
+                build()
+            lib = ctypes.CDLL(LIB)
         sig = {
             "orc_set_threads": (ctypes.c_int, [ctypes.c_int]),
             "orc_to_f32_n": (None, [_P, _I64, ctypes.c_int, _P]),

@@ -36,14 +36,17 @@ def test_status_strings():
 
 
 def test_workspace_layout_regions_fit_and_align():
-    for (M, K, N) in [(1, 16, 8), (32, 256, 128), (300, 1040, 520), (4096, 12288, 36864), (0, 64, 8), (5, 0, 8)]:
+    for (M, K, N) in [(1, 16, 8), (32, 256, 128), (300, 1040, 520), (4096, 12288, 36864), (0, 64, 8), (5, 0, 8),
+                      (16, 8192, 8192)]:
         lay = L.int8_matmul_workspace_layout(M, K, N)
         assert lay["total"] == L.int8_matmul_workspace_bytes(M, K, N)
         assert lay["xq_pitch"] % 256 == 0 and lay["xq_pitch"] >= K
         assert lay["xo_pitch"] % 32 == 0 and lay["xo_pitch"] >= K
+        # the small-batch product kernel gathers Wq[:,O] itself: no W_O region then
+        wo = 0 if lay["small_batch"] else 2 * N * lay["xo_pitch"]
         regions = sorted([(lay["xq"], M * lay["xq_pitch"]), (lay["s_x"], 4 * M), (lay["n_outliers"], 4),
                           (lay["outliers"], 4 * K), (lay["xo"], 2 * M * lay["xo_pitch"]),
-                          (lay["wo"], 2 * N * lay["xo_pitch"]), (lay["scratch"], 4 * math.ceil(K / 32))])
+                          (lay["wo"], wo), (lay["scratch"], 4 * math.ceil(K / 32))])
         for (o, n), (o2, _) in zip(regions, regions[1:]):
             assert o % 256 == 0 and o + n <= o2
         assert regions[-1][0] + regions[-1][1] <= lay["total"]
