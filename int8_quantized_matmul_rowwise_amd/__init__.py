@@ -246,7 +246,9 @@ def workspace_views(ws: torch.Tensor, M: int, K: int, N: int, dtype: torch.dtype
     P = int(math.ceil(n_o / 32) * 32)
     xq = b[L["xq"]: L["xq"] + M * L["xq_pitch"]].view(torch.int8).view(M, L["xq_pitch"]) if L["xq_pitch"] else None
     xo = b[L["xo"]: L["xo"] + 2 * M * L["xo_pitch"]].view(dtype).view(M, L["xo_pitch"]) if L["xo_pitch"] else None
-    wo = b[L["wo"]: L["wo"] + 2 * N * L["xo_pitch"]].view(dtype).view(N, L["xo_pitch"]) if L["xo_pitch"] else None
+    # the small-batch path has no W_O region (its product kernel gathers Wq[:,O] itself)
+    wo = (b[L["wo"]: L["wo"] + 2 * N * L["xo_pitch"]].view(dtype).view(N, L["xo_pitch"])
+          if L["xo_pitch"] and not L["small_batch"] else None)
     return {
         "n_outliers": n_o,
         "outliers": b[L["outliers"]: L["outliers"] + 4 * n_o].view(torch.int32),

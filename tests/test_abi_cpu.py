@@ -52,6 +52,18 @@ def test_workspace_layout_regions_fit_and_align():
         assert regions[-1][0] + regions[-1][1] <= lay["total"]
 
 
+def test_workspace_views_of_both_paths():
+    # the views of a workspace (a host buffer here) for a small-batch and a tiled layout
+    import torch
+    for (M, K, N, small) in [(40, 1040, 264, True), (300, 1040, 520, False), (16, 8192, 8192, True)]:
+        lay = L.int8_matmul_workspace_layout(M, K, N)
+        assert lay["small_batch"] == small
+        ws = torch.zeros(lay["total"], dtype=torch.uint8)
+        v = L.workspace_views(ws, M, K, N, torch.float16)
+        assert v["Xq"].shape == (M, K) and v["s_x"].numel() == M and v["n_outliers"] == 0
+        assert (v["WO"] is None) == small
+
+
 def _mm(**kw):
     a = dict(X=A16, M=4, K=64, dt=0, Wq=A16 * 2, s_w=A16 * 3, N=8, tau=6.0, Y=A16 * 4 + 0x100000,
              ws=A16 * 0x1000, wsb=1 << 30, stream=None)
