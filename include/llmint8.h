@@ -26,7 +26,9 @@
  *
  * Conventions for every call below.
  *   - Pointers are DEVICE pointers owned by the caller unless marked HOST.  The library
- *     allocates no memory and keeps no state between calls; it is re-entrant.
+ *     allocates no memory and keeps no state between calls; it is re-entrant.  (The one
+ *     exception, int8_matmul_noalloc at the end, works in a static device array of the
+ *     library's own instead of a caller workspace.)
  *   - `stream` is a hipStream_t (NULL: the default stream).  Calls only enqueue work on
  *     it and return before it runs, except int8_matmul_stats, which synchronizes it.
  *   - `dtype` is LLMINT8_F16 or LLMINT8_BF16; X, W and Y share it.
@@ -55,7 +57,8 @@
  *                            xpass_small, gemm, gemm_small, weight, list_bitmap, gather_wo,
  *                            stats_copy, stats_sync, stats_copy_cols, group_colmax,
  *                            quantize_weight_groups, group_xpass, gemm_group,
- *                            gemm_group_small, fill_zero, block_quantize, block_dequantize).
+ *                            gemm_group_small, fill_zero, block_quantize, block_dequantize,
+ *                            scratch_symbol).
  */
 #ifndef LLMINT8_H
 #define LLMINT8_H
@@ -278,6 +281,29 @@ int int8_matmul_group_prepare(const void* X, int64_t M, int64_t K, int dtype, in
 int int8_matmul_group_products(int64_t M, int64_t K, int dtype, int64_t group, const int8_t* Wq,
                                const float* w_scale, int64_t N, void* Y, void* workspace, size_t workspace_bytes,
                                void* stream);
+
+/*
+ * int8_matmul without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Arguments, result and status codes are int8_matmul's, minus the workspace: the same
+ * kernels run on a scratch array the library keeps in device memory,
+ * LLMINT8_NOALLOC_SCRATCH_BYTES bytes on every GPU the library runs on, held until the
+ * process ends.  The call allocates nothing (no hipMalloc, no allocating library routine);
+ * its first call on a device looks up that device's copy of the array.
+ *   Sizes: int8_matmul_workspace_bytes(M, K, N) must not exceed
+ *          LLMINT8_NOALLOC_SCRATCH_BYTES, else LLMINT8_EWORKSPACE and nothing is enqueued.
+ *          Small batches (M <= 128 on the small-batch path: e.g. 16 x 8192 x 8192 needs
+ *          under 1 MiB) fit; so do tiled calls of moderate size (the tiled path reserves
+ *          the worst case of every column an outlier, 2 N K bytes for the gathered weight
+ *          columns alone).
+ *   Concurrency: every call on one GPU works in that GPU's single array.  Calls that
+ *          overlap in time on one GPU (on different streams or host threads) race and
+ *          give undefined results; calls ordered on one stream are safe.  The array keeps
+ *          the last call's contents; no call needs any of it to start at zero.
+ */
+#define LLMINT8_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int int8_matmul_noalloc(const void* X, int64_t M, int64_t K, int dtype, const int8_t* Wq, const float* w_scale,
+                        int64_t N, float threshold, void* Y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -51,6 +51,7 @@ _SIGNATURES = {
     "int8_quantize_weight": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
     "int8_matmul_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
     "int8_matmul": (_I, [_P, _I64, _I64, _I, _P, _P, _I64, _F, _P, _P, _SZ, _P]),
+    "int8_matmul_noalloc": (_I, [_P, _I64, _I64, _I, _P, _P, _I64, _F, _P, _P]),
     "int8_matmul_stats": (_I, [_P, _I64, _I64, _I, _F, _P, _P, _P, _SZ, _P]),
     "int8_matmul_workspace_layout": (_I, [_I64, _I64, _I64, ctypes.POINTER(WorkspaceLayout)]),
     "int8_matmul_accumulators": (_I, [_P, _I64, _I64, _I, _P, _I64, _F, _P, _P, _P, _SZ, _P]),
@@ -171,6 +172,32 @@ def int8_matmul(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor, thresh
     ws = _workspace(workspace, nbytes, X.device)
     _check(lib().int8_matmul(_ptr(X), M, K, _DT[X.dtype], _ptr(Wq), _ptr(w_scale), N, float(threshold), _ptr(Y),
                              _ptr(ws), ws.numel(), _stream(X, stream)), "int8_matmul")
+    return Y
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # LLMINT8_NOALLOC_SCRATCH_BYTES
+
+
+def int8_matmul_noalloc(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor, threshold: float = 6.0,
+                        Y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """int8_matmul on the library's own device scratch (no workspace; the library call
+    allocates nothing -- pass Y to keep the binding from allocating it either)."""
+    _dev_tensor(X, "X")
+    if X.dtype not in _DT or X.dim() != 2:
+        raise TypeError("X must be a 2-D fp16 or bf16 tensor")
+    M, K = X.shape
+    _dev_tensor(Wq, "Wq", torch.int8)
+    _dev_tensor(w_scale, "w_scale", torch.float32)
+    N = Wq.shape[0]
+    if Wq.dim() != 2 or Wq.shape[1] != K or tuple(w_scale.shape) != (N,):
+        raise ValueError("Wq must be N x K and w_scale N")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=X.dtype, device=X.device)
+    _dev_tensor(Y, "Y", X.dtype)
+    if tuple(Y.shape) != (M, N):
+        raise ValueError("Y must be M x N")
+    _check(lib().int8_matmul_noalloc(_ptr(X), M, K, _DT[X.dtype], _ptr(Wq), _ptr(w_scale), N, float(threshold),
+                                     _ptr(Y), _stream(X, stream)), "int8_matmul_noalloc")
     return Y
 
 
@@ -435,7 +462,7 @@ def group_workspace_views(ws: torch.Tensor, M: int, K: int, group: int) -> dict:
 
 
 __all__ = [
-    "int8_quantize_weight", "int8_matmul", "int8_matmul_stats", "int8_matmul_prepare", "int8_matmul_products", "int8_matmul_workspace_bytes",
+    "int8_quantize_weight", "int8_matmul", "int8_matmul_noalloc", "int8_matmul_stats", "int8_matmul_prepare", "int8_matmul_products", "int8_matmul_workspace_bytes",
     "int8_matmul_workspace_layout", "int8_matmul_accumulators", "workspace_views", "LLMInt8Error", "lib",
     "int8_blockwise_quantize", "int8_blockwise_dequantize", "int8_quantize_weight_fixed", "int8_matmul_fixed",
     "status_string", "int8_quantize_weight_group", "int8_matmul_group", "int8_matmul_group_workspace_bytes",

@@ -273,13 +273,14 @@ int64_t fixed_pitch(int64_t nO) { return (nO + 31) / 32 * 32; }
 
 int matmul_common(const void* X, int64_t M, int64_t K, int dtype, const int8_t* Wq, const float* w_scale,
                   int64_t N, float threshold, void* Y, int32_t* C, float* F, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+                  size_t workspace_bytes, void* stream, bool enqueue = true) {
     // validate both stages before enqueueing either
     int rc = prepare_common(X, M, K, dtype, Wq, N, threshold, workspace, workspace_bytes, stream, false);
     if (rc) return rc;
     rc = products_common(M, K, dtype, Wq, w_scale, N, Y, C, F, workspace, workspace_bytes, stream, false);
     if (rc) return rc;
     if (Y && overlap(Y, (size_t)M * (size_t)N * 2, X, (size_t)M * (size_t)K * 2)) return LLMINT8_EINVAL;
+    if (!enqueue) return LLMINT8_OK;
     rc = prepare_common(X, M, K, dtype, Wq, N, threshold, workspace, workspace_bytes, stream, true);
     if (rc) return rc;
     return products_common(M, K, dtype, Wq, w_scale, N, Y, C, F, workspace, workspace_bytes, stream, true);
@@ -613,4 +614,62 @@ LLMINT8_API int int8_matmul_group_products(int64_t M, int64_t K, int dtype, int6
                                            size_t workspace_bytes, void* stream) {
     return group_common(nullptr, M, K, dtype, group, Wq, w_scale, N, Y, workspace, workspace_bytes, stream, false,
                         true);
+}
+
+// ---- int8_matmul without a caller workspace: the same kernels on a scratch array the
+// library keeps in device memory.  In host code `scratch` names a host-side stand-in, not
+// the device array: its device address is looked up per device (hipGetSymbolAddress, with
+// that device current) and only that address is handed to kernels.
+
+static __device__ __align__(256) int8_t scratch[LLMINT8_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+// Stands for the scratch address where nothing may dereference it: the argument checks, and
+// dry runs (LLMINT8_FAULT), which enqueue nothing.
+void* const kScratchStandIn = (void*)((uintptr_t)1 << 40);
+
+// The current device's copy of `scratch` (looked up on the first call on that device).
+hipError_t scratch_for_current_device(void** out) {
+    if (fault_stage()) {
+        *out = kScratchStandIn;
+        return stage("scratch_symbol", [] { return hipSuccess; });
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        p = g_scratch[dev].load(std::memory_order_acquire);
+        if (!p) {
+            e = stage("scratch_symbol", [&] { return hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)); });
+            if (e != hipSuccess) return e;
+            if (!p) return hipErrorInvalidSymbol;
+            g_scratch[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+}  // namespace
+
+LLMINT8_API int int8_matmul_noalloc(const void* X, int64_t M, int64_t K, int dtype, const int8_t* Wq,
+                                    const float* w_scale, int64_t N, float threshold, void* Y, void* stream) {
+    if (!Y && M > 0 && N > 0) return LLMINT8_EINVAL;
+    // every argument check of int8_matmul (sizes beyond the scratch: LLMINT8_EWORKSPACE) before any HIP call
+    int rc = matmul_common(X, M, K, dtype, Wq, w_scale, N, threshold, Y, nullptr, nullptr, kScratchStandIn,
+                           LLMINT8_NOALLOC_SCRATCH_BYTES, stream, false);
+    if (rc || M == 0) return rc;
+    void* ws = nullptr;
+    hipError_t e = scratch_for_current_device(&ws);
+    if (e != hipSuccess) return hip_status(e);
+    log_call("int8_matmul_noalloc", M, K, N, dtype, threshold, "library scratch");
+    return matmul_common(X, M, K, dtype, Wq, w_scale, N, threshold, Y, nullptr, nullptr, ws,
+                         LLMINT8_NOALLOC_SCRATCH_BYTES, stream);
 }
