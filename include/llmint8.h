@@ -266,6 +266,9 @@ int int8_quantize_weight_group(const void* W, int64_t K, int64_t N, int dtype, i
  * Inputs, Y and the workspace must not overlap (LLMINT8_EINVAL).
  */
 size_t int8_matmul_group_workspace_bytes(int64_t M, int64_t K, int64_t group);
+/* Which product kernel int8_matmul_group runs for these sizes: 1 the small-batch (split-N,
+ * weight-streaming) kernel, 0 the tiled one; a negative status for invalid sizes. */
+int int8_matmul_group_small_batch(int64_t M, int64_t K, int64_t N, int64_t group);
 int int8_matmul_group(const void* X, int64_t M, int64_t K, int dtype, int64_t group, const int8_t* Wq,
                       const float* w_scale, int64_t N, void* Y, void* workspace, size_t workspace_bytes,
                       void* stream);

@@ -64,6 +64,7 @@ _SIGNATURES = {
     "int8_blockwise_dequantize": (_I, [_P, _P, _I64, _I64, _P, _P]),
     "int8_quantize_weight_group": (_I, [_P, _I64, _I64, _I, _I64, _P, _P, _P]),
     "int8_matmul_group_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "int8_matmul_group_small_batch": (_I, [_I64, _I64, _I64, _I64]),
     "int8_matmul_group": (_I, [_P, _I64, _I64, _I, _I64, _P, _P, _I64, _P, _P, _SZ, _P]),
     "int8_matmul_group_prepare": (_I, [_P, _I64, _I64, _I, _I64, _P, _SZ, _P]),
     "int8_matmul_group_products": (_I, [_I64, _I64, _I, _I64, _P, _P, _I64, _P, _P, _SZ, _P]),
@@ -392,6 +393,13 @@ def int8_matmul_group_workspace_bytes(M: int, K: int, group: int) -> int:
     return int(lib().int8_matmul_group_workspace_bytes(M, K, group))
 
 
+def int8_matmul_group_small_batch(M: int, K: int, N: int, group: int) -> bool:
+    """True when int8_matmul_group takes the small-batch product kernel for these sizes."""
+    r = int(lib().int8_matmul_group_small_batch(M, K, N, group))
+    _check(min(r, 0), "int8_matmul_group_small_batch")
+    return r == 1
+
+
 def int8_matmul_group(X: torch.Tensor, Wq: torch.Tensor, w_scale: torch.Tensor, group: int = 1024,
                       Y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                       stream=None) -> torch.Tensor:
@@ -466,5 +474,5 @@ __all__ = [
     "int8_matmul_workspace_layout", "int8_matmul_accumulators", "workspace_views", "LLMInt8Error", "lib",
     "int8_blockwise_quantize", "int8_blockwise_dequantize", "int8_quantize_weight_fixed", "int8_matmul_fixed",
     "status_string", "int8_quantize_weight_group", "int8_matmul_group", "int8_matmul_group_workspace_bytes",
-    "group_workspace_views", "int8_matmul_group_prepare", "int8_matmul_group_products",
+    "group_workspace_views", "int8_matmul_group_small_batch", "int8_matmul_group_prepare", "int8_matmul_group_products",
 ]

@@ -24,6 +24,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libllmint8.so")
+# the benchmark's measurement probes (MFMA rate and clock, stream read), a library of their own
+PROBE_LIB = os.path.join(HERE, "libllmint8_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 SOURCES = ["api.hip", "xpass.hip", "weight.hip", "gemm.hip", "gemm_small.hip", "codec.hip", "gemm_group.hip",
            "gemm_group_small.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -48,7 +51,7 @@ def _jobs() -> int:
     return max(1, min(n, int(os.environ.get("MAX_JOBS") or 16), len(SOURCES)))
 
 
-def build(verbose: bool = False, extra=(), out: str = LIB, sanitize: bool = False) -> str:
+def build(verbose: bool = False, extra=(), out: str = LIB, sanitize: bool = False, sources=SOURCES) -> str:
     flags = FLAGS + (SANITIZE if sanitize else []) + list(extra)
     inc = ["-I", os.path.join(ROOT, "include")]
     with tempfile.TemporaryDirectory(prefix="llmint8_build_") as tmpd:
@@ -61,7 +64,7 @@ def build(verbose: bool = False, extra=(), out: str = LIB, sanitize: bool = Fals
             return obj
 
         with ThreadPoolExecutor(_jobs()) as ex:
-            objs = list(ex.map(compile_one, SOURCES))
+            objs = list(ex.map(compile_one, sources))
         tmp = out + ".tmp%d" % os.getpid()
         cmd = [HIPCC, *flags, "-shared", *objs, "-o", tmp]
         if verbose:
@@ -71,9 +74,14 @@ def build(verbose: bool = False, extra=(), out: str = LIB, sanitize: bool = Fals
     return out
 
 
+def build_probe(verbose: bool = False) -> str:
+    return build(verbose=verbose, out=PROBE_LIB, sources=PROBE_SOURCES)
+
+
 if __name__ == "__main__":
     args = sys.argv[1:]
     if args[:1] == ["--sanitize"]:
         print(build(verbose=True, out=os.path.abspath(args[1]), sanitize=True, extra=args[2:]))
     else:
         print(build(verbose=True, extra=args))
+        print(build_probe(verbose=True))

@@ -595,6 +595,12 @@ int group_common(const void* X, int64_t M, int64_t K, int dtype, int64_t group, 
 
 }  // namespace
 
+LLMINT8_API int int8_matmul_group_small_batch(int64_t M, int64_t K, int64_t N, int64_t group) {
+    int rc = check_group(M, K, N, LLMINT8_F16, group);
+    if (rc) return rc;
+    return K > 0 && N > 0 && group_small_batch(M, K, N, group) ? 1 : 0;
+}
+
 LLMINT8_API int int8_matmul_group(const void* X, int64_t M, int64_t K, int dtype, int64_t group, const int8_t* Wq,
                                   const float* w_scale, int64_t N, void* Y, void* workspace, size_t workspace_bytes,
                                   void* stream) {

@@ -198,6 +198,13 @@ def test_group_entry_points_reject():
     assert mg(X, 4, 1024, 0, 128, Wq, S, 0, None, None, 0, None) == L.OK        # N = 0
 
 
+def test_group_route_query():
+    q = L.int8_matmul_group_small_batch
+    assert q(16, 8192, 8192, 1024) and q(1, 1024, 264, 128)
+    assert not q(4096, 12288, 36864, 1024) and not q(300, 1024, 264, 128)
+    assert L.lib().int8_matmul_group_small_batch(16, 8192, 8192, 100) == L.EINVAL
+
+
 def test_group_two_stage_entry_points_reject():
     pg, gp = L.lib().int8_matmul_group_prepare, L.lib().int8_matmul_group_products
     need = L.lib().int8_matmul_group_workspace_bytes(4, 1024, 128)
