@@ -1,0 +1,127 @@
+"""Exact symmetries, determinism and memory hygiene of the GPU path (through the C ABI).
+
+- Negation: Y(-X) = -Y(X) bit for bit (zeros of either sign equal).  Every step is odd in
+  X: the outlier set and the row scales see |x|, round-to-nearest-even and the clamp are
+  symmetric, the int32 product is exact, the 16-bit product sums the negated terms in the
+  same order, and the epilogue's roundings are symmetric.
+- K permutation: permuting the features of X together with the rows of W leaves the int32
+  product C and the row scales bit-identical (exact integer sums; maxima are exact).
+- Determinism: two calls leave Y and the whole workspace bit-identical.
+- Canaries: the calls write nothing outside the workspace regions they own -- not in the
+  gaps between regions, not past the listed outlier columns, not past the workspace.
+Each runs on both batch paths (small-batch and tiled) and both 16-bit types."""
+import numpy as np
+import pytest
+import torch
+
+import int8_quantized_matmul_rowwise_amd as lm
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+CASES = [(40, 1040, 264, "fp16"), (16, 8192, 512, "bf16"), (300, 1040, 520, "bf16"), (257, 2064, 264, "fp16")]
+
+
+def _inputs(M, K, N, dt, seed):
+    x, _ = workloads.make_x(M, K, dt, n_outliers=4, outlier_range=(6.5, 40.0), seed=seed, wid=90)
+    w = workloads.make_w(K, N, dt, sigma=0.02, seed=seed, wid=90)
+    return x, w
+
+
+def _bits(t):
+    return t.contiguous().view(torch.int16)
+
+
+@pytest.mark.parametrize("M,K,N,dt", CASES)
+def test_negation_is_exact(M, K, N, dt):
+    print(f"\n[case] negation {M}x{K}x{N} {dt}", flush=True)
+    x, w = _inputs(M, K, N, dt, seed=M + 1)
+    X, W = x.cuda(), w.cuda()
+    Wq, s_w = lm.int8_quantize_weight(W)
+    Y = lm.int8_matmul(X, Wq, s_w, 6.0)
+    Yn = lm.int8_matmul(-X, Wq, s_w, 6.0)
+    torch.cuda.synchronize()
+    y, yn = Y.float(), Yn.float()
+    assert torch.equal(y, -yn), f"{int((y != -yn).sum())} elements of Y(-X) differ from -Y(X)"
+    nz = y != 0
+    assert torch.equal(_bits(Y)[nz], _bits(-Yn)[nz])
+    assert lm.int8_matmul_stats(X, 6.0)[0] >= 4
+
+
+@pytest.mark.parametrize("M,K,N,dt", CASES)
+def test_k_permutation_leaves_c_and_scales_identical(M, K, N, dt):
+    print(f"\n[case] K permutation {M}x{K}x{N} {dt}", flush=True)
+    x, w = _inputs(M, K, N, dt, seed=M + 2)
+    perm = torch.as_tensor(np.random.default_rng(K).permutation(K))
+    X, W = x.cuda(), w.cuda()
+    Xp, Wp = x[:, perm].contiguous().cuda(), w[perm, :].contiguous().cuda()
+    Wq, s_w = lm.int8_quantize_weight(W)
+    Wqp, s_wp = lm.int8_quantize_weight(Wp)
+    C, _, ws = lm.int8_matmul_accumulators(X, Wq, 6.0)
+    Cp, _, wsp = lm.int8_matmul_accumulators(Xp, Wqp, 6.0)
+    torch.cuda.synchronize()
+    assert torch.equal(s_w, s_wp) and torch.equal(Wqp, Wq[:, perm.cuda()])
+    assert torch.equal(C, Cp), f"C differs at {int((C != Cp).sum())} elements"
+    v, vp = lm.workspace_views(ws, M, K, N, X.dtype), lm.workspace_views(wsp, M, K, N, X.dtype)
+    assert torch.equal(v["s_x"].view(torch.int32), vp["s_x"].view(torch.int32))
+    assert v["n_outliers"] == vp["n_outliers"] >= 4
+    assert torch.equal(vp["Xq"], v["Xq"][:, perm.cuda()])
+
+
+@pytest.mark.parametrize("M,K,N,dt", CASES)
+def test_two_calls_are_bitwise_equal_everywhere(M, K, N, dt):
+    print(f"\n[case] determinism {M}x{K}x{N} {dt}", flush=True)
+    x, w = _inputs(M, K, N, dt, seed=M + 3)
+    X, W = x.cuda(), w.cuda()
+    Wq, s_w = lm.int8_quantize_weight(W)
+    n = lm.int8_matmul_workspace_bytes(M, K, N)
+    ws1 = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    ws2 = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    Y1 = lm.int8_matmul(X, Wq, s_w, 6.0, workspace=ws1)
+    Y2 = lm.int8_matmul(X, Wq, s_w, 6.0, workspace=ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(Y1), _bits(Y2))
+    assert torch.equal(ws1, ws2), "the workspace differs between two identical calls"
+
+
+CANARY = 0xA5
+
+
+@pytest.mark.parametrize("M,K,N,dt", CASES)
+def test_workspace_canaries(M, K, N, dt):
+    print(f"\n[case] canaries {M}x{K}x{N} {dt}", flush=True)
+    x, w = _inputs(M, K, N, dt, seed=M + 4)
+    X, W = x.cuda(), w.cuda()
+    Wq, s_w = lm.int8_quantize_weight(W)
+    L = lm.int8_matmul_workspace_layout(M, K, N)
+    guard = 4096
+    buf = torch.full((L["total"] + 2 * guard,), CANARY, dtype=torch.uint8, device="cuda")
+    ws = buf[guard: guard + L["total"]]
+    Yb = torch.full((M * N + 2048,), 1234.0, dtype=X.dtype, device="cuda")
+    Y = Yb[1024: 1024 + M * N].view(M, N)
+    lm.int8_matmul(X, Wq, s_w, 6.0, Y=Y, workspace=ws)
+    torch.cuda.synchronize()
+    b = buf.cpu().numpy()
+    assert np.all(b[:guard] == CANARY) and np.all(b[guard + L["total"]:] == CANARY), "write past the workspace"
+    assert torch.all(Yb[:1024] == 1234.0) and torch.all(Yb[1024 + M * N:] == 1234.0), "write past Y"
+    w_ = b[guard: guard + L["total"]]
+    n_o = int(w_[L["n_outliers"]: L["n_outliers"] + 4].view(np.int32)[0])
+    P = -(-n_o // 32) * 32
+    # the bytes each region owns: whole rows of Xq, s_x, n_O, the listed outlier columns,
+    # the first P columns of every row of X[:,O] and (tiled path) of the gathered weights
+    owned = np.zeros(L["total"], bool)
+    owned[L["xq"]: L["xq"] + M * L["xq_pitch"]] = True
+    owned[L["s_x"]: L["s_x"] + 4 * M] = True
+    owned[L["n_outliers"]: L["n_outliers"] + 4] = True
+    owned[L["outliers"]: L["outliers"] + 4 * n_o] = True
+    for r in range(M):
+        o = L["xo"] + 2 * r * L["xo_pitch"]
+        owned[o: o + 2 * P] = True
+    if not L["small_batch"]:
+        for r in range(N):
+            o = L["wo"] + 2 * r * L["xo_pitch"]
+            owned[o: o + 2 * P] = True
+    owned[L["scratch"]:] = True  # the internal scratch (flags, partials) is the last region
+    stray = np.flatnonzero(~owned & (w_ != CANARY))
+    assert stray.size == 0, f"{stray.size} bytes written outside the regions, first at offset {stray[:4].tolist()}"
+    assert n_o >= 4

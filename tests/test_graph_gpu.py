@@ -42,8 +42,10 @@ def test_vectorwise_call_replays_from_a_graph(M, K, N, dt):
         assert torch.equal(Y.view(torch.int16), ref.view(torch.int16)), f"replay {r} differs"
 
 
-def test_groupwise_call_replays_from_a_graph():
-    M, K, N, G = 300, 2048, 264, 512
+@pytest.mark.parametrize("M,K,N,G", [(300, 2048, 264, 512),   # the tiled group kernel
+                                     (24, 2048, 264, 256)])   # the split-N small-batch group kernel
+def test_groupwise_call_replays_from_a_graph(M, K, N, G):
+    assert lm.int8_matmul_group_small_batch(M, K, N, G) == (M <= 64)
     print(f"\n[case] graph int8_matmul_group fp16 {M}x{K}x{N} G={G}", flush=True)
     X, W = _inputs(M, K, N, "fp16", seed=7)
     Wq, s_w = lm.int8_quantize_weight_group(W, G)

@@ -67,6 +67,8 @@ def _case(M, K, N, dt, seed, n_outliers=3):
     (16, 8192, 512, 1024),
     (48, 2048, 264, 128),
     (33, 1536, 8200, 512),
+    # 17 to 32 rows: two row groups of the split-N group kernel
+    (24, 2048, 264, 256),
 ])
 def test_group_parity(dt, M, K, N, G):
     print(f"\n[case] group {dt} {M}x{K}x{N} G={G}", flush=True)

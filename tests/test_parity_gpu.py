@@ -253,8 +253,11 @@ def _full_inputs(name):
 def test_full_size_workload_sampled(name):
     x, w, cols, wl = _full_inputs(name)
     _banner(f"full size {name} {wl.M}x{wl.K}x{wl.N} {wl.dtype}")
+    # one seeded row in every 256-row tile of the product kernel's schedule, plus the first and last
     rng = np.random.default_rng(11)
-    rows = np.unique(np.concatenate([[0, wl.M - 1], rng.integers(0, wl.M, 6)])) if wl.M > 16 else None
+    tiles = np.arange(0, wl.M, 256)
+    rows = (np.unique(np.concatenate([[0, wl.M - 1], tiles + rng.integers(0, np.minimum(256, wl.M - tiles))]))
+            if wl.M > 16 else None)
     st = parity.run_case(x, w, wl.tau, rows=rows)
     assert st["n_outliers"] >= len(cols)
     print(f"[stats] {name}: {st}", flush=True)

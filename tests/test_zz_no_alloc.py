@@ -85,3 +85,29 @@ def test_noalloc_too_large_leaves_y_alone():
     assert e.value.status == lm.EWORKSPACE
     torch.cuda.synchronize()
     assert torch.all(Y == 7.0)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("M,K,N,dt", [(16, 2048, 264, "bf16"), (300, 1040, 520, "fp16")])
+def test_noalloc_call_replays_from_a_graph(M, K, N, dt):
+    """Captured once in a HIP graph (the case it is for) and replayed on new X contents, with
+    eager work between the replays: every replay equals the eager int8_matmul bit for bit."""
+    print(f"\n[case] graph int8_matmul_noalloc {M}x{K}x{N} {dt}", flush=True)
+    x, w = _inputs(M, K, N, dt, seed=M)
+    X, W = x.cuda(), w.cuda()
+    Wq, s_w = lm.int8_quantize_weight(W)
+    Y = torch.empty((M, N), dtype=X.dtype, device="cuda")
+    lm.int8_matmul_noalloc(X, Wq, s_w, 6.0, Y=Y)  # the first call on the device, outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        lm.int8_matmul_noalloc(X, Wq, s_w, 6.0, Y=Y)
+    torch.cuda.synchronize()
+    for r in range(3):
+        X.copy_(_inputs(M, K, N, dt, seed=300 + r)[0].cuda())
+        ref = lm.int8_matmul(X, Wq, s_w, 6.0)
+        torch.cuda.synchronize()
+        Y.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y.view(torch.int16), ref.view(torch.int16)), f"replay {r} differs"
