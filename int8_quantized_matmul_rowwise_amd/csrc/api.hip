@@ -123,7 +123,8 @@ int hip_status(hipError_t e) {
     return LLMINT8_EHIP;
 }
 
-// Enqueue the X pass (detect, compact, code rows [+ gather W_O]) into the workspace.
+// Enqueue the X pass into the workspace: on the small-batch path its own launches; on the
+// tiled path detect, compact and the row coding (+ the W_O gather).
 int run_xpass(const void* X, int64_t M, int64_t K, int dtype, float tau, const int8_t* Wq, int64_t N,
               int8_t* ws, const Layout& L, hipStream_t st) {
     uint32_t* partial = (uint32_t*)(ws + L.partial);

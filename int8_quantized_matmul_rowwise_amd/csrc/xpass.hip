@@ -14,6 +14,10 @@
 namespace llmint8 {
 
 // ---------------------------------------------------------------------------
+// rows of X in flight per thread of the detection (16 x 16 B: with three to six
+// workgroups per compute unit, enough bytes in flight to stream X at HBM rate)
+constexpr int kDetectRows = 16;
+
 // Detect: bit j of word w of partial[rb] is set iff some row of row-block rb has
 // |X[i, 32w + j]| > tau.  One thread owns 8 consecutive columns (one 16-byte load per
 // row); the four waves of a block split the rows.  No atomics and no pre-zeroed
@@ -31,12 +35,12 @@ __global__ __launch_bounds__(256) void detect_kernel(const uint16_t* __restrict_
     if (chunk < nchunks) {
         const uint16_t* col = X + chunk * 8;
         int64_t r = r0 + w;
-        for (; r + 28 < r1; r += 32) {  // eight rows in flight per thread
-            u32x4 v[8];
+        for (; r + 4 * (kDetectRows - 1) < r1; r += 4 * kDetectRows) {  // kDetectRows rows in flight per thread
+            u32x4 v[kDetectRows];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = *(const u32x4*)(col + (r + 4 * u) * K);
+            for (int u = 0; u < kDetectRows; ++u) v[u] = *(const u32x4*)(col + (r + 4 * u) * K);
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+            for (int u = 0; u < kDetectRows; ++u)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     uint16_t h = (uint16_t)(v[u][j >> 1] >> (16 * (j & 1)));
@@ -221,16 +225,18 @@ __device__ __forceinline__ u16x2 absmax_bits(u16x2 acc, const u32x4& x, uint32_t
 // Codes of a chunk, byte j of dword d for element 4d + j: clamp(rne(RN32(x * inv)), -127,
 // 127), 0 in outlier columns.  Rounding to an integer by adding 1.5 * 2^23: the sum lies
 // in [2^23, 2^24), where the float spacing is 1, so the add rounds to nearest even and the
-// integer sits in the low mantissa bits (its low byte is the two's-complement code).
+// integer sits in the low mantissa bits (its low byte is the two's-complement code).  The
+// clamp is never taken here: inv = RN32(127/s) with s the largest |x| of the row's
+// non-outlier columns, so for them |RN32(x * inv)| <= RN32(s * inv) < 127.5 and the code is
+// within +-127 as it is; the outlier columns' bytes (any value, even past the add's range)
+// are masked to 0 below.
 template <int DT>
 __device__ __forceinline__ u32x2 code_chunk(const u32x4& x, uint32_t o, float inv, bool any) {
     uint32_t t[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const float f = to_f32<DT>((uint16_t)(x[j >> 1] >> (16 * (j & 1))));
-        float v = __fmul_rn(f, inv);
-        v = fminf(fmaxf(v, -127.0f), 127.0f);
-        t[j] = __builtin_bit_cast(uint32_t, __fadd_rn(v, 12582912.0f));
+        t[j] = __builtin_bit_cast(uint32_t, __fadd_rn(__fmul_rn(f, inv), 12582912.0f));
     }
     u32x2 q;
     q[0] = __builtin_amdgcn_perm(t[1], t[0], 0x0c0c0400u) | __builtin_amdgcn_perm(t[3], t[2], 0x04000c0cu);

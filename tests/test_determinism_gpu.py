@@ -19,7 +19,9 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-CASES = [(40, 1040, 264, "fp16"), (16, 8192, 512, "bf16"), (300, 1040, 520, "bf16"), (257, 2064, 264, "fp16")]
+# small-batch path and tiled path (K from 1040 to 8192)
+CASES = [(40, 1040, 264, "fp16"), (16, 8192, 512, "bf16"), (300, 1040, 520, "bf16"), (257, 2064, 264, "fp16"),
+         (300, 4096, 264, "fp16"), (520, 8192, 136, "bf16")]
 
 
 def _inputs(M, K, N, dt, seed):

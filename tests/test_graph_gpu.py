@@ -18,7 +18,8 @@ def _inputs(M, K, N, dt, seed):
     return x.cuda(), w.cuda()
 
 
-@pytest.mark.parametrize("M,K,N,dt", [(300, 1040, 520, "fp16"), (16, 2048, 264, "bf16")])
+@pytest.mark.parametrize("M,K,N,dt", [(300, 1040, 520, "fp16"), (16, 2048, 264, "bf16"),
+                                      (300, 4096, 264, "fp16")])
 def test_vectorwise_call_replays_from_a_graph(M, K, N, dt):
     print(f"\n[case] graph int8_matmul {dt} {M}x{K}x{N}", flush=True)
     X, W = _inputs(M, K, N, dt, seed=M)
