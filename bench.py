@@ -8,9 +8,14 @@ HIP event between them.  The weight conversion is offline and not timed.  Defaul
 workload: the 175B-like QKV projection, X 4096 x 12288 fp16 (7 outlier feature
 dimensions), W 12288 x 36864.
 
-Caches: the headline is cold.  Before every step (warmup and timed) 512 MiB are written,
-which evicts L2 and the 256 MB memory-side cache; each step is timed by its own events,
-so the flush is outside the step's time.  Warm steps (back to back) are reported beside.
+Caches: the headline is cold.  Before every step (warmup and timed) 512 MiB are written
+and then 512 MiB of a second buffer are read: no byte of the step's operands is left in L2
+or the 256 MB memory-side cache, and no dirty line of the flush is left there either (a
+write-only flush leaves up to 256 MB of dirty lines, whose write-back would share HBM with
+the step's reads: a plain read of the 453 MB QKV weight takes about 140 us after a
+write-only flush and about 85 us after this one, as long as warm).  Each step is timed by
+its own events, so the flush is outside the step's time.  Warm steps (back to back) are
+reported beside.
 
 Printed: one JSON line with
   value            effective TOPS of the cold step, 2*M*N*K / step time
@@ -29,7 +34,9 @@ Printed: one JSON line with
                    product kernel and the X pass each back to back
   ceilings         measured on this machine in this run: the int8 MFMA rate and shader clock
                    of a register-only MFMA loop (zero operands, and random operands that
-                   change from one MFMA to the next), and the HBM stream-read rate
+                   change from one MFMA to the next), the HBM stream-read rate (2 GiB,
+                   back to back), and a plain read of as many bytes as the weight after
+                   the same flush as the cold steps
   cpu_baseline     the CPU oracle on a bounded sample of the same workload, with the host's
                    core count and CPU model
   fp16_gemm        torch.matmul (hipBLASLt) of X and W in the 16-bit type, same shape
@@ -191,8 +198,17 @@ def timed_steps(stages, steps: int, warmup: int, torch, stream, flush=None):
 
 
 def make_flush(dev, torch):
-    buf = torch.empty(FLUSH_MIB * 1024 * 1024 // 4, dtype=torch.int32, device=dev)
-    return buf, (lambda: buf.add_(1))
+    """The cold-step flush: FLUSH_MIB MiB written (an in-place add), then FLUSH_MIB MiB of a
+    second buffer read (a sum), which leaves clean lines of that buffer in the caches."""
+    n = FLUSH_MIB * 1024 * 1024 // 4
+    wr = torch.empty(n, dtype=torch.int32, device=dev)
+    rd = torch.zeros(n, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def flush():
+        wr.add_(1)
+        torch.sum(rd, dim=0, out=sink)
+    return (wr, rd, sink), flush
 
 
 # ---------------------------------------------------------------------------------------
@@ -223,9 +239,10 @@ def oracle_threads() -> int:
     return min(int(env), n) if env else n
 
 
-def measured_ceilings(dev, torch) -> dict:
+def measured_ceilings(dev, torch, cold_bytes: int = 0) -> dict:
     """The int8 MFMA rate and shader clock of a register-only MFMA loop (zero and changing
-    random operands) and the HBM stream-read rate, measured now on this device."""
+    random operands) and the HBM stream-read rate, measured now on this device; with
+    cold_bytes, also a plain read of that many bytes after the cold-step flush."""
     import ctypes
 
     import numpy as np
@@ -268,7 +285,20 @@ def measured_ceilings(dev, torch) -> dict:
     ms = time_loop(fn, 10, torch)
     res["stream_read_gbs"] = nbytes / (ms * 1e-3) / 1e9
     log(f"stream read: {res['stream_read_gbs']:.0f} GB/s")
-    del buf, part
+    del buf
+    if cold_bytes > 0:
+        nb = (cold_bytes + 15) // 16 * 16
+        buf = torch.ones(nb // 4, dtype=torch.int32, device=dev)
+        fbuf, flush = make_flush(dev, torch)
+        st = torch.cuda.current_stream(dev)
+        fn = lambda: P.llmint8_probe_stream_read(buf.data_ptr(), nb, grid, part.data_ptr(), sp)
+        _, (ms_c,), _ = timed_steps([fn], 7, 2, torch, st, flush)
+        res["cold_read_bytes"] = nb
+        res["cold_read_us"] = ms_c * 1e3
+        res["cold_read_gbs"] = nb / (ms_c * 1e-3) / 1e9
+        log(f"plain read of {nb / 1e6:.1f} MB after the flush: {ms_c * 1e3:.1f} us = {res['cold_read_gbs']:.0f} GB/s")
+        del buf, fbuf
+    del part
     torch.cuda.empty_cache()
     return res
 
@@ -636,7 +666,7 @@ def group_bench(args, wl) -> int:
     kernel = product_kernel(wl.M, wl.K, wl.N, G)
     tag = workload_tag(wl, G)
     log(f"workload {tag}: X {wl.M}x{wl.K} {wl.dtype}, W {wl.K}x{wl.N}, groups of {G}; product kernel {kernel}")
-    x, w, _, _ = workloads.make_workload(wl.name)
+    x, w, _, _ = workloads.make_workload(args.workload, rows=args.rows)
     X, W = x.to(dev), w.to(dev)
     Wq, s_w = lm.int8_quantize_weight_group(W, G)
     del W
@@ -671,7 +701,7 @@ def group_bench(args, wl) -> int:
         "dtype": "i8",
         "data": "synthetic",
         "config": {"workload": tag, "M": wl.M, "K": wl.K, "N": wl.N, "x_dtype": wl.dtype, "group": G, "seed": 0,
-                   "caches": f"cold ({FLUSH_MIB} MiB written before each step)"},
+                   "caches": f"cold ({FLUSH_MIB} MiB written, then {FLUSH_MIB} MiB of another buffer read, before each step)"},
         "pct_of_i8_peak": tops / I8_PEAK_TOPS * 100.0,
         "roofline": roof,
         "cpu_baseline": None,
@@ -728,7 +758,7 @@ def vector_bench(args, wl) -> int:
     kernel = product_kernel(wl.M, wl.K, wl.N)
     log(f"workload {wl.name}: X {wl.M}x{wl.K} {wl.dtype}, W {wl.K}x{wl.N}, tau {wl.tau}; product kernel {kernel}")
     import workloads
-    x, w, cols, _ = workloads.make_workload(wl.name)
+    x, w, cols, _ = workloads.make_workload(args.workload, rows=args.rows)
     X = x.to(dev)
     W = w.to(dev)
     Wq, s_w = lm.int8_quantize_weight(W)
@@ -752,7 +782,8 @@ def vector_bench(args, wl) -> int:
                   lambda: lm.int8_matmul_products(wl.M, wl.K, X.dtype, Wq, s_w, ws, Y=Y, stream=stream)]
 
     flush_buf, flush = make_flush(dev, torch)
-    log(f"cold steps ({FLUSH_MIB} MiB written before each): warmup {args.warmup}, timing {args.steps}")
+    log(f"cold steps ({FLUSH_MIB} MiB written, {FLUSH_MIB} MiB read before each): warmup {args.warmup}, "
+        f"timing {args.steps}")
     ms_step, parts, t_wall = timed_steps(stages, args.steps, args.warmup, torch, stream, flush)
     del flush_buf
     torch.cuda.empty_cache()
@@ -801,7 +832,10 @@ def vector_bench(args, wl) -> int:
         log(f"fp16 GEMM {ms16 * 1e3:.1f} us = {fp16['tflops']:.0f} TFLOP/s")
     del W
     torch.cuda.empty_cache()
-    ceilings = None if args.no_ceilings else measured_ceilings(dev, torch)
+    ceilings = None if args.no_ceilings else measured_ceilings(dev, torch, cold_bytes=wl.N * wl.K)
+    if ceilings and roof["bound"] == "hbm" and ceilings.get("cold_read_gbs"):
+        # the product kernel's byte rate against a plain read of the weight in the same state
+        roof["frac_of_cold_read"] = roof["achieved"] / ceilings["cold_read_gbs"]
 
     line = {
         "metric": "effective TOPS of int8 outlier-decomposed matmul; % i8 MFMA peak",
@@ -818,7 +852,7 @@ def vector_bench(args, wl) -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "x_dtype": wl.dtype,
                    "threshold": None if args.fixed else wl.tau, "n_outliers": n_out, "seed": 0,
-                   "caches": f"cold ({FLUSH_MIB} MiB written before each step)",
+                   "caches": f"cold ({FLUSH_MIB} MiB written, then {FLUSH_MIB} MiB of another buffer read, before each step)",
                    **({"outliers": "fixed (caller-supplied)"} if args.fixed else {})},
         "pct_of_i8_peak": tops / I8_PEAK_TOPS * 100.0,
         "roofline": roof,
@@ -840,6 +874,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qkv_175b")
+    ap.add_argument("--rows", type=int, default=None, metavar="M",
+                    help="another number of rows of X on the workload's weight (a mid-size or small batch)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="CPU work budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp16-gemm", action="store_true")
@@ -865,7 +901,7 @@ def main() -> int:
 
     import workloads
 
-    wl = workloads.WORKLOADS[args.workload]
+    wl = workloads.with_rows(workloads.WORKLOADS[args.workload], args.rows)
     if args.trace_summary:
         return trace_summary(args.trace_summary[0], args.trace_summary[1], wl, args.trace_summary[2], args.group)
     if args.traffic_summary:

@@ -137,7 +137,11 @@ int int8_matmul_stats(const void* X, int64_t M, int64_t K, int dtype, float thre
  *   int8_matmul_products: C = Xq Wq^T (int8, int32 accumulation), F = X[:,O] Wq[:,O]^T
  *                         (16-bit, fp32 accumulation) and the dequantizing epilogue,
  *                         from a workspace prepared for the same X, Wq, M, K, N, dtype
- *                         and threshold on the same stream.
+ *                         and threshold on the same stream.  It may be called again on
+ *                         the same prepared workspace; the calls then follow each other on
+ *                         one stream (with few output tiles the products split their K
+ *                         stages over the GPU and exchange exact int32 partial sums through
+ *                         the workspace's scratch, so concurrent calls on one workspace race).
  * int8_matmul(X, ...) == int8_matmul_prepare(X, ...) then int8_matmul_products(...).
  * Same conventions and status codes as int8_matmul.
  */
@@ -145,7 +149,7 @@ int int8_matmul_prepare(const void* X, int64_t M, int64_t K, int dtype, const in
                         float threshold, void* workspace, size_t workspace_bytes, void* stream);
 
 int int8_matmul_products(int64_t M, int64_t K, int dtype, const int8_t* Wq, const float* w_scale, int64_t N,
-                         void* Y, const void* workspace, size_t workspace_bytes, void* stream);
+                         void* Y, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Where int8_matmul leaves the X pass's products in its workspace (byte offsets from
  * the workspace start; pitches in elements).  All regions are 256-byte aligned.
@@ -298,7 +302,8 @@ int int8_matmul_group_products(int64_t M, int64_t K, int dtype, int64_t group, c
  *          Small batches (M <= 128 on the small-batch path: e.g. 16 x 8192 x 8192 needs
  *          under 1 MiB) fit; so do tiled calls of moderate size (the tiled path reserves
  *          the worst case of every column an outlier, 2 N K bytes for the gathered weight
- *          columns alone).
+ *          columns alone, and with few output tiles 512 KB of int32 partial sums per
+ *          workgroup of its K split).
  *   Concurrency: every call on one GPU works in that GPU's single array.  Calls that
  *          overlap in time on one GPU (on different streams or host threads) race and
  *          give undefined results; calls ordered on one stream are safe.  The array keeps

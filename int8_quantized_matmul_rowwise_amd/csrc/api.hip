@@ -45,7 +45,8 @@ int check_shape(int64_t M, int64_t K, int64_t N, int dtype) {
 int check_threshold(float t) { return (isnan(t) || t < 0.0f) ? LLMINT8_EINVAL : LLMINT8_OK; }
 
 struct Layout {
-    size_t xq, xq_pitch, s_x, n_outliers, outliers, xo, xo_pitch, wo, bitmap, partial, pmax, total;
+    size_t xq, xq_pitch, s_x, n_outliers, outliers, xo, xo_pitch, wo, bitmap, partial, pmax, sk_cnt, sk_part, total;
+    bool sk;  // the tiled product kernel runs stream-K for these sizes
 };
 
 Layout make_layout(int64_t M, int64_t K, int64_t N) {
@@ -74,6 +75,12 @@ Layout make_layout(int64_t M, int64_t K, int64_t N) {
     off = align_up(off + 4 * kw * (size_t)detect_row_blocks(M));
     L.pmax = off;  // small batches: per row and 512-column slab, the slab's row maximum
     off = align_up(off + (small_batch(M, K, N) ? 4 * m * (size_t)ceil_div(K, 512) : 0));
+    // stream-K (tiled path, few tiles): a counter per tile, two partial tiles per workgroup
+    L.sk = stream_k_shape(M, K, N);
+    L.sk_cnt = off;
+    off = align_up(off + (L.sk ? 4 * (size_t)gemm_tiles(M, N) : 0));
+    L.sk_part = off;
+    off = align_up(off + (L.sk ? 2 * (size_t)stream_k_grid(M, K, N) * (size_t)kStreamKSlotBytes : 0));
     L.total = off;
     return L;
 }
@@ -145,8 +152,11 @@ int run_xpass(const void* X, int64_t M, int64_t K, int dtype, float tau, const i
     a.xo_pitch = (int64_t)L.xo_pitch;
     if (small_batch(M, K, N))
         return hip_status(stage("xpass_small", [&] { return launch_xpass_small(a, O, nO, bitmap, (uint32_t*)(ws + L.pmax), st); }));
+    int32_t* sk_cnt = L.sk ? (int32_t*)(ws + L.sk_cnt) : nullptr;  // zeroed for the product kernel
+    const int64_t n_tiles = gemm_tiles(M, N);
     hipError_t e = stage("detect", [&] { return launch_detect(dtype, X, M, K, tau, partial, st); });
-    if (e == hipSuccess) e = stage("compact", [&] { return launch_compact(M, K, partial, bitmap, O, nO, st); });
+    if (e == hipSuccess)
+        e = stage("compact", [&] { return launch_compact(M, K, partial, bitmap, O, nO, st, sk_cnt, n_tiles); });
     if (e == hipSuccess) {
         a.M = M;
         a.K = K;
@@ -188,7 +198,7 @@ int prepare_common(const void* X, int64_t M, int64_t K, int dtype, const int8_t*
 
 // Products + epilogue (Y != NULL) or the accumulator dump (C, F) from a prepared workspace.
 int products_common(int64_t M, int64_t K, int dtype, const int8_t* Wq, const float* w_scale, int64_t N, void* Y,
-                    int32_t* C, float* F, const void* workspace, size_t workspace_bytes, void* stream,
+                    int32_t* C, float* F, void* workspace, size_t workspace_bytes, void* stream,
                     bool enqueue, const void* WO_fixed = nullptr, int64_t wo_pitch_fixed = 0) {
     int rc = check_shape(M, K, N, dtype);
     if (rc) return rc;
@@ -211,8 +221,8 @@ int products_common(int64_t M, int64_t K, int dtype, const int8_t* Wq, const flo
     }
     if (M == 0 || N == 0 || !enqueue) return LLMINT8_OK;
     log_call(acc ? "products (accumulator dump)" : (WO_fixed ? "products (fixed outlier set)" : "products"), M, K, N,
-             dtype, NAN, small_batch(M, K, N) ? "small_batch" : "tiled");
-    const int8_t* ws = (const int8_t*)workspace;
+             dtype, NAN, small_batch(M, K, N) ? "small_batch" : (L.sk ? "tiled_stream_k" : "tiled"));
+    int8_t* ws = (int8_t*)workspace;
     GemmArgs g;
     g.dt = dtype;
     g.Xq = ws + L.xq;
@@ -233,20 +243,25 @@ int products_common(int64_t M, int64_t K, int dtype, const int8_t* Wq, const flo
     g.Y = Y;
     g.C_acc = C;
     g.F_acc = F;
+    g.sk_cnt = L.sk ? (int32_t*)(ws + L.sk_cnt) : nullptr;
+    g.sk_part = L.sk ? (int32_t*)(ws + L.sk_part) : nullptr;
     if (small_batch(M, K, N)) return hip_status(stage("gemm_small", [&] { return launch_gemm_small(g, (hipStream_t)stream); }));
     return hip_status(stage("gemm", [&] { return launch_gemm(g, (hipStream_t)stream); }));
 }
 
 // X pass against a caller's fixed outlier set: its bitmap (as one partial), the
 // compaction (O, n_O in the workspace), then the row coding; no W_O gather.
-int run_xpass_fixed(const void* X, int64_t M, int64_t K, int dtype, const int32_t* Ofix, int64_t nO, int8_t* ws,
-                    const Layout& L, hipStream_t st) {
+int run_xpass_fixed(const void* X, int64_t M, int64_t K, int64_t N, int dtype, const int32_t* Ofix, int64_t nO,
+                    int8_t* ws, const Layout& L, hipStream_t st) {
     uint32_t* partial = (uint32_t*)(ws + L.partial);
     uint32_t* bitmap = (uint32_t*)(ws + L.bitmap);
     int32_t* O = (int32_t*)(ws + L.outliers);
     int32_t* n_out = (int32_t*)(ws + L.n_outliers);
+    int32_t* sk_cnt = L.sk ? (int32_t*)(ws + L.sk_cnt) : nullptr;  // zeroed for the product kernel
+    const int64_t n_tiles = gemm_tiles(M, N);
     hipError_t e = stage("list_bitmap", [&] { return launch_list_bitmap(K, Ofix, nO, partial, st); });
-    if (e == hipSuccess) e = stage("compact", [&] { return launch_compact(1, K, partial, bitmap, O, n_out, st); });
+    if (e == hipSuccess)
+        e = stage("compact", [&] { return launch_compact(1, K, partial, bitmap, O, n_out, st, sk_cnt, n_tiles); });
     if (e == hipSuccess) {
         XPassArgs a;
         a.dt = dtype;
@@ -397,7 +412,7 @@ LLMINT8_API int int8_matmul_prepare(const void* X, int64_t M, int64_t K, int dty
 }
 
 LLMINT8_API int int8_matmul_products(int64_t M, int64_t K, int dtype, const int8_t* Wq, const float* w_scale,
-                                     int64_t N, void* Y, const void* workspace, size_t workspace_bytes,
+                                     int64_t N, void* Y, void* workspace, size_t workspace_bytes,
                                      void* stream) {
     if (!Y && M > 0 && N > 0) return LLMINT8_EINVAL;
     return products_common(M, K, dtype, Wq, w_scale, N, Y, nullptr, nullptr, workspace, workspace_bytes, stream,
@@ -495,7 +510,7 @@ LLMINT8_API int int8_matmul_fixed(const void* X, int64_t M, int64_t K, int dtype
         return LLMINT8_EINVAL;
     if (M == 0) return LLMINT8_OK;
     log_call("fixed x pass", M, K, N, dtype, NAN, "fixed");
-    rc = run_xpass_fixed(X, M, K, dtype, outlier_cols, nO, (int8_t*)workspace, L, (hipStream_t)stream);
+    rc = run_xpass_fixed(X, M, K, N, dtype, outlier_cols, nO, (int8_t*)workspace, L, (hipStream_t)stream);
     if (rc) return rc;
     return products_common(M, K, dtype, Wq, w_scale, N, Y, nullptr, nullptr, workspace, workspace_bytes, stream, true,
                            W_O, P);

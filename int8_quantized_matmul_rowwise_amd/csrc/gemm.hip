@@ -122,6 +122,8 @@ struct Params {
     int32_t* C_acc;
     float* F_acc;
     int tiles_m, tiles_n;
+    int32_t* sk_cnt;   // stream-K: per tile, the contributors done so far (0 between calls)
+    int32_t* sk_part;  // stream-K: two 256 x 256 int32 partial tiles per workgroup
 };
 
 template <int DT>
@@ -132,30 +134,81 @@ __device__ __forceinline__ v16f mfma16(const u32x4& a, const u32x4& b, const v16
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
-template <int DT, bool ACC_OUT>
+// SK (stream-K, for calls with fewer tiles than twice the workgroups, not a multiple of
+// them): the K stages of all tiles, taken in order (tile t's stages are units t nk .. t nk +
+// nk - 1), are split evenly over the workgroups; a workgroup's range covers at most three
+// segments of tiles.  A segment that is a whole tile ends in the epilogue as usual.  A part
+// of a tile ends by storing its exact int32 partial sums to the workgroup's slot and
+// counting itself in on the tile's counter; the tile's last contributor adds the others'
+// partials (integer sums: the order does not matter) and runs the epilogue, so Y is the
+// same bits as without the split.  It leaves the counter at 0 again (the X pass zeroes the
+// counters; every call leaves them so).
+// HALF (M <= 128: every valid row lies in the first half of its tile): the four waves of
+// rows 128..255 issue their share of the loads and meet every barrier, but run no MFMA and
+// read no operands, so each SIMD's matrix unit serves one wave.
+template <int DT, bool ACC_OUT, bool SK, bool HALF>
 __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
     __shared__ __attribute__((aligned(1024))) int8_t smem[kSlotsA * kTileBytes + kSlotsB * kSlotBytesB];
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int wm = w >> 2, wn = w & 3;
+    const int nk = (int)ceil_div(p.K, BK);  // >= 1 (K = 0 never reaches this kernel)
 
     // ---- tiles of this workgroup: the XCD-contiguous run of tiles (grouped order) of the
     // XCD the dispatcher places it on (ids congruent mod 8), strided by the number of
-    // workgroups on that XCD
+    // workgroups on that XCD (SK: the segments of its range of units)
     const int T = p.tiles_m * p.tiles_n;
     const int bid = blockIdx.x, nwg = gridDim.x;
     const int xcd = bid % kXcds, local = bid / kXcds;
     const int per = T / kXcds, rem = T % kXcds;
     const int x_start = xcd * per + (xcd < rem ? xcd : rem), x_cnt = per + (xcd < rem ? 1 : 0);
     const int on_xcd = (nwg - xcd + kXcds - 1) / kXcds;
-    const int my_tiles = local < x_cnt ? (x_cnt - local + on_xcd - 1) / on_xcd : 0;
+    const int64_t sk_units = (int64_t)T * nk;
+    auto sk_begin = [&](int c) -> int64_t { return sk_units * c / nwg; };
+    // segments s = 0, 1, 2: tile t_s, first stage k_s, stages n_s (scalars, not an array: an
+    // array indexed by the segment number would live in scratch memory)
+    int t_0 = 0, t_1 = 0, t_2 = 0, k_0 = 0, k_1 = 0, k_2 = 0, n_0 = nk, n_1 = nk, n_2 = nk;
+    int my_tiles = 0;
+    if constexpr (SK) {
+        int64_t u = sk_begin(bid);
+        const int64_t u1 = sk_begin(bid + 1);
+        // past the range: whole-tile dummies (tile 0, all stages), loaded through empty resources
+        auto next = [&](int& t, int& k, int& n) {
+            if (u < u1) {
+                t = (int)(u / nk);
+                const int64_t e = (int64_t)(t + 1) * nk < u1 ? (int64_t)(t + 1) * nk : u1;
+                k = (int)(u - (int64_t)t * nk);
+                n = (int)(e - u);
+                ++my_tiles;
+                u = e;
+            }
+            t = __builtin_amdgcn_readfirstlane(t);  // uniform: scalar registers
+            k = __builtin_amdgcn_readfirstlane(k);
+            n = __builtin_amdgcn_readfirstlane(n);
+        };
+        next(t_0, k_0, n_0);
+        next(t_1, k_1, n_1);
+        next(t_2, k_2, n_2);
+        my_tiles = __builtin_amdgcn_readfirstlane(my_tiles);
+    } else {
+        my_tiles = local < x_cnt ? (x_cnt - local + on_xcd - 1) / on_xcd : 0;
+    }
     if (my_tiles == 0) return;  // the same for every wave of the workgroup
+    auto seg_tile = [&](int i) { return i <= 0 ? t_0 : (i == 1 ? t_1 : t_2); };
+    auto seg_k = [&](int i) { return i <= 0 ? k_0 : (i == 1 ? k_1 : k_2); };
+    auto seg_n = [&](int i) { return i <= 0 ? n_0 : (i == 1 ? n_1 : n_2); };
     auto tile_origin = [&](int i, int64_t& m0, int64_t& n0) {
-        const int t = x_start + local + i * on_xcd;
-        const int in_group = kGroupM * p.tiles_n;
-        const int first_m = (t / in_group) * kGroupM;
-        const int gm = p.tiles_m - first_m < kGroupM ? p.tiles_m - first_m : kGroupM;
-        m0 = (int64_t)(first_m + (t % in_group) % gm) * BM;
-        n0 = (int64_t)((t % in_group) / gm) * BN;
+        if constexpr (SK) {
+            const int t = seg_tile(i);
+            m0 = (int64_t)(t % p.tiles_m) * BM;
+            n0 = (int64_t)(t / p.tiles_m) * BN;
+        } else {
+            const int t = x_start + local + i * on_xcd;
+            const int in_group = kGroupM * p.tiles_n;
+            const int first_m = (t / in_group) * kGroupM;
+            const int gm = p.tiles_m - first_m < kGroupM ? p.tiles_m - first_m : kGroupM;
+            m0 = (int64_t)(first_m + (t % in_group) % gm) * BM;
+            n0 = (int64_t)((t % in_group) / gm) * BN;
+        }
     };
 
     // ---- per-lane offsets of the stage loop: loader (wave w fills LDS slots
@@ -184,7 +237,6 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
         for (int u = 0; u < kSubSteps; ++u) rd[u] = rl * BK + (((2 * u + h) ^ swz(rl)) << 4);
     };
     lane_offsets(lane);
-    const int nk = (int)ceil_div(p.K, BK);  // >= 1 (K = 0 never reaches this kernel)
 
     // ---- operand resources.  A tile's resources span its rows (at most 256 of them:
     // offsets fit 32 bits for any K the library accepts); rows past M or N lie past the
@@ -293,13 +345,31 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
     // -- except in a tile's last stage (LAST), where the epilogue comes first.  Each
     // sub-step is fenced (sched_barrier) so that the interleave stays inside it.
     v4i fa[2][4], fb[2][NJ];  // operand sets of the current / next sub-step
+    // where the loads of stage kt of segment ti go: stage ka of tile d_a ahead (A), stage
+    // kb of tile d_b ahead (B)
+    auto stage_loads = [&](int kt, int ti, int& ka, int& da, int& kb, int& db) {
+        // (readfirstlane: the compiler then knows these, and so the resources, are uniform)
+        if constexpr (SK) {
+            // kt counts this segment's stages; the loads take absolute stages (the segment's
+            // first stage + its count), running on into the next segments
+            const int l0 = seg_n(ti), l1 = seg_n(ti + 1);
+            da = __builtin_amdgcn_readfirstlane(kt + 1 < l0 ? 0 : 1);
+            ka = __builtin_amdgcn_readfirstlane(da == 0 ? seg_k(ti) + kt + 1 : seg_k(ti + 1) + kt + 1 - l0);
+            db = __builtin_amdgcn_readfirstlane(kt + 2 < l0 ? 0 : (kt + 2 - l0 < l1 ? 1 : 2));
+            kb = __builtin_amdgcn_readfirstlane(
+                db == 0 ? seg_k(ti) + kt + 2
+                        : (db == 1 ? seg_k(ti + 1) + kt + 2 - l0 : seg_k(ti + 2) + kt + 2 - l0 - l1));
+        } else {
+            ka = kt + 1 < nk ? kt + 1 : kt + 1 - nk;
+            da = __builtin_amdgcn_readfirstlane(kt + 1 < nk ? 0 : 1);
+            db = __builtin_amdgcn_readfirstlane(kt + 2 < nk ? 0 : (kt + 2 < 2 * nk ? 1 : 2));
+            kb = kt + 2 - db * nk;
+        }
+    };
     auto stage = [&](int sa, int sb, int kt, int ti, auto last_tag) {
         constexpr bool LAST = decltype(last_tag)::value;
-        // (readfirstlane: the compiler then knows these, and so the resources, are uniform)
-        const int ka = kt + 1 < nk ? kt + 1 : kt + 1 - nk;
-        const int da = __builtin_amdgcn_readfirstlane(kt + 1 < nk ? 0 : 1);
-        const int db = __builtin_amdgcn_readfirstlane(kt + 2 < nk ? 0 : (kt + 2 < 2 * nk ? 1 : 2));
-        const int kb = kt + 2 - db * nk;
+        int ka, da, kb, db;
+        stage_loads(kt, ti, ka, da, kb, db);
         if constexpr (LAST && !ACC_OUT) {
             epilogue_reads(ti, false);
             __builtin_amdgcn_sched_barrier(0);
@@ -345,6 +415,17 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
         __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
         __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // HALF, rows 128..255: the stage's loads and its barrier, no operand reads or products
+    auto idle_stage = [&](int sa, int sb, int kt, int ti, auto last_tag) {
+        constexpr bool LAST = decltype(last_tag)::value;
+        int ka, da, kb, db;
+        stage_loads(kt, ti, ka, da, kb, db);
+        if constexpr (LAST && !ACC_OUT) epilogue_reads(ti, false);  // the column factors
+        issue_a(sa ^ 1, ka, da);
+        issue_b(sb == 0 ? 2 : sb - 1, kb, db);
+        LLMINT8_WAIT_BARRIER(4);
     };
 
     // ---- epilogue of tile ti: 16-bit outlier product, dequantization, Y.  The LDS slots of
@@ -454,11 +535,151 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
         }
     };
 
+    // ---- stream-K: the end of a segment that is part of a tile (see the kernel's comment).
+    // The partial sums go to slot 2 bid + (first segment of the range ? 0 : 1), 16-byte
+    // piece (accumulator quarter) * 512 + tid; the partial parts of a tile are the first or
+    // the last segment of their workgroups' ranges.  Slots and counters are written and read
+    // with the agent-scope coherence bit, coherent across the XCDs without writing back or
+    // invalidating any L2 (that would cost the other workgroups their operands).
+    // (the grid has at most one workgroup per unit: every range holds at least one unit)
+    auto sk_owner = [&](int64_t x) {  // the workgroup whose range holds unit x
+        int c = (int)(x * nwg / sk_units);
+        while (c > 0 && sk_begin(c) > x) --c;
+        while (c + 1 < nwg && sk_begin(c + 1) <= x) ++c;
+        return c;
+    };
+    auto sk_slot = [&](int c, int t) {
+        return p.sk_part + (int64_t)(2 * c + (sk_begin(c) / nk == t ? 0 : 1)) * (BM * BN);
+    };
+    // (the verdict travels through the last word of the B slot the segment's last stage
+    // freed: the epilogue's staging stops short of it and no load in flight goes there)
+    static_assert(4 * kYQuarterBytes + 4 <= kSlotBytesB, "stream-K flag");
+    auto sk_finish = [&](int ti, int sb) -> bool {  // true: this workgroup runs the tile's epilogue
+        int* sk_flag = (int*)(slot_b(sb) + kSlotBytesB - 4);
+        const int t = seg_tile(ti);
+        if (seg_k(ti) == 0 && seg_n(ti) == nk) return true;
+        // the 32 x 32 blocks of the wave that hold outputs (a mid-size batch fills a
+        // quarter of the rows), 16 bytes per lane, through a buffer resource over the slot
+        // with the agent-scope coherence bit (sc1, cache policy 16): coherent across XCDs
+        int64_t m0, n0;
+        tile_origin(ti, m0, n0);
+        const int64_t vr = p.M - m0, vc = p.N - n0;  // valid rows / columns of the tile
+        auto block_live = [&](int i, int j) {
+            return (int64_t)(wm * 128 + 32 * i) < vr && (int64_t)(wn * (32 * NJ) + 32 * j) < vc;
+        };
+        constexpr int kCoherent = 16;
+        auto slot_rsrc = [&](int c) { return buffer_rsrc(sk_slot(c, t), (int64_t)BM * BN * 4); };
+        // lane part in the one VGPR offset, piece part in the scalar offset (a VGPR per
+        // piece would be hoisted over the main loop)
+        const uint32_t lane_off = (uint32_t)tid * 16;
+        auto piece = [&](int i, int j, int q) { return (uint32_t)(((i * NJ + j) * 4 + q) * (64 * kWaves) * 16); };
+        {
+            const __amdgpu_buffer_rsrc_t rs = slot_rsrc(bid);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    if (block_live(i, j))
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                __builtin_bit_cast(u32x4, v4i{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                                              acc[i][j][4 * q + 3]}),
+                                rs, lane_off, piece(i, j, q), kCoherent);
+        }
+        // every wave's stores complete before the count
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        if (tid == 0) {
+            const int c0 = sk_owner((int64_t)t * nk), c1 = sk_owner((int64_t)(t + 1) * nk - 1);
+            const int done = __hip_atomic_fetch_add(&p.sk_cnt[t], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+            *sk_flag = done == c1 - c0 + 1 ? 1 : 0;
+            if (*sk_flag) __hip_atomic_store(&p.sk_cnt[t], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        const int last = __builtin_amdgcn_readfirstlane(*sk_flag);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();  // every wave has the verdict before the slot is reused
+        if (!last) return false;
+        // the last contributor: the others' partials (complete before they counted in)
+        const int c0 = sk_owner((int64_t)t * nk), c1 = sk_owner((int64_t)(t + 1) * nk - 1);
+        for (int c = c0; c <= c1; ++c) {
+            if (c == bid) continue;
+            const __amdgpu_buffer_rsrc_t rs = slot_rsrc(c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+                    if (block_live(i, j))
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const v4i v = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, piece(i, j, q), kCoherent));
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[e];
+                        }
+                // one row of blocks in flight at a time: the loads are not hoisted over the
+                // adds of the row before (that would hold 128 loaded vectors)
+                asm volatile("" ::: "memory");
+            }
+        }
+        return true;
+    };
+
     // ---- prologue: global stages 0 and (of the long-lead operand) 1 in flight
-    issue_a(0, 0, 0);
-    issue_b(0, 0, 0);
-    issue_b(1, nk > 1 ? 1 : 0, nk > 1 ? 0 : 1);
+    if constexpr (SK) {
+        issue_a(0, k_0, 0);
+        issue_b(0, k_0, 0);
+        if (n_0 > 1) issue_b(1, k_0 + 1, 0);
+        else issue_b(1, k_1, 1);
+    } else {
+        issue_a(0, 0, 0);
+        issue_b(0, 0, 0);
+        issue_b(1, nk > 1 ? 1 : 0, nk > 1 ? 0 : 1);
+    }
     LLMINT8_WAIT_BARRIER(4);
+    if constexpr (HALF && !ACC_OUT) {
+        // rows 128..255 hold no valid row: the same loads and barriers as the other waves
+        // (the stream-K exchange skips blocks without valid rows, and the epilogue needs only
+        // this wave's entries of the factor tables)
+        if (wu >= 4) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) acc[i][j] = v16i{};
+            int sa = 0, sb = 0;
+            for (int ti = 0; ti < my_tiles; ++ti) {
+                const int len = SK ? __builtin_amdgcn_readfirstlane(seg_n(ti)) : nk;
+                for (int kt = 0; kt + 1 < len; ++kt) {
+                    idle_stage(sa, sb, kt, ti, std::false_type{});
+                    sa ^= 1;
+                    sb = sb == 2 ? 0 : sb + 1;
+                }
+                idle_stage(sa, sb, len - 1, ti, std::true_type{});
+                bool fin = true;
+                if constexpr (SK) fin = sk_finish(ti, sb);
+                if (fin) {
+                    float* rsc = (float*)slot_a(sa);
+                    rsc[tid] = sc / 127.0f;
+                    __builtin_amdgcn_s_waitcnt(0xC07F);
+                    __builtin_amdgcn_s_barrier();
+                }
+                sa ^= 1;
+                sb = sb == 2 ? 0 : sb + 1;
+                if (ti + 1 < my_tiles) {
+                    ra0 = ra1;
+                    rb0 = rb1;
+                    ra1 = ra2;
+                    rb1 = rb2;
+                    tile_rsrc(ti + 3, ra2, rb2);
+                    __builtin_amdgcn_s_waitcnt(0xC07F);
+                    __builtin_amdgcn_s_barrier();
+                }
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            return;
+        }
+    }
     read_frags(0, 0, 0, fa[0], fb[0]);
     int sa = 0, sb = 0;
     for (int ti = 0; ti < my_tiles; ++ti) {
@@ -466,13 +687,18 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < NJ; ++j) acc[i][j] = v16i{};
-        for (int kt = 0; kt + 1 < nk; ++kt) {
+        const int len = SK ? __builtin_amdgcn_readfirstlane(seg_n(ti)) : nk;
+        for (int kt = 0; kt + 1 < len; ++kt) {
             stage(sa, sb, kt, ti, std::false_type{});
             sa ^= 1;
             sb = sb == 2 ? 0 : sb + 1;
         }
-        stage(sa, sb, nk - 1, ti, std::true_type{});
-        epilogue(ti, sa, sb);
+        stage(sa, sb, len - 1, ti, std::true_type{});
+        if constexpr (SK) {
+            if (sk_finish(ti, sb)) epilogue(ti, sa, sb);
+        } else {
+            epilogue(ti, sa, sb);
+        }
         sa ^= 1;
         sb = sb == 2 ? 0 : sb + 1;
         if (ti + 1 < my_tiles) {
@@ -494,16 +720,25 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int DT, bool ACC_OUT>
+template <int DT, bool ACC_OUT, bool HALF>
 hipError_t launch_one(const Params& p, hipStream_t stream) {
-    // persistent: one workgroup per compute unit (its LDS admits one), at most one per tile
+    // persistent: one workgroup per compute unit (its LDS admits one), at most one per tile;
+    // stream-K (one workgroup per compute unit) where the tiles leave the last round uneven
     int dev = 0, cus = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
     const int64_t T = (int64_t)p.tiles_m * p.tiles_n;
+    const int64_t G = cus < kStreamKGrid ? cus : kStreamKGrid;
+    if (p.sk_cnt != nullptr && p.sk_part != nullptr && G > 0 && T < 2 * G && T % G != 0) {
+        // at most one workgroup per unit, so that every workgroup's range holds a stage (the
+        // tile counts count the workgroups whose ranges meet the tile)
+        const int64_t units = T * ceil_div(p.K, BK), g = units < G ? units : G;  // <= stream_k_grid
+        gemm_kernel<DT, ACC_OUT, true, HALF><<<(unsigned)g, 64 * kWaves, 0, stream>>>(p);
+        return hipGetLastError();
+    }
     const int64_t wgs = T < cus ? T : (cus > 0 ? cus : 1);
-    gemm_kernel<DT, ACC_OUT><<<(unsigned)wgs, 64 * kWaves, 0, stream>>>(p);
+    gemm_kernel<DT, ACC_OUT, false, HALF><<<(unsigned)wgs, 64 * kWaves, 0, stream>>>(p);
     return hipGetLastError();
 }
 
@@ -538,9 +773,12 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     p.F_acc = a.F_acc;
     p.tiles_m = (int)ceil_div(a.M, BM);
     p.tiles_n = (int)ceil_div(a.N, BN);
-    const bool acc_out = a.Y == nullptr;
-    if (a.dt == F16) return acc_out ? launch_one<F16, true>(p, stream) : launch_one<F16, false>(p, stream);
-    return acc_out ? launch_one<BF16, true>(p, stream) : launch_one<BF16, false>(p, stream);
+    p.sk_cnt = a.sk_cnt;
+    p.sk_part = a.sk_part;
+    const bool acc_out = a.Y == nullptr, half = a.M <= BM / 2;
+    if (acc_out) return a.dt == F16 ? launch_one<F16, true, false>(p, stream) : launch_one<BF16, true, false>(p, stream);
+    if (a.dt == F16) return half ? launch_one<F16, false, true>(p, stream) : launch_one<F16, false, false>(p, stream);
+    return half ? launch_one<BF16, false, true>(p, stream) : launch_one<BF16, false, false>(p, stream);
 }
 
 }  // namespace llmint8

@@ -27,8 +27,9 @@ hipError_t launch_list_bitmap(int64_t K, const int32_t* O, int64_t nO, uint32_t*
 int64_t detect_row_blocks(int64_t M);
 hipError_t launch_detect(int dt, const void* X, int64_t M, int64_t K, float tau, uint32_t* partial,
                          hipStream_t stream);
+// (also zeroes zero[0, n_zero): the product kernel's stream-K tile counters)
 hipError_t launch_compact(int64_t M, int64_t K, const uint32_t* partial, uint32_t* bitmap, int32_t* O,
-                          int32_t* n_out, hipStream_t stream);
+                          int32_t* n_out, hipStream_t stream, int32_t* zero = nullptr, int64_t n_zero = 0);
 
 // Small-batch path (slab X pass, split-N product kernel), for M <= kSmallM and K <= kSmallK
 // where it beats the tiled path.  The split-N kernel streams Wq once at about 5 TB/s, and
@@ -93,7 +94,25 @@ struct GemmArgs {
     void* Y;          // product path
     int32_t* C_acc;   // accumulator dump (test hook); Y == NULL then
     float* F_acc;
+    int32_t* sk_cnt = nullptr;   // stream-K tile counters (zero between calls) and partial
+    int32_t* sk_part = nullptr;  // slots, when the workspace holds them (stream_k_shape)
 };
+// Stream-K on the tiled path: with fewer tiles than twice the grid (kStreamKGrid at most,
+// one workgroup per compute unit) and not a multiple of it, the tiles' K stages are split
+// evenly over the grid.  The workspace then holds one counter per tile and two 256 x 256
+// int32 partial tiles per workgroup.
+constexpr int64_t kStreamKGrid = 256;
+inline int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256); }
+inline bool stream_k_shape(int64_t M, int64_t K, int64_t N) {
+    const int64_t T = gemm_tiles(M, N);
+    return M > 0 && N > 0 && K > 0 && !small_batch(M, K, N) && T < 2 * kStreamKGrid && T % kStreamKGrid != 0;
+}
+constexpr int64_t kStreamKSlotBytes = 256 * 256 * 4;
+// the stream-K grid: one workgroup per unit (tile and K stage of 128) at most
+inline int64_t stream_k_grid(int64_t M, int64_t K, int64_t N) {
+    const int64_t units = gemm_tiles(M, N) * ((K + 127) / 128);
+    return units < kStreamKGrid ? units : kStreamKGrid;
+}
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_small(const GemmArgs& a, hipStream_t stream);
 

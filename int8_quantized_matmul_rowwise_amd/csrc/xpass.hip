@@ -77,10 +77,12 @@ constexpr int64_t kMaxKw = (133143 + 31) / 32 + 1;
 
 __global__ __launch_bounds__(1024) void compact_kernel(const uint32_t* __restrict__ partial, int64_t n_rb, int64_t Kw,
                                                        uint32_t* __restrict__ bitmap, int32_t* __restrict__ O,
-                                                       int32_t* __restrict__ n_out) {
+                                                       int32_t* __restrict__ n_out, int32_t* __restrict__ zero,
+                                                       int64_t n_zero) {
     __shared__ uint32_t bits[kMaxKw];
     __shared__ int32_t wsum[16];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    for (int64_t i = tid; i < n_zero; i += 1024) zero[i] = 0;
     for (int64_t w = tid; w < Kw; w += 1024) bits[w] = 0;
     __syncthreads();
     const int64_t total_entries = n_rb * Kw;
@@ -178,10 +180,10 @@ hipError_t launch_detect(int dt, const void* X, int64_t M, int64_t K, float tau,
 }
 
 hipError_t launch_compact(int64_t M, int64_t K, const uint32_t* partial, uint32_t* bitmap, int32_t* O,
-                          int32_t* n_out, hipStream_t stream) {
+                          int32_t* n_out, hipStream_t stream, int32_t* zero, int64_t n_zero) {
     const int64_t nrb = detect_row_blocks(M);
     const int64_t Kw = (M > 0 && K > 0) ? ceil_div(K, 32) : 0;
-    compact_kernel<<<1, 1024, 0, stream>>>(partial, nrb, Kw, bitmap, O, n_out);
+    compact_kernel<<<1, 1024, 0, stream>>>(partial, nrb, Kw, bitmap, O, n_out, zero, zero ? n_zero : 0);
     return hipGetLastError();
 }
 

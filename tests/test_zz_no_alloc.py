@@ -54,8 +54,8 @@ def test_noalloc_dry_run_stages(monkeypatch, capfd):
     # and a tiled call followed by a small-batch one
     [(16, 8192, 8192, "bf16"), (5, 4096, 1024, "bf16")],
     [(300, 1040, 520, "fp16"), (257, 272, 264, "fp16")],
-    [(520, 2048, 1032, "bf16"), (33, 1024, 264, "bf16")],
-    [(300, 4096, 520, "fp16"), (260, 4096, 264, "fp16")],
+    [(520, 512, 1032, "bf16"), (33, 1024, 264, "bf16")],
+    [(300, 1024, 264, "fp16"), (260, 1024, 264, "fp16")],
 ])
 def test_noalloc_equals_int8_matmul(shapes):
     for i, (M, K, N, dt) in enumerate(shapes):

@@ -25,6 +25,7 @@ chosen columns are the first n of a seeded random permutation of range(K), sorte
 """
 from __future__ import annotations
 
+import dataclasses
 from dataclasses import dataclass
 from typing import Optional, Sequence, Tuple
 
@@ -108,9 +109,17 @@ def make_w(K: int, N: int, dtype: str, *, sigma: float = 0.02, seed: int = 0, wi
     return w.to(DTYPES[dtype])
 
 
-def make_workload(name: str, seed: int = 0):
-    """(X, W, injected_cols, workload) for a named workload."""
-    wl = WORKLOADS[name]
+def with_rows(wl: Workload, rows: Optional[int]) -> Workload:
+    """The workload with another number of rows of X (the same weight and X distribution)."""
+    if rows is None or rows == wl.M:
+        return wl
+    return dataclasses.replace(wl, name=f"{wl.name}_m{rows}", M=int(rows))
+
+
+def make_workload(name: str, seed: int = 0, rows: Optional[int] = None):
+    """(X, W, injected_cols, workload) for a named workload; rows: another number of rows of X
+    (the first rows of the same draw: the generators run in row-major order)."""
+    wl = with_rows(WORKLOADS[name], rows)
     x, cols = make_x(wl.M, wl.K, wl.dtype, sigma=wl.x_sigma, n_outliers=wl.n_outliers,
                      outlier_range=wl.outlier_range, fixed_cols=wl.fixed_cols, seed=seed, wid=wl.wid)
     w = make_w(wl.K, wl.N, wl.dtype, sigma=wl.w_sigma, seed=seed, wid=wl.wid)
