@@ -4,7 +4,8 @@
 A step is one int8_matmul on resident inputs: the X pass (outlier columns, row scales,
 int8 codes, outlier gather) and the products with the dequantizing epilogue, issued as
 the two stages int8_matmul runs (int8_matmul_prepare, then int8_matmul_products) with a
-HIP event between them.  The weight conversion is offline and not timed.  Default
+HIP event between them (created without the system-scope fence, which would hold the next
+kernel back by about 3 us).  The weight conversion is offline and not timed.  Default
 workload: the 175B-like QKV projection, X 4096 x 12288 fp16 (7 outlier feature
 dimensions), W 12288 x 36864.
 
@@ -100,6 +101,18 @@ def product_kernel(M: int, K: int, N: int, group: int = 0) -> str:
     return "gemm_small_kernel" if lm.int8_matmul_workspace_layout(M, K, N)["small_batch"] else "gemm_kernel"
 
 
+def workload_args(wl, group: int = 0) -> str:
+    """The bench.py arguments that select the configuration wl (and group) names."""
+    import re
+
+    import workloads
+    base, rows = wl.name, None
+    m = re.match(r"(.+)_m(\d+)$", wl.name)
+    if m and m.group(1) in workloads.WORKLOADS:
+        base, rows = m.group(1), int(m.group(2))
+    return f"--workload {base}" + (f" --rows {rows}" if rows else "") + (f" --group {group}" if group else "")
+
+
 def workload_tag(wl, group: int = 0) -> str:
     """The name of a timed configuration: the workload, with the group size for the group-wise path."""
     return f"{wl.name}_g{group}" if group else wl.name
@@ -168,11 +181,48 @@ def time_loop(fn, steps: int, torch) -> float:
     return s.elapsed_time(e) / steps
 
 
+class HipEvent:
+    """A timing event recorded without the system-scope fence: HIP's default event record
+    releases to system scope, which delays the next kernel on the stream by about 3 us (an
+    event between the X pass and the products of a decode step added that much to the
+    step); without the fence the stage events cost nothing measurable."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if HipEvent._hip is None:
+            h = ctypes.CDLL("libamdhip64.so")
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipEvent._hip = h
+        self._ct = ctypes
+        self.ev = ctypes.c_void_p()
+        if HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev), self.DISABLE_SYSTEM_FENCE):
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream):
+        if HipEvent._hip.hipEventRecord(self.ev, self._ct.c_void_p(int(stream.cuda_stream))):
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end) -> float:
+        ms = self._ct.c_float()
+        if HipEvent._hip.hipEventElapsedTime(self._ct.byref(ms), self.ev, end.ev):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.ev:
+            HipEvent._hip.hipEventDestroy(self.ev)
+
+
 def timed_steps(stages, steps: int, warmup: int, torch, stream, flush=None):
     """Run warmup + `steps` steps, each the callables in `stages` in order, with an event on
-    `stream` before, between and after them; flush (if given) runs before every step,
-    outside its events.  Returns (mean ms of the whole step, mean ms of each stage, wall s
-    of the timed steps)."""
+    `stream` before, between and after them (HipEvent: no system fence); flush (if given)
+    runs before every step, outside its events.  Returns (mean ms of the whole step, mean
+    ms of each stage, wall s of the timed steps)."""
     def run(evs):
         if flush is not None:
             flush()
@@ -186,7 +236,7 @@ def timed_steps(stages, steps: int, warmup: int, torch, stream, flush=None):
     for _ in range(warmup):
         run(None)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    evs = [[HipEvent() for _ in range(len(stages) + 1)] for _ in range(steps)]
     t0 = time.perf_counter()
     for ev in evs:
         run(ev)
@@ -392,7 +442,6 @@ def _per_dispatch(rows, counter: str, match) -> dict:
 def traffic_summary(fetch_dir: str, write_dir: str, wl, copy_mib: int, group: int = 0) -> int:
     kernel = product_kernel(wl.M, wl.K, wl.N, group)
     tag = workload_tag(wl, group)
-    gflag = f" --group {group}" if group else ""
     copy_bytes = copy_mib * 1024 * 1024
     is_copy = lambda name: "elementwise_kernel" in name  # the calibration copy (torch add of 1 GiB)
     is_prod = lambda name: f"::{kernel}<" in name
@@ -433,12 +482,12 @@ def traffic_summary(fetch_dir: str, write_dir: str, wl, copy_mib: int, group: in
               "Commands (from the repository root on the GPU box, then on any host):", "",
               "    cd /tmp && export TMPDIR=/tmp; cd -",
               f"    rocprofv3 --pmc FETCH_SIZE --output-format csv -d {fetch_dir} -o run -- python3 bench.py "
-              f"--workload {wl.name}{gflag} --steps 3 --warmup 1 --no-cpu-baseline --no-fp16-gemm --no-warm "
+              f"{workload_args(wl, group)} --steps 3 --warmup 1 --no-cpu-baseline --no-fp16-gemm --no-warm "
               f"--no-ceilings --copy-mib {copy_mib}",
               f"    rocprofv3 --pmc WRITE_SIZE --output-format csv -d {write_dir} -o run -- python3 bench.py "
-              f"--workload {wl.name}{gflag} --steps 3 --warmup 1 --no-cpu-baseline --no-fp16-gemm --no-warm "
+              f"{workload_args(wl, group)} --steps 3 --warmup 1 --no-cpu-baseline --no-fp16-gemm --no-warm "
               f"--no-ceilings --copy-mib {copy_mib}",
-              f"    python3 bench.py --traffic-summary {fetch_dir} {write_dir} --workload {wl.name}{gflag} "
+              f"    python3 bench.py --traffic-summary {fetch_dir} {write_dir} {workload_args(wl, group)} "
               f"--copy-mib {copy_mib}", ""]
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(record_path(kernel, "traffic", tag, "json"), "w") as f:
@@ -464,7 +513,6 @@ def counter_summary(d: str, wl, group: int = 0) -> int:
     with --kernel-trace and --pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES (+ MFMA op counts)."""
     kernel = product_kernel(wl.M, wl.K, wl.N, group)
     tag = workload_tag(wl, group)
-    gflag = f" --group {group}" if group else ""
     is_prod = lambda name: f"::{kernel}<" in name
     rows = _counter_rows(d)
     dur = _durations(rows, is_prod)
@@ -508,9 +556,9 @@ def counter_summary(d: str, wl, group: int = 0) -> int:
     lines += ["", "Command (repository root on the GPU box, then on any host):", "",
               "    cd /tmp && export TMPDIR=/tmp; cd -",
               f"    rocprofv3 --kernel-trace --pmc {' '.join(counters)} --output-format csv -d {d} -o run -- "
-              f"python3 bench.py --workload {wl.name}{gflag} --steps 5 --warmup 1 --no-cpu-baseline --no-fp16-gemm "
+              f"python3 bench.py {workload_args(wl, group)} --steps 3 --warmup 1 --no-cpu-baseline --no-fp16-gemm "
               f"--no-warm --no-ceilings",
-              f"    python3 bench.py --counter-summary {d} --workload {wl.name}{gflag}", ""]
+              f"    python3 bench.py --counter-summary {d} {workload_args(wl, group)}", ""]
     with open(record_path(kernel, "counters", tag, "json"), "w") as f:
         json.dump(out, f, indent=1)
         f.write("\n")
@@ -556,6 +604,10 @@ def trace_summary(trace_dir: str, bench_json: str, wl, cmd: str, group: int = 0)
                 frac = algorithmic_bytes(wl, group) / (avg_prod * 1e-6) / 1e9 / roof["peak"]
             lines.append(f"trace average of {kernel}: {avg_prod:.1f} us ({(avg_prod / (ms * 1e3) - 1) * 100:+.1f} % "
                          f"vs the events): roofline frac from the trace {frac:.4f}")
+            if avg_prod < 0.95 * ms * 1e3:
+                lines.append("(the events bracket the product stage from the end of the X pass: under the profiler "
+                             "the dispatch gap before the kernel, which lands inside that bracket, grows by a few "
+                             "us, a large share of a short kernel; without the profiler the two agree more closely)")
     lines += ["", "Command (repository root on the GPU box):", "", "    " + cmd, ""]
     out = os.path.join(ROOT, "profiles", f"kernel_trace_{tag}.md")
     with open(out, "w") as f:
