@@ -304,12 +304,18 @@ __global__ __launch_bounds__(256) void code_rows_kernel(const uint16_t* __restri
     int32_t* wrank = (int32_t*)(dyn_lds + Kw);
     constexpr int H = HOLD > 0 ? HOLD : 1;
     u32x4 va[H];
+    // through a buffer resource over the row: 32-bit lane offsets (the whole offset, which
+    // the range check covers), no 64-bit address per chunk, and chunks past the row read 0,
+    // so every load is issued
     auto load_row = [&](u32x4(&v)[H], int64_t i) {
-        const uint16_t* row = X + i * K;
+        const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc((void*)(X + i * K), (short)0, (int)(2 * K),
+                                                                            0x00020000);
+        uint32_t off = 16 * tid;  // stepped behind an opaque copy: one register, not one per chunk
 #pragma unroll
         for (int h = 0; h < H; ++h) {
-            const int64_t c = tid + 256 * h;
-            v[h] = c < nch ? *(const u32x4*)(row + c * 8) : u32x4{0u, 0u, 0u, 0u};
+            v[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, 0));
+            off += 16 * 256;
+            asm volatile("" : "+v"(off));
         }
     };
     if constexpr (HOLD > 0) load_row(va, g);  // in flight during the set-up
@@ -354,7 +360,7 @@ __global__ __launch_bounds__(256) void code_rows_kernel(const uint16_t* __restri
         if constexpr (HOLD > 0) {
 #pragma unroll
             for (int h = 0; h < HOLD; ++h) {
-                const int64_t c = tid + 256 * h;
+                const int c = tid + 256 * h;
                 const uint32_t o = c < nch ? obits(c) : 0u;  // chunks past the row hold zeros
                 mb = absmax_bits(mb, v[h], o, wave_any(o));
             }
@@ -385,9 +391,13 @@ __global__ __launch_bounds__(256) void code_rows_kernel(const uint16_t* __restri
             }
         };
         if constexpr (HOLD > 0) {
+            // one chunk at a time: the index is opaque per chunk (and memory is clobbered), so
+            // the compiler neither keeps the first pass's flags nor codes several chunks ahead
+            int tx = tid;
 #pragma unroll
             for (int h = 0; h < HOLD; ++h) {
-                const int64_t c = tid + 256 * h;
+                asm volatile("" : "+v"(tx)::"memory");
+                const int c = tx + 256 * h;
                 if (c < nch) code_store(v[h], c);
             }
         } else {
