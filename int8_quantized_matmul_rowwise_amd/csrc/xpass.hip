@@ -718,7 +718,10 @@ __global__ __launch_bounds__(256) void code_slab_kernel(const uint16_t* __restri
 template <int DT, int HOLD>
 static hipError_t code_rows_launch1(const XPassArgs& a, const uint32_t* bitmap, int32_t* O, int32_t* n_out,
                                     int64_t n_wo, hipStream_t stream) {
-    // persistent row workgroups: as many as fit on the device at once (at most M)
+    // persistent row workgroups: as many as fit on the device at once (at most M).  Rows of
+    // more than 16384 elements (HOLD 16) take one workgroup each instead, which measured
+    // faster at every batch tried (K = 28672: 246 -> 237 us at M = 8192, 136 -> 132 us at
+    // M = 4096), while at K = 12288 the persistent form stays about 1 us ahead.
     const size_t lds = (size_t)ceil_div(a.K, 32) * 8;
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -726,7 +729,7 @@ static hipError_t code_rows_launch1(const XPassArgs& a, const uint32_t* bitmap, 
     if (e == hipSuccess)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, code_rows_kernel<DT, HOLD>, 256, lds);
     if (e != hipSuccess) return e;
-    int64_t groups = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    int64_t groups = HOLD == 16 ? a.M : (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     groups = groups < a.M ? groups : a.M;
     const unsigned grid = (unsigned)(n_wo + groups);
     if (grid == 0) return hipSuccess;
