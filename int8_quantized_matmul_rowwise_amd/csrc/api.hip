@@ -45,7 +45,8 @@ int check_shape(int64_t M, int64_t K, int64_t N, int dtype) {
 int check_threshold(float t) { return (isnan(t) || t < 0.0f) ? LLMINT8_EINVAL : LLMINT8_OK; }
 
 struct Layout {
-    size_t xq, xq_pitch, s_x, n_outliers, outliers, xo, xo_pitch, wo, bitmap, partial, pmax, sk_cnt, sk_part, total;
+    size_t xq, xq_pitch, s_x, n_outliers, outliers, xo, xo_pitch, wo, bitmap, partial, pmax, xqb, sk_cnt, sk_part,
+        total;
     bool sk;  // the tiled product kernel runs stream-K for these sizes
 };
 
@@ -75,6 +76,9 @@ Layout make_layout(int64_t M, int64_t K, int64_t N) {
     off = align_up(off + 4 * kw * (size_t)detect_row_blocks(M));
     L.pmax = off;  // small batches: per row and 512-column slab, the slab's row maximum
     off = align_up(off + (small_batch(M, K, N) ? 4 * m * (size_t)ceil_div(K, 512) : 0));
+    L.xqb = off;  // small batches of 8 rows or more: Xq again, in the product kernel's 1 KB blocks
+    const bool blocked = small_batch(M, K, N) && small_blocked_codes(M);
+    off = align_up(off + (blocked ? (size_t)round_up(M, 16) * (size_t)ceil_div(K, 64) * 64 : 0));
     // stream-K (tiled path, few tiles): a counter per tile, two partial tiles per workgroup
     L.sk = stream_k_shape(M, K, N);
     L.sk_cnt = off;
@@ -150,8 +154,11 @@ int run_xpass(const void* X, int64_t M, int64_t K, int dtype, float tau, const i
     a.s_x = (float*)(ws + L.s_x);
     a.XO = ws + L.xo;
     a.xo_pitch = (int64_t)L.xo_pitch;
-    if (small_batch(M, K, N))
+    if (small_batch(M, K, N)) {
+        a.Xqb = small_blocked_codes(M) ? ws + L.xqb : nullptr;
         return hip_status(stage("xpass_small", [&] { return launch_xpass_small(a, O, nO, bitmap, (uint32_t*)(ws + L.pmax), st); }));
+    }
+    a.Xqb = nullptr;
     int32_t* sk_cnt = L.sk ? (int32_t*)(ws + L.sk_cnt) : nullptr;  // zeroed for the product kernel
     const int64_t n_tiles = gemm_tiles(M, N);
     hipError_t e = stage("detect", [&] { return launch_detect(dtype, X, M, K, tau, partial, st); });
@@ -245,6 +252,8 @@ int products_common(int64_t M, int64_t K, int dtype, const int8_t* Wq, const flo
     g.F_acc = F;
     g.sk_cnt = L.sk ? (int32_t*)(ws + L.sk_cnt) : nullptr;
     g.sk_part = L.sk ? (int32_t*)(ws + L.sk_part) : nullptr;
+    // the small-batch X pass writes the blocked copy; the fixed-set X pass (row coding) does not
+    g.Xqb = !WO_fixed && small_blocked_codes(M) ? ws + L.xqb : nullptr;
     if (small_batch(M, K, N)) return hip_status(stage("gemm_small", [&] { return launch_gemm_small(g, (hipStream_t)stream); }));
     return hip_status(stage("gemm", [&] { return launch_gemm(g, (hipStream_t)stream); }));
 }
@@ -275,6 +284,7 @@ int run_xpass_fixed(const void* X, int64_t M, int64_t K, int64_t N, int dtype, c
         a.n_out = n_out;
         a.Xq = ws + L.xq;
         a.xq_pitch = (int64_t)L.xq_pitch;
+        a.Xqb = nullptr;
         a.s_x = (float*)(ws + L.s_x);
         a.XO = ws + L.xo;
         a.xo_pitch = (int64_t)L.xo_pitch;

@@ -59,4 +59,13 @@ __device__ __forceinline__ float wave_max(float v) {
 __host__ __device__ constexpr int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 __host__ __device__ constexpr int64_t ceil_div(int64_t v, int64_t m) { return (v + m - 1) / m; }
 
+// Small batches also keep Xq in the small-batch product kernel's operand layout: blocks of
+// 16 rows x 64 columns (1 KB, row-major inside), the nsteps = ceil(K/64) blocks of one
+// group of 16 rows in K order, then the next group.  One operand load of that kernel (16
+// rows x 64 bytes) is then one 1 KB block, eight whole cache lines, instead of 16 halves
+// of lines.  Columns K..64*nsteps of a block are 0; rows past M are not stored.
+__host__ __device__ constexpr int64_t xqb_offset(int64_t r, int64_t k, int64_t nsteps) {
+    return ((r >> 4) * nsteps + (k >> 6)) * 1024 + (r & 15) * 64 + (k & 63);
+}
+
 }  // namespace llmint8

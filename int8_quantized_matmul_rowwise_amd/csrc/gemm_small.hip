@@ -7,7 +7,9 @@
 // flight (the next batch is loaded before the current one's MFMAs).  Two 64-deep steps of
 // a wave cover one 128-byte line of each Wq row.  Every workgroup re-reads all of Xq from
 // the cache; with 32 columns per workgroup each X operand load feeds two MFMAs, which
-// halves those re-reads (they grow with M).  Partial int32 sums are combined exactly
+// halves those re-reads (they grow with M).  From 8 rows up they read the blocked copy of
+// Xq that the small-batch X pass writes (xqb_offset), where one operand load is one 1 KB
+// block, eight whole cache lines, instead of halves of 16 lines.  Partial int32 sums are combined exactly
 // through LDS.  Each workgroup gathers the 16-bit outlier operands Wq[n, O[t]] of its own
 // columns, at kernel start so that the scattered loads overlap the weight stream.
 // "LLM.int8(): 8-bit Matrix Multiplication for Transformers at Scale", abstract.
@@ -22,6 +24,7 @@ namespace {
 struct SmallParams {
     const int8_t* Xq;
     int64_t xq_pitch;
+    const int8_t* Xqb;  // NULL: Xq row by row; else the blocked copy (xqb_offset)
     const int8_t* Wq;
     int64_t M, N, K;
     const float* s_x;
@@ -82,7 +85,7 @@ __device__ __forceinline__ void gather_w_side(const SmallParams& p, int64_t n, i
 // stream never waits for the arithmetic.  WAVES waves split K; waves g * NC + c (g < MG,
 // c < NC) finish the row group g of column group c: MG * NC <= WAVES.
 template <int DT, int MG, int NC, int WAVES, bool ACC_OUT>
-__global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(SmallParams p) {
+__global__ __launch_bounds__(64 * WAVES, MG == 1 && NC == 1 ? 3 : 1) void gemm_small_kernel(SmallParams p) {
     static_assert(MG * NC <= WAVES, "one finishing wave per row and column group");
     constexpr int kWaves = WAVES;
     constexpr int PAIRS = MG == 1 ? 4 : (MG * NC == 2 ? 2 : 1);
@@ -97,13 +100,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(SmallParams p) {
         const int64_t n = n0 + 16 * c + li < p.N ? n0 + 16 * c + li : p.N - 1;
         brow[c] = p.Wq + n * p.K;
     }
+    const int64_t nsteps = ceil_div(p.K, 64);
+    // lane's X row: its bytes of step st at arow[g] + (st << ash) + 16 q.  Row by row the
+    // rows are zero-padded up to a multiple of 256 bytes; in the blocked copy one step of a
+    // row group is one 1 KB block (whole cache lines), zero past K.  Rows past M read row
+    // M - 1 (their sums are not stored).
     const int8_t* arow[MG];
+    const int ash = p.Xqb ? 10 : 6;
 #pragma unroll
     for (int g = 0; g < MG; ++g) {
         const int64_t m = g * 16 + li < p.M ? g * 16 + li : p.M - 1;
-        arow[g] = p.Xq + m * p.xq_pitch;  // rows are zero-padded up to a multiple of 256 bytes
+        arow[g] = p.Xqb ? p.Xqb + xqb_offset(m, 0, nsteps) : p.Xq + m * p.xq_pitch;
     }
-    const int64_t nsteps = ceil_div(p.K, 64);
 
     // The outlier operands of the epilogue (first 32 outlier columns), gathered now so that
     // their scattered loads overlap the weight stream: for the finishing wave of (g, c),
@@ -136,7 +144,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_small_kernel(SmallParams p) {
 #pragma unroll
             for (int c = 0; c < NC; ++c) b[u][c] = (in && k < p.K) ? *(const v4i*)(brow[c] + k) : v4i{0, 0, 0, 0};
 #pragma unroll
-            for (int g = 0; g < MG; ++g) a[u][g] = in ? *(const v4i*)(arow[g] + k) : v4i{0, 0, 0, 0};
+            for (int g = 0; g < MG; ++g)
+                a[u][g] = in ? *(const v4i*)(arow[g] + (st << ash) + q * 16) : v4i{0, 0, 0, 0};
         }
     };
     auto compute = [&](const v4i (&b)[U][NC], const v4i (&a)[U][MG]) {
@@ -257,6 +266,7 @@ hipError_t launch_gemm_small(const GemmArgs& a, hipStream_t stream) {
     SmallParams p;
     p.Xq = a.Xq;
     p.xq_pitch = a.xq_pitch;
+    p.Xqb = a.Xqb;
     p.Wq = a.Wq;
     p.M = a.M;
     p.N = a.N;

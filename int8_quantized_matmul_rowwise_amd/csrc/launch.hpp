@@ -60,6 +60,7 @@ struct XPassArgs {
     const int32_t* n_out;
     int8_t* Xq;
     int64_t xq_pitch;
+    int8_t* Xqb;  // nullable: the blocked copy of Xq (small batches)
     float* s_x;
     void* XO;
     int64_t xo_pitch;
@@ -68,6 +69,10 @@ struct XPassArgs {
 };
 hipError_t launch_code_rows(const XPassArgs& a, const uint32_t* bitmap, int32_t* O, int32_t* n_out,
                             hipStream_t stream);
+// The small-batch X pass also writes Xq in the product kernel's 1 KB blocks (xqb_offset)
+// from 8 rows up: with fewer rows the operand loads touch few cache lines either way (at
+// M = 1 every lane reads the same row), and the extra writes cost more than they save.
+inline bool small_blocked_codes(int64_t M) { return M >= 8; }
 // pmax (M x ceil(K/512) words of scratch): per row and 512-column slab, the slab's
 // maximum over its non-outlier columns
 hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, uint32_t* bitmap, uint32_t* pmax,
@@ -78,6 +83,8 @@ struct GemmArgs {
     int dt;
     const int8_t* Xq;
     int64_t xq_pitch;
+    const int8_t* Xqb = nullptr;  // small-batch kernel: the blocked copy of Xq when the X
+                                  // pass wrote one (xqb_offset), else Xq row by row
     const int8_t* Wq;
     int64_t M, N, K;
     const float* s_x;

@@ -432,8 +432,9 @@ template <int DT>
 __global__ __launch_bounds__(1024) void xpass_one_kernel(const uint16_t* __restrict__ X, int M, int K, float tau,
                                                          uint32_t* __restrict__ bitmap, int32_t* __restrict__ O,
                                                          int32_t* __restrict__ n_out, int8_t* __restrict__ Xq,
-                                                         int xq_pitch, float* __restrict__ s_x,
-                                                         uint16_t* __restrict__ XO, int xo_pitch) {
+                                                         int xq_pitch, int8_t* __restrict__ Xqb, int nsteps,
+                                                         float* __restrict__ s_x, uint16_t* __restrict__ XO,
+                                                         int xo_pitch) {
     __shared__ uint32_t bits[1024];
     __shared__ int32_t wrank[1024];
     __shared__ uint32_t rmax[kSmallM];
@@ -529,7 +530,9 @@ __global__ __launch_bounds__(1024) void xpass_one_kernel(const uint16_t* __restr
         const int rr = r[u], cc = c[u];
         const float inv = inv_scale(to_f32<DT>((uint16_t)rmax[rr]));
         const uint32_t o = obits(cc);
-        *(u32x2*)(Xq + rr * xq_pitch + 8 * cc) = code_chunk<DT>(v[u], o, inv, true);
+        const u32x2 q = code_chunk<DT>(v[u], o, inv, true);
+        *(u32x2*)(Xq + rr * xq_pitch + 8 * cc) = q;
+        if (Xqb) *(u32x2*)(Xqb + xqb_offset(rr, 8 * cc, nsteps)) = q;
         if (o) {
             int32_t t = wrank[cc >> 2] + __popc(bits[cc >> 2] & ((1u << (8 * (cc & 3))) - 1u));
 #pragma unroll
@@ -541,6 +544,10 @@ __global__ __launch_bounds__(1024) void xpass_one_kernel(const uint16_t* __restr
     const int pad_c = (xq_pitch - K) / 8, pad_o = ((total + 31) & ~31) - total;
     for (int e = tid; e < M * pad_c; e += 1024)
         *(u32x2*)(Xq + (e / pad_c) * xq_pitch + K + 8 * (e % pad_c)) = u32x2{0u, 0u};
+    const int pad_b = 8 * nsteps - K / 8;  // the blocked copy's zero columns, K .. 64 nsteps
+    if (Xqb)
+        for (int e = tid; e < M * pad_b; e += 1024)
+            *(u32x2*)(Xqb + xqb_offset(e / pad_b, K + 8 * (e % pad_b), nsteps)) = u32x2{0u, 0u};
     for (int e = tid; e < M * pad_o; e += 1024) XO[(e / pad_o) * xo_pitch + total + e % pad_o] = 0;
 }
 
@@ -618,6 +625,7 @@ __global__ __launch_bounds__(256) void code_slab_kernel(const uint16_t* __restri
                                                         const uint32_t* __restrict__ pmax, int64_t nslab,
                                                         int32_t* __restrict__ O, int32_t* __restrict__ n_out,
                                                         int8_t* __restrict__ Xq, int64_t xq_pitch,
+                                                        int8_t* __restrict__ Xqb, int64_t nsteps,
                                                         float* __restrict__ s_x, uint16_t* __restrict__ XO,
                                                         int64_t xo_pitch) {
     __shared__ float inv_s[4];
@@ -700,7 +708,9 @@ __global__ __launch_bounds__(256) void code_slab_kernel(const uint16_t* __restri
         if (live) {
             wd = wb[(c >> 2) - 16 * sl];
             const uint32_t o = (wd >> (8 * (c & 3))) & 0xffu;
-            *(u32x2*)(Xq + r * xq_pitch + 8 * c) = code_chunk<DT>(v, o, inv_s[w], o != 0u);
+            const u32x2 q = code_chunk<DT>(v, o, inv_s[w], o != 0u);
+            *(u32x2*)(Xq + r * xq_pitch + 8 * c) = q;
+            if (Xqb) *(u32x2*)(Xqb + xqb_offset(r, 8 * c, nsteps)) = q;
             if (o) {
                 int32_t t = wr[(c >> 2) - 16 * sl] + __popc(wd & ((1u << (8 * (c & 3))) - 1u));
 #pragma unroll
@@ -709,6 +719,7 @@ __global__ __launch_bounds__(256) void code_slab_kernel(const uint16_t* __restri
             }
         } else if (c < Cp) {
             *(u32x2*)(Xq + r * xq_pitch + 8 * c) = u32x2{0u, 0u};
+            if (Xqb && c < 8 * nsteps) *(u32x2*)(Xqb + xqb_offset(r, 8 * c, nsteps)) = u32x2{0u, 0u};
         }
         if (sl == 0)
             for (int32_t t = total + lane; t < P; t += 64) XO[r * xo_pitch + t] = 0;
@@ -765,13 +776,16 @@ hipError_t launch_code_rows(const XPassArgs& a, const uint32_t* bitmap, int32_t*
 hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, uint32_t* bitmap, uint32_t* pmax,
                               hipStream_t stream) {
     const uint16_t* x = (const uint16_t*)a.X;
+    const int64_t nsteps = ceil_div(a.K, 64);  // blocks per row group of the blocked copy
     if (a.K > 0 && a.M * a.K <= kOneMaxElems) {
         if (a.dt == F16)
             xpass_one_kernel<F16><<<1, 1024, 0, stream>>>(x, (int)a.M, (int)a.K, a.tau, bitmap, O, n_out, a.Xq,
-                                                          (int)a.xq_pitch, a.s_x, (uint16_t*)a.XO, (int)a.xo_pitch);
+                                                          (int)a.xq_pitch, a.Xqb, (int)nsteps, a.s_x,
+                                                          (uint16_t*)a.XO, (int)a.xo_pitch);
         else
             xpass_one_kernel<BF16><<<1, 1024, 0, stream>>>(x, (int)a.M, (int)a.K, a.tau, bitmap, O, n_out, a.Xq,
-                                                           (int)a.xq_pitch, a.s_x, (uint16_t*)a.XO, (int)a.xo_pitch);
+                                                           (int)a.xq_pitch, a.Xqb, (int)nsteps, a.s_x,
+                                                           (uint16_t*)a.XO, (int)a.xo_pitch);
         return hipGetLastError();
     }
     const int64_t nslab = ceil_div(a.K / 8, 64);
@@ -795,10 +809,10 @@ hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, ui
     const dim3 g2((unsigned)(gx > 0 ? gx : 1), (unsigned)ceil_div(a.M, 4));
     if (a.dt == F16)
         code_slab_kernel<F16><<<g2, 256, 0, stream>>>(x, a.M, a.K, bitmap, pmax, nslab, O, n_out, a.Xq, a.xq_pitch,
-                                                      a.s_x, (uint16_t*)a.XO, a.xo_pitch);
+                                                      a.Xqb, nsteps, a.s_x, (uint16_t*)a.XO, a.xo_pitch);
     else
         code_slab_kernel<BF16><<<g2, 256, 0, stream>>>(x, a.M, a.K, bitmap, pmax, nslab, O, n_out, a.Xq, a.xq_pitch,
-                                                       a.s_x, (uint16_t*)a.XO, a.xo_pitch);
+                                                       a.Xqb, nsteps, a.s_x, (uint16_t*)a.XO, a.xo_pitch);
     return hipGetLastError();
 }
 

@@ -67,7 +67,11 @@ def test_ragged_medium(dt):
                                       (2, 65536, 8, "bf16"), (16, 40976, 24, "fp16"), (8, 65552, 16, "fp16"),
                                       # 65 to 128 rows on the small-batch path (5 to 8 row groups), one
                                       # of them through the one-workgroup X pass
-                                      (80, 1024, 512, "fp16"), (128, 2048, 264, "bf16"), (100, 304, 136, "fp16")])
+                                      (80, 1024, 512, "fp16"), (128, 2048, 264, "bf16"), (100, 304, 136, "fp16"),
+                                      # the fewest rows that take the blocked copy of the codes (8), through
+                                      # the slab launches with K % 64 = 16, and a partial row group (12)
+                                      # through the one-workgroup X pass
+                                      (8, 4112, 72, "bf16"), (12, 2048, 40, "fp16")])
 def test_edge_shapes(M, K, N, dt):
     _banner(f"edge {M}x{K}x{N} {dt}")
     x, w = _case(M, K, N, dt, n_out=2, seed=M + K + N)
