@@ -531,16 +531,19 @@ LLMINT8_API int int8_matmul_fixed(const void* X, int64_t M, int64_t K, int dtype
 namespace {
 
 struct GroupLayout {
-    size_t xq, s_x, rg, total;
+    size_t xq, s_x, rg, xqb, total;
+    bool blocked;  // the X pass also writes the blocked copy (xqb) for the small-batch kernel
 };
 
 GroupLayout group_layout(int64_t M, int64_t K, int64_t G) {
     GroupLayout L;
     const size_t m = (size_t)M, ng = (size_t)(K / G);
+    L.blocked = group_blocked_codes(M, K, G);
     L.xq = 0;
     L.s_x = align_up(m * (size_t)K);
     L.rg = align_up(L.s_x + 4 * m * ng);
-    L.total = align_up(L.rg + 4 * m * ng);
+    L.xqb = align_up(L.rg + 4 * m * ng);
+    L.total = align_up(L.xqb + (L.blocked ? (size_t)round_up(M, 16) * (size_t)K : 0));
     return L;
 }
 
@@ -612,9 +615,10 @@ int group_common(const void* X, int64_t M, int64_t K, int dtype, int64_t group, 
     const bool small = products && N > 0 && group_small_batch(M, K, N, group);
     log_call(xpass ? (products ? "int8_matmul_group" : "int8_matmul_group_prepare") : "int8_matmul_group_products", M, K,
              N, dtype, NAN, small ? "group_small_batch" : "group_tiled");
-    if (xpass) e = stage("group_xpass", [&] { return launch_group_xpass(dtype, X, M, K, group, Xq, s_x, rg, st); });
+    int8_t* Xqb = L.blocked ? ws + L.xqb : nullptr;
+    if (xpass) e = stage("group_xpass", [&] { return launch_group_xpass(dtype, X, M, K, group, Xq, s_x, rg, Xqb, st); });
     if (e == hipSuccess && products && N > 0)
-        e = small ? stage("gemm_group_small", [&] { return launch_gemm_group_small(dtype, Xq, rg, Wq, w_scale, M, N, K, group, Y, st); })
+        e = small ? stage("gemm_group_small", [&] { return launch_gemm_group_small(dtype, Xq, Xqb, rg, Wq, w_scale, M, N, K, group, Y, st); })
                   : stage("gemm_group", [&] { return launch_gemm_group(dtype, Xq, rg, Wq, w_scale, M, N, K, group, Y, st); });
     return hip_status(e);
 }

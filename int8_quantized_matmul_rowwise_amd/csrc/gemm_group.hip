@@ -351,10 +351,12 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_group_kernel(GroupParams p) 
 // ---- X pass: the group-wise codes of X.  Row groups never cross rows (G divides K), so X
 // is a flat run of M * ng groups of G elements: SEG lanes take one group (SEG = 64, or 16 /
 // 32 for G = 128 / 256), each lane NV 16-byte chunks of 8 elements, one wave access 1 KB.
+// Xqb (nullable; used for G = 256 to 1024): the codes again, in the small-batch kernel's blocks
+// (K is a multiple of G, hence of 64: no padding).
 template <int DT, int NV, int SEG>
 __global__ __launch_bounds__(256) void group_rows_kernel(const uint16_t* __restrict__ X, int64_t M, int64_t K,
                                                          int64_t G, int8_t* __restrict__ Xq, float* __restrict__ s_x,
-                                                         float* __restrict__ rg) {
+                                                         float* __restrict__ rg, int8_t* __restrict__ Xqb) {
     constexpr int BPW = 64 / SEG;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int sub = lane / SEG, sl = lane % SEG;
@@ -384,6 +386,8 @@ __global__ __launch_bounds__(256) void group_rows_kernel(const uint16_t* __restr
         }
         const float s = to_f32<DT>((uint16_t)m);
         const float inv = inv_scale(s);
+        int8_t* qb = nullptr;  // groups of at most 1024 (NV <= 2): more would cost occupancy here
+        if constexpr (NV <= 2) qb = Xqb && in ? Xqb + xqb_offset(b / ng, (b % ng) * G + 8 * sl, K / 64) : nullptr;
 #pragma unroll
         for (int j = 0; j < NV; ++j) {
             uint32_t t[8];
@@ -396,7 +400,11 @@ __global__ __launch_bounds__(256) void group_rows_kernel(const uint16_t* __restr
             u32x2 q;
             q[0] = __builtin_amdgcn_perm(t[1], t[0], 0x0c0c0400u) | __builtin_amdgcn_perm(t[3], t[2], 0x04000c0cu);
             q[1] = __builtin_amdgcn_perm(t[5], t[4], 0x0c0c0400u) | __builtin_amdgcn_perm(t[7], t[6], 0x04000c0cu);
-            if (in) *(u32x2*)(Xq + lo + 8 * ((int64_t)j * SEG + sl)) = q;
+            if (in) {
+                *(u32x2*)(Xq + lo + 8 * ((int64_t)j * SEG + sl)) = q;
+                // chunk j lies 8 SEG columns (8 SEG / 64 blocks of 1 KB) past chunk 0
+                if (qb) *(u32x2*)(qb + (int64_t)j * SEG * 128) = q;
+            }
         }
         if (sl == 0 && in) {
             const int64_t i = b / ng, g = b % ng;
@@ -436,27 +444,27 @@ __global__ __launch_bounds__(256) void group_colmax_kernel(const uint16_t* __res
 
 template <int DT, int NV, int SEG>
 hipError_t group_rows_launch(const void* X, int64_t M, int64_t K, int64_t G, int8_t* Xq, float* s_x, float* rg,
-                             hipStream_t stream) {
+                             int8_t* Xqb, hipStream_t stream) {
     const int64_t nblocks = M * (K / G);
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
     const int64_t need = ceil_div(nblocks, 4 * (64 / SEG));
     const unsigned grid = (unsigned)(need < (int64_t)cus * 8 ? need : (int64_t)cus * 8);
-    group_rows_kernel<DT, NV, SEG><<<grid, 256, 0, stream>>>((const uint16_t*)X, M, K, G, Xq, s_x, rg);
+    group_rows_kernel<DT, NV, SEG><<<grid, 256, 0, stream>>>((const uint16_t*)X, M, K, G, Xq, s_x, rg, Xqb);
     return hipGetLastError();
 }
 
 template <int DT>
 hipError_t group_rows_dispatch(const void* X, int64_t M, int64_t K, int64_t G, int8_t* Xq, float* s_x, float* rg,
-                               hipStream_t stream) {
+                               int8_t* Xqb, hipStream_t stream) {
     switch (G) {
-        case 128: return group_rows_launch<DT, 1, 16>(X, M, K, G, Xq, s_x, rg, stream);
-        case 256: return group_rows_launch<DT, 1, 32>(X, M, K, G, Xq, s_x, rg, stream);
-        case 512: return group_rows_launch<DT, 1, 64>(X, M, K, G, Xq, s_x, rg, stream);
-        case 1024: return group_rows_launch<DT, 2, 64>(X, M, K, G, Xq, s_x, rg, stream);
-        case 2048: return group_rows_launch<DT, 4, 64>(X, M, K, G, Xq, s_x, rg, stream);
-        default: return group_rows_launch<DT, 8, 64>(X, M, K, G, Xq, s_x, rg, stream);  // 4096
+        case 128: return group_rows_launch<DT, 1, 16>(X, M, K, G, Xq, s_x, rg, Xqb, stream);
+        case 256: return group_rows_launch<DT, 1, 32>(X, M, K, G, Xq, s_x, rg, Xqb, stream);
+        case 512: return group_rows_launch<DT, 1, 64>(X, M, K, G, Xq, s_x, rg, Xqb, stream);
+        case 1024: return group_rows_launch<DT, 2, 64>(X, M, K, G, Xq, s_x, rg, Xqb, stream);
+        case 2048: return group_rows_launch<DT, 4, 64>(X, M, K, G, Xq, s_x, rg, Xqb, stream);
+        default: return group_rows_launch<DT, 8, 64>(X, M, K, G, Xq, s_x, rg, Xqb, stream);  // 4096
     }
 }
 
@@ -465,10 +473,10 @@ hipError_t group_rows_dispatch(const void* X, int64_t M, int64_t K, int64_t G, i
 bool group_size_ok(int64_t G, int64_t K) { return G >= 128 && G <= 4096 && (G & (G - 1)) == 0 && K % G == 0; }
 
 hipError_t launch_group_xpass(int dt, const void* X, int64_t M, int64_t K, int64_t G, int8_t* Xq, float* s_x,
-                              float* rg, hipStream_t stream) {
+                              float* rg, int8_t* Xqb, hipStream_t stream) {
     if (M == 0 || K == 0) return hipSuccess;
-    return dt == F16 ? group_rows_dispatch<F16>(X, M, K, G, Xq, s_x, rg, stream)
-                     : group_rows_dispatch<BF16>(X, M, K, G, Xq, s_x, rg, stream);
+    return dt == F16 ? group_rows_dispatch<F16>(X, M, K, G, Xq, s_x, rg, Xqb, stream)
+                     : group_rows_dispatch<BF16>(X, M, K, G, Xq, s_x, rg, Xqb, stream);
 }
 
 hipError_t launch_group_colmax(int dt, const void* W, int64_t K, int64_t N, int64_t G, float* s_w,

@@ -23,7 +23,8 @@ constexpr int kGsWaves = 4;
 constexpr int kGsMaxGroups = 64;
 
 struct GroupSmallParams {
-    const int8_t* Xq;  // M x K (pitch K)
+    const int8_t* Xq;   // M x K (pitch K)
+    const int8_t* Xqb;  // NULL, or the blocked copy of Xq (xqb_offset)
     const float* rg;   // ng x M, group-major
     const int8_t* Wq;  // N x K
     const float* s_w;  // N x ng
@@ -43,11 +44,14 @@ __global__ __launch_bounds__(256) void gemm_group_small_kernel(GroupSmallParams 
     const int64_t n0 = (int64_t)blockIdx.x * 16;
     const int64_t n = n0 + li < p.N ? n0 + li : p.N - 1;
     const int8_t* brow = p.Wq + n * p.K;
+    // lane's X row: its bytes of step st (of K) at arow[g] + (st << ash) + 16 q, row by row
+    // or in the blocked copy (one 1 KB block per step and row group)
     const int8_t* arow[MG];
+    const int ash = p.Xqb ? 10 : 6;
 #pragma unroll
     for (int g = 0; g < MG; ++g) {
         const int64_t m = g * 16 + li < p.M ? g * 16 + li : p.M - 1;
-        arow[g] = p.Xq + m * p.K;
+        arow[g] = p.Xqb ? p.Xqb + xqb_offset(m, 0, p.K / 64) : p.Xq + m * p.K;
     }
     const int ng = p.ng, spg = p.G / 64;
     // the factors (ordered before their first use by the first group's barrier)
@@ -67,10 +71,11 @@ __global__ __launch_bounds__(256) void gemm_group_small_kernel(GroupSmallParams 
         for (int u = 0; u < U; ++u) {
             const int s = s0 + 4 * u;
             const bool in = s < spg;
-            const int64_t k = (int64_t)g * p.G + s * 64 + q * 16;
+            const int64_t st = (int64_t)g * spg + s;
+            const int64_t k = st * 64 + q * 16;
             b[u] = in ? *(const v4i*)(brow + k) : v4i{0, 0, 0, 0};
 #pragma unroll
-            for (int m = 0; m < MG; ++m) a[u][m] = in ? *(const v4i*)(arow[m] + k) : v4i{0, 0, 0, 0};
+            for (int m = 0; m < MG; ++m) a[u][m] = in ? *(const v4i*)(arow[m] + (st << ash) + q * 16) : v4i{0, 0, 0, 0};
         }
     };
     v4i acc[MG];
@@ -150,11 +155,22 @@ bool group_small_batch(int64_t M, int64_t K, int64_t N, int64_t G) {
     return M <= 64 && K / G <= kGsMaxGroups && small_batch(M, K, N);
 }
 
-hipError_t launch_gemm_group_small(int dt, const int8_t* Xq, const float* rg, const int8_t* Wq, const float* s_w,
-                                   int64_t M, int64_t N, int64_t K, int64_t G, void* Y, hipStream_t stream) {
+// Measured on the 8192 x 8192 weight (cold steps, interleaved on one box), blocked against
+// row by row: G = 1024 24.3 against 27.1 us at M = 16 and 38.7 against 50.1 us at M = 64;
+// G = 512 26.1 / 27.3 and 42.0 / 53.4; G = 256 33.9 / 33.8 and 53.1 / 57.1; G = 128 at
+// M = 16 54.5 against 53.5 us (its two steps per group make the kernel bound by the
+// per-group barrier and fold, not by the operand loads).
+bool group_blocked_codes(int64_t M, int64_t K, int64_t G) {
+    return small_blocked_codes(M) && M <= 64 && K > 0 && G >= 256 && G <= 1024 && K / G <= kGsMaxGroups;
+}
+
+hipError_t launch_gemm_group_small(int dt, const int8_t* Xq, const int8_t* Xqb, const float* rg, const int8_t* Wq,
+                                   const float* s_w, int64_t M, int64_t N, int64_t K, int64_t G, void* Y,
+                                   hipStream_t stream) {
     if (M == 0 || N == 0) return hipSuccess;
     GroupSmallParams p;
     p.Xq = Xq;
+    p.Xqb = Xqb;
     p.rg = rg;
     p.Wq = Wq;
     p.s_w = s_w;

@@ -138,16 +138,22 @@ hipError_t launch_group_colmax(int dt, const void* W, int64_t K, int64_t N, int6
 // Wq (N x K) with the per-group column scales
 hipError_t launch_quantize_weight_groups(int dt, const void* W, int64_t K, int64_t N, const float* s_w, int64_t G,
                                          int8_t* Wq, hipStream_t stream);
-// Xq (M x K), s_x (M x ng) and rg (ng x M, RN32(s_x/127), group-major) of X's row groups
+// Xq (M x K), s_x (M x ng) and rg (ng x M, RN32(s_x/127), group-major) of X's row groups,
+// and, when Xqb is not NULL, Xq again in the small-batch kernel's 1 KB blocks (xqb_offset)
 hipError_t launch_group_xpass(int dt, const void* X, int64_t M, int64_t K, int64_t G, int8_t* Xq, float* s_x,
-                              float* rg, hipStream_t stream);
+                              float* rg, int8_t* Xqb, hipStream_t stream);
 // Y (M x N, 16-bit) = the group-wise product (per-group int32 partials folded into fp32)
 hipError_t launch_gemm_group(int dt, const int8_t* Xq, const float* rg, const int8_t* Wq, const float* s_w, int64_t M,
                              int64_t N, int64_t K, int64_t G, void* Y, hipStream_t stream);
 // Small batches of the group-wise path (M <= 64, K / G <= 64, where small_batch holds):
-// the split-N group kernel.
+// the split-N group kernel, reading the blocked copy Xqb when it is not NULL.
 bool group_small_batch(int64_t M, int64_t K, int64_t N, int64_t G);
-hipError_t launch_gemm_group_small(int dt, const int8_t* Xq, const float* rg, const int8_t* Wq, const float* s_w,
-                                   int64_t M, int64_t N, int64_t K, int64_t G, void* Y, hipStream_t stream);
+// The part of group_small_batch that does not depend on N, with at least 8 rows and groups
+// of 256 to 1024: where the group X pass writes the blocked copy (it runs before N is
+// known).
+bool group_blocked_codes(int64_t M, int64_t K, int64_t G);
+hipError_t launch_gemm_group_small(int dt, const int8_t* Xq, const int8_t* Xqb, const float* rg, const int8_t* Wq,
+                                   const float* s_w, int64_t M, int64_t N, int64_t K, int64_t G, void* Y,
+                                   hipStream_t stream);
 
 }  // namespace llmint8
