@@ -732,8 +732,9 @@ hipError_t launch_one(const Params& p, hipStream_t stream) {
     const int64_t G = cus < kStreamKGrid ? cus : kStreamKGrid;
     if (p.sk_cnt != nullptr && p.sk_part != nullptr && G > 0 && T < 2 * G && T % G != 0) {
         // at most one workgroup per unit, so that every workgroup's range holds a stage (the
-        // tile counts count the workgroups whose ranges meet the tile)
-        const int64_t units = T * ceil_div(p.K, BK), g = units < G ? units : G;  // <= stream_k_grid
+        // tile counts count the workgroups whose ranges meet the tile), and stream_k_per_tile
+        // per tile; the workspace holds slots for stream_k_grid(M, K, N) >= g workgroups
+        const int64_t g = stream_k_grid(p.M, p.K, p.N, G);
         gemm_kernel<DT, ACC_OUT, true, HALF><<<(unsigned)g, 64 * kWaves, 0, stream>>>(p);
         return hipGetLastError();
     }

@@ -115,10 +115,28 @@ inline bool stream_k_shape(int64_t M, int64_t K, int64_t N) {
     return M > 0 && N > 0 && K > 0 && !small_batch(M, K, N) && T < 2 * kStreamKGrid && T % kStreamKGrid != 0;
 }
 constexpr int64_t kStreamKSlotBytes = 256 * 256 * 4;
-// the stream-K grid: one workgroup per unit (tile and K stage of 128) at most
-inline int64_t stream_k_grid(int64_t M, int64_t K, int64_t N) {
-    const int64_t units = gemm_tiles(M, N) * ((K + 127) / 128);
-    return units < kStreamKGrid ? units : kStreamKGrid;
+// Workgroups per tile of the stream-K split, by the tile's K stages nk.  A tile's last
+// contributor adds the others' partial sums one contributor after another (dependent round
+// trips through the memory-side cache), so a short K loop is better split over fewer,
+// longer ranges, some compute units left idle.  Measured on whole calls (cold, one box)
+// against the full grid: 2 per tile at nk = 32 (256 x 4096 x 4096: 169 -> 64 us; 112 x
+// 4096 x 8192: 106 -> 63 us), 3 at nk = 64 and 128 (128 x 8192 x 8192: 107 -> 73 us; 128 x
+// 16384 x 8192: 122 -> 97 us), 4 at nk = 224 (128 x 28672 x 8192: 145 -> 131 us).
+inline int64_t stream_k_per_tile(int64_t nk) {
+    if (nk <= 48) return 2;
+    if (nk <= 160) return 3;
+    if (nk <= 320) return 4;
+    return nk / 80 < 8 ? nk / 80 : 8;
+}
+// the stream-K grid: at most kStreamKGrid workgroups (or the compute units, `cus`, if
+// fewer), one per unit (tile and K stage of 128), stream_k_per_tile per tile.  At least
+// 2 per tile or half the tiles, so a workgroup's range meets at most three tiles.
+inline int64_t stream_k_grid(int64_t M, int64_t K, int64_t N, int64_t cus = kStreamKGrid) {
+    const int64_t nk = (K + 127) / 128, T = gemm_tiles(M, N), units = T * nk;
+    int64_t g = cus < kStreamKGrid ? cus : kStreamKGrid;
+    if (units < g) g = units;
+    const int64_t cap = stream_k_per_tile(nk) * T;
+    return cap < g ? cap : g;
 }
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_small(const GemmArgs& a, hipStream_t stream);
