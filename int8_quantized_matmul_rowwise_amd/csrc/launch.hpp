@@ -31,6 +31,32 @@ hipError_t launch_detect(int dt, const void* X, int64_t M, int64_t K, float tau,
 hipError_t launch_compact(int64_t M, int64_t K, const uint32_t* partial, uint32_t* bitmap, int32_t* O,
                           int32_t* n_out, hipStream_t stream, int32_t* zero = nullptr, int64_t n_zero = 0);
 
+// The tiled path's stream-K grid (the small-batch routing below consults it).
+constexpr int64_t kStreamKGrid = 256;
+inline int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256); }
+// Workgroups per tile of the stream-K split, by the tile's K stages nk.  A tile's last
+// contributor adds the others' partial sums one contributor after another (dependent round
+// trips through the memory-side cache), so a short K loop is better split over fewer,
+// longer ranges, some compute units left idle.  Measured on whole calls (cold, one box)
+// against the full grid: 2 per tile at nk = 32 (256 x 4096 x 4096: 169 -> 64 us; 112 x
+// 4096 x 8192: 106 -> 63 us), 3 at nk = 64 and 128 (128 x 8192 x 8192: 107 -> 73 us; 128 x
+// 16384 x 8192: 122 -> 97 us), 4 at nk = 224 (128 x 28672 x 8192: 145 -> 131 us).
+inline int64_t stream_k_per_tile(int64_t nk) {
+    if (nk <= 48) return 2;
+    if (nk <= 160) return 3;
+    if (nk <= 320) return 4;
+    return nk / 80 < 8 ? nk / 80 : 8;
+}
+// the stream-K grid: at most kStreamKGrid workgroups (or the compute units, `cus`, if
+// fewer), one per unit (tile and K stage of 128), stream_k_per_tile per tile.  At least
+// 2 per tile or half the tiles, so a workgroup's range meets at most three tiles.
+inline int64_t stream_k_grid(int64_t M, int64_t K, int64_t N, int64_t cus = kStreamKGrid) {
+    const int64_t nk = (K + 127) / 128, T = gemm_tiles(M, N), units = T * nk;
+    int64_t g = cus < kStreamKGrid ? cus : kStreamKGrid;
+    if (units < g) g = units;
+    const int64_t cap = stream_k_per_tile(nk) * T;
+    return cap < g ? cap : g;
+}
 // Small-batch path (slab X pass, split-N product kernel), for M <= kSmallM and K <= kSmallK
 // where it beats the tiled path.  The split-N kernel streams Wq once at about 5 TB/s, and
 // every row of X adds to that time (its re-reads of Xq from the cache): about 2.2 % per
@@ -47,7 +73,15 @@ inline bool small_batch(int64_t M, int64_t K, int64_t N) {
     if (M > kSmallM || K > kSmallK) return false;
     const int64_t rounds = ((N + 255) / 256 + kRoutingCUs - 1) / kRoutingCUs;
     const int64_t c = M <= 64 ? 22 : 50;  // per mille of the Wq stream time per row
-    return N * (1000 + c * M) < 52500000 * (rounds > 0 ? rounds : 1);
+    if (N * (1000 + c * M) < 52500000 * (rounds > 0 ? rounds : 1)) return true;
+    // Past 64 rows the tiled path runs the stream-K split; on a narrow weight with a short
+    // K loop its grid fills less than half the compute units, and the small-batch path
+    // (which reads its codes in 1 KB blocks from 8 rows up) is faster: whole calls, cold,
+    // N = 8192, M = 112 and 128: K = 4096 43.6 / 46.9 against 65.6 / 58.9 us, K = 8192
+    // 62.8 / 67.6 against 77.5 / 73.5 us; at K = 16384 the tiled path is as fast or faster
+    // (100.7 / 109.4 against 101.2 / 97.4 us), and at N = 16384 (a grid of 128 or more)
+    // faster from M = 96 on.
+    return M > 64 && K <= 8192 && 2 * stream_k_grid(M, K, N) < kStreamKGrid;
 }
 
 struct XPassArgs {
@@ -108,36 +142,11 @@ struct GemmArgs {
 // one workgroup per compute unit) and not a multiple of it, the tiles' K stages are split
 // evenly over the grid.  The workspace then holds one counter per tile and two 256 x 256
 // int32 partial tiles per workgroup.
-constexpr int64_t kStreamKGrid = 256;
-inline int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256); }
 inline bool stream_k_shape(int64_t M, int64_t K, int64_t N) {
     const int64_t T = gemm_tiles(M, N);
     return M > 0 && N > 0 && K > 0 && !small_batch(M, K, N) && T < 2 * kStreamKGrid && T % kStreamKGrid != 0;
 }
 constexpr int64_t kStreamKSlotBytes = 256 * 256 * 4;
-// Workgroups per tile of the stream-K split, by the tile's K stages nk.  A tile's last
-// contributor adds the others' partial sums one contributor after another (dependent round
-// trips through the memory-side cache), so a short K loop is better split over fewer,
-// longer ranges, some compute units left idle.  Measured on whole calls (cold, one box)
-// against the full grid: 2 per tile at nk = 32 (256 x 4096 x 4096: 169 -> 64 us; 112 x
-// 4096 x 8192: 106 -> 63 us), 3 at nk = 64 and 128 (128 x 8192 x 8192: 107 -> 73 us; 128 x
-// 16384 x 8192: 122 -> 97 us), 4 at nk = 224 (128 x 28672 x 8192: 145 -> 131 us).
-inline int64_t stream_k_per_tile(int64_t nk) {
-    if (nk <= 48) return 2;
-    if (nk <= 160) return 3;
-    if (nk <= 320) return 4;
-    return nk / 80 < 8 ? nk / 80 : 8;
-}
-// the stream-K grid: at most kStreamKGrid workgroups (or the compute units, `cus`, if
-// fewer), one per unit (tile and K stage of 128), stream_k_per_tile per tile.  At least
-// 2 per tile or half the tiles, so a workgroup's range meets at most three tiles.
-inline int64_t stream_k_grid(int64_t M, int64_t K, int64_t N, int64_t cus = kStreamKGrid) {
-    const int64_t nk = (K + 127) / 128, T = gemm_tiles(M, N), units = T * nk;
-    int64_t g = cus < kStreamKGrid ? cus : kStreamKGrid;
-    if (units < g) g = units;
-    const int64_t cap = stream_k_per_tile(nk) * T;
-    return cap < g ? cap : g;
-}
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_small(const GemmArgs& a, hipStream_t stream);
 

@@ -71,7 +71,10 @@ def test_ragged_medium(dt):
                                       # the fewest rows that take the blocked copy of the codes (8), through
                                       # the slab launches with K % 64 = 16, and a partial row group (12)
                                       # through the one-workgroup X pass
-                                      (8, 4112, 72, "bf16"), (12, 2048, 40, "fp16")])
+                                      (8, 4112, 72, "bf16"), (12, 2048, 40, "fp16"),
+                                      # 128 rows on the small-batch path only because the stream-K
+                                      # grid of the tiled path would fill under half the chip
+                                      (128, 2064, 7424, "fp16")])
 def test_edge_shapes(M, K, N, dt):
     _banner(f"edge {M}x{K}x{N} {dt}")
     x, w = _case(M, K, N, dt, n_out=2, seed=M + K + N)

@@ -31,6 +31,14 @@ def route(M, K, N, monkeypatch, capfd):
     (300, 1040, 520, "tiled_stream_k"),      # 6 tiles
     (16, 8192, 8192, "small_batch"),
     (64, 2048, 8192, "small_batch"),
+    # past 64 rows: the small-batch path where the stream-K grid would fill under half the
+    # compute units and K <= 8192 (32 tiles, 2 or 3 workgroups each), else stream-K
+    (128, 8192, 8192, "small_batch"),
+    (112, 4096, 8192, "small_batch"),
+    (128, 2064, 7424, "small_batch"),
+    (128, 16384, 8192, "tiled_stream_k"),
+    (96, 4096, 16384, "tiled_stream_k"),
+    (128, 12288, 36864, "tiled_stream_k"),
 ])
 def test_product_kernel_routes(M, K, N, path, monkeypatch, capfd):
     assert route(M, K, N, monkeypatch, capfd) == path
