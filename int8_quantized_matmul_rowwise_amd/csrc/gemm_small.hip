@@ -9,9 +9,10 @@
 // the cache; with 32 columns per workgroup each X operand load feeds two MFMAs, which
 // halves those re-reads (they grow with M).  From 8 rows up they read the blocked copy of
 // Xq that the small-batch X pass writes (xqb_offset), where one operand load is one 1 KB
-// block, eight whole cache lines, instead of halves of 16 lines.  Partial int32 sums are combined exactly
-// through LDS.  Each workgroup gathers the 16-bit outlier operands Wq[n, O[t]] of its own
-// columns, at kernel start so that the scattered loads overlap the weight stream.
+// block, eight whole cache lines, instead of halves of 16 lines.  Partial int32 sums are
+// combined exactly through LDS.  Each workgroup gathers the 16-bit outlier operands
+// Wq[n, O[t]] of its own columns, at kernel start so that the scattered loads overlap the
+// weight stream.
 // "LLM.int8(): 8-bit Matrix Multiplication for Transformers at Scale", abstract.
 #include "common.hpp"
 #include "launch.hpp"
@@ -83,7 +84,8 @@ __device__ __forceinline__ void gather_w_side(const SmallParams& p, int64_t n, i
 // NC) times instead of N / 16).  Batches of PAIRS step pairs per wave, two register sets:
 // the next batch's loads are issued before the current batch's MFMAs, so the weight
 // stream never waits for the arithmetic.  WAVES waves split K; waves g * NC + c (g < MG,
-// c < NC) finish the row group g of column group c: MG * NC <= WAVES.
+// c < NC) finish the row group g of column group c: MG * NC <= WAVES.  The one-group
+// layout (decode shapes) is held to three waves per SIMD (at most 168 registers).
 template <int DT, int MG, int NC, int WAVES, bool ACC_OUT>
 __global__ __launch_bounds__(64 * WAVES, MG == 1 && NC == 1 ? 3 : 1) void gemm_small_kernel(SmallParams p) {
     static_assert(MG * NC <= WAVES, "one finishing wave per row and column group");

@@ -423,7 +423,8 @@ __global__ __launch_bounds__(256) void code_rows_kernel(const uint16_t* __restri
 // chunks' outlier bits ORed into an LDS bitmap), the list O and the per-word ranks (a
 // block scan of the words' popcounts, one word per thread: K <= 32768), the row maxima
 // over the non-outlier columns (per row in LDS, one atomic per wave when the wave's 64
-// chunks lie in one row) and the coding.  The same per-chunk arithmetic as the two-launch
+// chunks lie in one row) and the coding (also into the blocked copy Xqb when it is not
+// NULL).  The same per-chunk arithmetic as the two-launch
 // path, so the results are the same bits.  All indices fit 32 bits (M * K <= 32768).
 constexpr int kOneChunks = 4;
 constexpr int64_t kOneMaxElems = 1024 * kOneChunks * 8;
@@ -560,7 +561,9 @@ __global__ __launch_bounds__(1024) void xpass_one_kernel(const uint16_t* __restr
 //     pattern over its non-outlier columns (pmax);
 //   code_slab (one workgroup per slab and 4 rows, a wave per row): the rows' maxima (max
 //     over the slabs' pmax), the slab's outlier ranks (popcounts of the words before it, a
-//     scan within it), its part of O, n_O (slab 0), then the codes, X_O and the padding.
+//     scan within it), its part of O, n_O (slab 0), then the codes, X_O and the padding,
+//     and (Xqb not NULL, 8 rows or more) the codes again in the product kernel's 1 KB
+//     blocks (xqb_offset), zero from K up to the block edge.
 // Both read X (the second time mostly from the cache); together they replace a detection
 // launch with too few threads to hide its latency and a one-workgroup-per-row coding.
 
