@@ -554,7 +554,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
     // (the verdict travels through the last word of the B slot the segment's last stage
     // freed: the epilogue's staging stops short of it and no load in flight goes there)
     static_assert(4 * kYQuarterBytes + 4 <= kSlotBytesB, "stream-K flag");
-    auto sk_finish = [&](int ti, int sb) -> bool {  // true: this workgroup runs the tile's epilogue
+    auto sk_finish = [&](int ti, int sa, int sb) -> bool {  // true: this workgroup runs the tile's epilogue
         int* sk_flag = (int*)(slot_b(sb) + kSlotBytesB - 4);
         const int t = seg_tile(ti);
         if (seg_k(ti) == 0 && seg_n(ti) == nk) return true;
@@ -602,27 +602,58 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __builtin_amdgcn_s_barrier();  // every wave has the verdict before the slot is reused
         if (!last) return false;
-        // the last contributor: the others' partials (complete before they counted in)
+        // the last contributor: the others' partials (complete before they counted in).  They
+        // come through the two LDS slots the last stage freed (A slot sa, B slot sb; the
+        // verdict above is read, so its word may go): a wave's live pieces of kRows rows of
+        // 32 x 32 blocks are loaded straight into its own region of them with the coherence
+        // bit, all in flight at once (they hold no registers), then read back and added.
+        // Loaded into registers instead, one 16-byte piece was in flight at a time (the
+        // accumulators leave four registers free here): 32 dependent round trips per
+        // partial.  The half-tile mode's four output waves take two rows a round, 16 KB each.
+        constexpr int kRows = HALF ? 2 : 1;
+        constexpr int kRegion = kRows * NJ * 4 * 1024;  // bytes per wave and round
+        constexpr int kPerSlot = kTileBytes / kRegion;    // waves per slot
+        static_assert(kTileBytes == kSlotBytesB && kPerSlot * kRegion == kTileBytes, "exchange regions");
+        int8_t* region = (wu / kPerSlot == 0 ? slot_a(sa) : slot_b(sb)) + (wu % kPerSlot) * kRegion;
+        const bool has_region = wu < 2 * kPerSlot;  // every wave that holds outputs
         const int c0 = sk_owner((int64_t)t * nk), c1 = sk_owner((int64_t)(t + 1) * nk - 1);
         for (int c = c0; c <= c1; ++c) {
             if (c == bid) continue;
             const __amdgpu_buffer_rsrc_t rs = slot_rsrc(c);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+            for (int i0 = 0; i0 < 4; i0 += kRows) {
+                if (has_region) {
 #pragma unroll
-                for (int j = 0; j < NJ; ++j)
-                    if (block_live(i, j))
+                    for (int di = 0; di < kRows; ++di)
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const v4i v = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, lane_off, piece(i, j, q), kCoherent));
+                        for (int j = 0; j < NJ; ++j)
+                            if (block_live(i0 + di, j))
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[e];
-                        }
-                // one row of blocks in flight at a time: the loads are not hoisted over the
-                // adds of the row before (that would hold 128 loaded vectors)
-                asm volatile("" ::: "memory");
+                                for (int q = 0; q < 4; ++q)
+                                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                                        rs, (lds_ptr_t)(region + ((di * NJ + j) * 4 + q) * 1024), 16, (int)lane_off,
+                                        (int)piece(i0 + di, j, q), 0, kCoherent);
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+                    for (int di = 0; di < kRows; ++di)
+#pragma unroll
+                        for (int j = 0; j < NJ; ++j)
+                            if (block_live(i0 + di, j))
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) {
+                                    const v4i v = *(const v4i*)(region + ((di * NJ + j) * 4 + q) * 1024 + 16 * lane);
+#pragma unroll
+                                    for (int e = 0; e < 4; ++e) acc[i0 + di][j][4 * q + e] += v[e];
+                                }
+                    // this wave's reads are done before its region is loaded again
+                    __builtin_amdgcn_s_waitcnt(0xC07F);
+                }
             }
         }
+        // every wave is done with the regions before the slots are written again (the
+        // epilogue's factor table and staging)
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
         return true;
     };
 
@@ -657,7 +688,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
                 }
                 idle_stage(sa, sb, len - 1, ti, std::true_type{});
                 bool fin = true;
-                if constexpr (SK) fin = sk_finish(ti, sb);
+                if constexpr (SK) fin = sk_finish(ti, sa, sb);
                 if (fin) {
                     float* rsc = (float*)slot_a(sa);
                     rsc[tid] = sc / 127.0f;
@@ -695,7 +726,7 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
         }
         stage(sa, sb, len - 1, ti, std::true_type{});
         if constexpr (SK) {
-            if (sk_finish(ti, sb)) epilogue(ti, sa, sb);
+            if (sk_finish(ti, sa, sb)) epilogue(ti, sa, sb);
         } else {
             epilogue(ti, sa, sb);
         }
