@@ -74,14 +74,14 @@ inline bool small_batch(int64_t M, int64_t K, int64_t N) {
     const int64_t rounds = ((N + 255) / 256 + kRoutingCUs - 1) / kRoutingCUs;
     const int64_t c = M <= 64 ? 22 : 50;  // per mille of the Wq stream time per row
     if (N * (1000 + c * M) < 52500000 * (rounds > 0 ? rounds : 1)) return true;
-    // Past 64 rows the tiled path runs the stream-K split; on a narrow weight with a short
-    // K loop its grid fills less than half the compute units, and the small-batch path
-    // (which reads its codes in 1 KB blocks from 8 rows up) is faster: whole calls, cold,
-    // N = 8192, M = 112 and 128: K = 4096 43.6 / 46.9 against 65.6 / 58.9 us, K = 8192
-    // 62.8 / 67.6 against 77.5 / 73.5 us; at K = 16384 the tiled path is as fast or faster
-    // (100.7 / 109.4 against 101.2 / 97.4 us), and at N = 16384 (a grid of 128 or more)
-    // faster from M = 96 on.
-    return M > 64 && K <= 8192 && 2 * stream_k_grid(M, K, N) < kStreamKGrid;
+    // Past 64 rows the tiled path runs the stream-K split; on a narrow weight its grid fills
+    // less than half the compute units, and while X is small (under 2^20 elements: every
+    // workgroup of the small-batch path re-reads all its codes) the small-batch path is
+    // faster.  Whole calls, cold, interleaved on one box, small against tiled, N = 8192:
+    // 112 x 4096 43.8 / 60.6 us, 128 x 4096 46.8 / 53.0, 112 x 8192 62.6 / 67.8, but
+    // 128 x 8192 67.6 / 62.3 (tiled); 128 x 2064 x 7424 34.8 / 48.7; at K = 16384, or at
+    // N = 16384 (a grid of 128 or more), the tiled path is as fast or faster.
+    return M > 64 && M * K < (int64_t)1 << 20 && 2 * stream_k_grid(M, K, N) < kStreamKGrid;
 }
 
 struct XPassArgs {

@@ -32,8 +32,10 @@ def route(M, K, N, monkeypatch, capfd):
     (16, 8192, 8192, "small_batch"),
     (64, 2048, 8192, "small_batch"),
     # past 64 rows: the small-batch path where the stream-K grid would fill under half the
-    # compute units and K <= 8192 (32 tiles, 2 or 3 workgroups each), else stream-K
-    (128, 8192, 8192, "small_batch"),
+    # compute units and X has under 2^20 elements (32 tiles, 2 or 3 workgroups each), else
+    # stream-K
+    (112, 8192, 8192, "small_batch"),
+    (128, 8192, 8192, "tiled_stream_k"),
     (112, 4096, 8192, "small_batch"),
     (128, 2064, 7424, "small_batch"),
     (128, 16384, 8192, "tiled_stream_k"),
