@@ -35,17 +35,17 @@ hipError_t launch_compact(int64_t M, int64_t K, const uint32_t* partial, uint32_
 constexpr int64_t kStreamKGrid = 256;
 inline int64_t gemm_tiles(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256); }
 // Workgroups per tile of the stream-K split, by the tile's K stages nk.  A tile's last
-// contributor adds the others' partial sums one contributor after another (dependent round
-// trips through the memory-side cache), so a short K loop is better split over fewer,
-// longer ranges, some compute units left idle.  Measured on whole calls (cold, one box)
-// against the full grid: 2 per tile at nk = 32 (256 x 4096 x 4096: 169 -> 64 us; 112 x
-// 4096 x 8192: 106 -> 63 us), 3 at nk = 64 and 128 (128 x 8192 x 8192: 107 -> 73 us; 128 x
-// 16384 x 8192: 122 -> 97 us), 4 at nk = 224 (128 x 28672 x 8192: 145 -> 131 us).
+// contributor loads and adds the others' partial sums, so a short K loop is better split
+// over fewer, longer ranges, some compute units left idle.  Measured on whole calls (cold,
+// interleaved on one box) with caps of 2, 3, 4, 6 and 8 against the full grid: nk = 32
+// takes 2 (256 x 4096 x 4096: 166 us with the full grid, 60 us; 3 is within 2 us either
+// way), nk = 64 takes 3 (4 was 11 us slower on 512 x 8192 x 8192), and longer loops 6
+// (128 x 16384 x 8192: 86.3 -> 83.0 us against 3; 256 x 28672 x 8192: 130.9 -> 124.8 us,
+// 384 x 16384 x 4096: 98.7 -> 88.0 us against 4).
 inline int64_t stream_k_per_tile(int64_t nk) {
     if (nk <= 48) return 2;
-    if (nk <= 160) return 3;
-    if (nk <= 320) return 4;
-    return nk / 80 < 8 ? nk / 80 : 8;
+    if (nk <= 96) return 3;
+    return 6;
 }
 // the stream-K grid: at most kStreamKGrid workgroups (or the compute units, `cus`, if
 // fewer), one per unit (tile and K stage of 128), stream_k_per_tile per tile.  At least
