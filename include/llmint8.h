@@ -162,8 +162,9 @@ int int8_matmul_products(int64_t M, int64_t K, int dtype, const int8_t* Wq, cons
  *   wo        dtype [N][xo_pitch]   Wq[:, O] cast to dtype (same padding); written only by
  *                                   the tiled path -- the small-batch product kernel
  *                                   gathers these values itself
- *   scratch   internal (outlier flags; for small batches also per-row partial maxima and,
- *             from 8 rows up, a copy of Xq in the product kernel's operand blocks)
+ *   scratch   internal (outlier flags; up to 112 rows, and for small batches, per-row
+ *             partial maxima; for small batches from 8 rows up, a copy of Xq in the
+ *             product kernel's operand blocks)
  *   total     bytes (int8_matmul_workspace_bytes)
  *   small_batch  1 when these sizes take the small-batch path (M <= 128, K <= 65536 and
  *             N small enough that streaming Wq once beats the tiled kernel), else 0 */

@@ -74,8 +74,8 @@ Layout make_layout(int64_t M, int64_t K, int64_t N) {
     off = align_up(off + 4 * kw);
     L.partial = off;
     off = align_up(off + 4 * kw * (size_t)detect_row_blocks(M));
-    L.pmax = off;  // small batches: per row and 512-column slab, the slab's row maximum
-    off = align_up(off + (small_batch(M, K, N) ? 4 * m * (size_t)ceil_div(K, 512) : 0));
+    L.pmax = off;  // the slab X pass: per row and 512-column slab, the slab's row maximum
+    off = align_up(off + (small_batch(M, K, N) || slab_xpass(M, K) ? 4 * m * (size_t)ceil_div(K, 512) : 0));
     L.xqb = off;  // small batches of 8 rows or more: Xq again, in the product kernel's 1 KB blocks
     const bool blocked = small_batch(M, K, N) && small_blocked_codes(M);
     off = align_up(off + (blocked ? (size_t)round_up(M, 16) * (size_t)ceil_div(K, 64) * 64 : 0));
@@ -142,7 +142,7 @@ int run_xpass(const void* X, int64_t M, int64_t K, int dtype, float tau, const i
     uint32_t* bitmap = (uint32_t*)(ws + L.bitmap);
     int32_t* O = (int32_t*)(ws + L.outliers);
     int32_t* nO = (int32_t*)(ws + L.n_outliers);
-    XPassArgs a;
+    XPassArgs a{};
     a.dt = dtype;
     a.X = X;
     a.tau = tau;
@@ -156,11 +156,21 @@ int run_xpass(const void* X, int64_t M, int64_t K, int dtype, float tau, const i
     a.xo_pitch = (int64_t)L.xo_pitch;
     if (small_batch(M, K, N)) {
         a.Xqb = small_blocked_codes(M) ? ws + L.xqb : nullptr;
-        return hip_status(stage("xpass_small", [&] { return launch_xpass_small(a, O, nO, bitmap, (uint32_t*)(ws + L.pmax), st); }));
+        return hip_status(stage("xpass_small", [&] {
+            return launch_xpass_small(a, O, nO, bitmap, (uint32_t*)(ws + L.pmax), false, nullptr, 0, st);
+        }));
     }
     a.Xqb = nullptr;
     int32_t* sk_cnt = L.sk ? (int32_t*)(ws + L.sk_cnt) : nullptr;  // zeroed for the product kernel
     const int64_t n_tiles = gemm_tiles(M, N);
+    if (slab_xpass(M, K)) {
+        a.Wq = Wq;
+        a.WO = ws + L.wo;
+        return hip_status(stage("xpass_small", [&] {
+            return launch_xpass_small(a, O, nO, bitmap, (uint32_t*)(ws + L.pmax), Wq != nullptr, sk_cnt,
+                                      sk_cnt ? n_tiles : 0, st);
+        }));
+    }
     hipError_t e = stage("detect", [&] { return launch_detect(dtype, X, M, K, tau, partial, st); });
     if (e == hipSuccess)
         e = stage("compact", [&] { return launch_compact(M, K, partial, bitmap, O, nO, st, sk_cnt, n_tiles); });
@@ -272,7 +282,7 @@ int run_xpass_fixed(const void* X, int64_t M, int64_t K, int64_t N, int dtype, c
     if (e == hipSuccess)
         e = stage("compact", [&] { return launch_compact(1, K, partial, bitmap, O, n_out, st, sk_cnt, n_tiles); });
     if (e == hipSuccess) {
-        XPassArgs a;
+        XPassArgs a{};
         a.dt = dtype;
         a.X = X;
         a.tau = 0.0f;

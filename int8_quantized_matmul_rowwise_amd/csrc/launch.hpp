@@ -108,9 +108,20 @@ hipError_t launch_code_rows(const XPassArgs& a, const uint32_t* bitmap, int32_t*
 // M = 1 every lane reads the same row), and the extra writes cost more than they save.
 inline bool small_blocked_codes(int64_t M) { return M >= 8; }
 // pmax (M x ceil(K/512) words of scratch): per row and 512-column slab, the slab's
-// maximum over its non-outlier columns
+// maximum over its non-outlier columns.  with_wo: the tiled product follows, so the coding
+// launch also gathers W_O (a.Wq, a.N into a.WO) and zeroes zero[0, n_zero) (the stream-K
+// tile counters); the one-workgroup form is not taken then.
 hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, uint32_t* bitmap, uint32_t* pmax,
-                              hipStream_t stream);
+                              bool with_wo, int32_t* zero, int64_t n_zero, hipStream_t stream);
+// The slab X pass also serves the tiled path for few rows (it needs every row of a slab in
+// one workgroup), where the detection and the row coding leave most of the device idle.
+// Whole steps, cold, interleaved on one box, row path against slab pass: 12288 x 36864 at
+// 24, 32, 48, 80, 96 and 112 rows 127.6 / 124.4, 128.5 / 124.2, 136.6 / 131.1, 141.9 /
+// 138.9, 142.6 / 139.5 and 149.5 / 145.8 us; 4096 x 16384 at 80, 96 and 112 rows 59.3 /
+// 57.4, 60.5 / 58.0 and 62.7 / 59.4 us; 28672 x 8192 at 112 rows 120.0 / 117.2 us.  At 128
+// rows the row path was 1.6 to 2.5 us faster on all three weights.
+constexpr int64_t kSlabXPassM = 112;
+inline bool slab_xpass(int64_t M, int64_t K) { return M > 0 && M <= kSlabXPassM && K <= kSmallK; }
 
 // ---- products + epilogue
 struct GemmArgs {

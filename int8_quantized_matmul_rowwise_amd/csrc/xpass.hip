@@ -250,10 +250,87 @@ __device__ __forceinline__ u32x2 code_chunk(const u32x4& x, uint32_t o, float in
     return q;
 }
 
-// Code the rows.  The first n_wo workgroups gather WO[n,t] = (dtype) Wq[n, O[t]] (exact;
-// zero up to the next multiple of 32), 64 rows of Wq each, from the O written by the
-// compaction; they come first so that their scattered loads overlap the row work instead
-// of trailing it.  The other `groups` workgroups each take rows g, g + groups, ...: for
+// The set-up shared by the row coding and the W_O gather (a block of 256 threads): the
+// bitmap's Kw words in bits[] and, per word, the number of outlier columns before it in
+// wrank[] (both LDS; a block-wide scan of popcounts).  Returns the number of outlier
+// columns.
+__device__ __forceinline__ int32_t bitmap_ranks(const uint32_t* __restrict__ bitmap, int64_t Kw, uint32_t* bits,
+                                                int32_t* wrank, int32_t* wsum) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    for (int64_t w = tid; w < Kw; w += 256) bits[w] = bitmap[w];
+    __syncthreads();
+    // thread tid takes words [tid*wpt, (tid+1)*wpt); its first rank is the exclusive prefix
+    // of the popcounts before them
+    const int64_t wpt = ceil_div(Kw, 256);
+    int32_t cnt = 0;
+    for (int64_t w = tid * wpt; w < (tid + 1) * wpt && w < Kw; ++w) cnt += __popc(bits[w]);
+    int32_t incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t t = __shfl_up(incl, off, kWave);
+        if (lane >= off) incl += t;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int32_t pos = incl - cnt, total = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        pos += q < wv ? wsum[q] : 0;
+        total += wsum[q];
+    }
+    for (int64_t w = tid * wpt; w < (tid + 1) * wpt && w < Kw; ++w) {
+        wrank[w] = pos;
+        pos += __popc(bits[w]);
+    }
+    __syncthreads();
+    return total;
+}
+
+// The column of outlier rank t < total from that set-up: the last word whose rank is at
+// most t holds it (empty words after it have larger ranks), as its (t - rank)-th set bit.
+__device__ __forceinline__ int64_t outlier_column(int32_t t, int64_t Kw, const uint32_t* bits, const int32_t* wrank) {
+    int64_t lo = 0, hi = Kw - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (wrank[mid] <= t) lo = mid;
+        else hi = mid - 1;
+    }
+    uint32_t b = bits[lo];
+    for (int32_t k = t - wrank[lo]; k > 0; --k) b &= b - 1;
+    return 32 * lo + __ffs(b) - 1;
+}
+
+// WO[n,t] = (dtype) Wq[n, O[t]] (exact; zero up to the next multiple of 32) for the 64 rows
+// of Wq from n0, with O[t] = col_of(t) for t < nO: thread: column t0 + tid%32 of W_O, rows
+// tid/32 + 8k; one column lookup, 8 independent Wq loads.
+template <int DT, class ColOf>
+__device__ __forceinline__ void gather_wo_rows(int64_t n0, int64_t K, int32_t nO, ColOf col_of,
+                                               const int8_t* __restrict__ Wq, int64_t N, uint16_t* __restrict__ WO,
+                                               int64_t xo_pitch) {
+    const int tid = threadIdx.x;
+    const int32_t P = (nO + 31) & ~31;
+    const int rr = tid >> 5;
+    for (int32_t t0 = 0; t0 < P; t0 += 32) {
+        const int32_t t = t0 + (tid & 31);
+        const int64_t col = t < nO ? col_of(t) : -1;
+        uint16_t v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t n = n0 + rr + 8 * k;
+            v[k] = (col >= 0 && n < N) ? from_f32<DT>((float)Wq[n * K + col]) : (uint16_t)0;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t n = n0 + rr + 8 * k;
+            if (n < N) WO[n * xo_pitch + t] = v[k];
+        }
+    }
+}
+
+// Code the rows.  The first n_wo workgroups gather W_O (gather_wo_rows), 64 rows of Wq
+// each, from the O written by the compaction; they come first so that their scattered
+// loads overlap the row work instead of trailing it.  The other `groups` workgroups each
+// take rows g, g + groups, ...: for
 // row i, s_x[i] = max over the non-outlier columns of |X[i,j]|; Xq[i,j] = 0 for j in O,
 // else the vector-wise code; Xq[i, K..pitch) = 0; XO[i,t] = X[i, O[t]] for t < n_O, 0 up
 // to the next multiple of 32.  Set-up once per workgroup: the bitmap in LDS and, per
@@ -272,26 +349,8 @@ __global__ __launch_bounds__(256) void code_rows_kernel(const uint16_t* __restri
                                                         uint16_t* __restrict__ WO, int64_t n_wo, int64_t groups) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     if ((int64_t)blockIdx.x < n_wo) {
-        // thread: column t0 + tid%32 of W_O, rows tid/32 + 8k; one O load, 8 independent Wq loads
-        const int32_t nO = *n_out;
-        const int32_t P = (nO + 31) & ~31;
-        const int64_t n0 = (int64_t)blockIdx.x * 64;
-        const int rr = tid >> 5;
-        for (int32_t t0 = 0; t0 < P; t0 += 32) {
-            const int32_t t = t0 + (tid & 31);
-            const int64_t col = t < nO ? O[t] : -1;
-            uint16_t v[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int64_t n = n0 + rr + 8 * k;
-                v[k] = (col >= 0 && n < N) ? from_f32<DT>((float)Wq[n * K + col]) : (uint16_t)0;
-            }
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int64_t n = n0 + rr + 8 * k;
-                if (n < N) WO[n * xo_pitch + t] = v[k];
-            }
-        }
+        gather_wo_rows<DT>((int64_t)blockIdx.x * 64, K, *n_out, [&](int32_t t) { return (int64_t)O[t]; }, Wq, N, WO,
+                           xo_pitch);
         return;
     }
     // dynamic LDS, sized to K: the bitmap, then the outlier count before each word
@@ -320,32 +379,7 @@ __global__ __launch_bounds__(256) void code_rows_kernel(const uint16_t* __restri
     };
     if constexpr (HOLD > 0) load_row(va, g);  // in flight during the set-up
 
-    for (int64_t w = tid; w < Kw; w += 256) bits[w] = bitmap[w];
-    __syncthreads();
-    // thread tid takes words [tid*wpt, (tid+1)*wpt); its first rank is the exclusive prefix
-    // of the popcounts before them
-    const int64_t wpt = ceil_div(Kw, 256);
-    int32_t cnt = 0;
-    for (int64_t w = tid * wpt; w < (tid + 1) * wpt && w < Kw; ++w) cnt += __popc(bits[w]);
-    int32_t incl = cnt;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int32_t t = __shfl_up(incl, off, kWave);
-        if (lane >= off) incl += t;
-    }
-    if (lane == 63) wsum[wv] = incl;
-    __syncthreads();
-    int32_t pos = incl - cnt, total = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        pos += q < wv ? wsum[q] : 0;
-        total += wsum[q];
-    }
-    for (int64_t w = tid * wpt; w < (tid + 1) * wpt && w < Kw; ++w) {
-        wrank[w] = pos;
-        pos += __popc(bits[w]);
-    }
-    __syncthreads();
+    const int32_t total = bitmap_ranks(bitmap, Kw, bits, wrank, wsum);
     const int32_t P = (total + 31) & ~31;
 
     auto obits = [&](int64_t c) { return (bits[c >> 2] >> (8 * (c & 3))) & 0xffu; };
@@ -630,14 +664,33 @@ __global__ __launch_bounds__(256) void code_slab_kernel(const uint16_t* __restri
                                                         int8_t* __restrict__ Xq, int64_t xq_pitch,
                                                         int8_t* __restrict__ Xqb, int64_t nsteps,
                                                         float* __restrict__ s_x, uint16_t* __restrict__ XO,
-                                                        int64_t xo_pitch) {
+                                                        int64_t xo_pitch, const int8_t* __restrict__ Wq, int64_t N,
+                                                        uint16_t* __restrict__ WO, int64_t ny_wo,
+                                                        int32_t* __restrict__ zero, int64_t n_zero) {
     __shared__ float inv_s[4];
     __shared__ int32_t wr[16];
     __shared__ uint32_t wb[16];
     __shared__ int32_t tot;
     const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int64_t sl = blockIdx.x, C = K / 8, Cp = xq_pitch / 8, Kw = ceil_div(K, 32);
-    const int64_t c = sl * 64 + lane, r = (int64_t)blockIdx.y * 4 + w;  // this thread's chunk and row
+    if ((int64_t)blockIdx.y < ny_wo) {
+        // the W_O gather (tiled product): 64 rows of Wq per workgroup, O[t] found from the
+        // bitmap (the coding workgroups write O meanwhile); workgroup 0 zeroes the counters
+        extern __shared__ uint32_t dyn_lds[];
+        __shared__ int32_t wsum[4];
+        const int64_t b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+        if (b == 0)
+            for (int64_t i = tid; i < n_zero; i += 256) zero[i] = 0;
+        if (b * 64 >= N) return;
+        uint32_t* bits = dyn_lds;
+        int32_t* wrank = (int32_t*)(dyn_lds + Kw);
+        const int32_t nO = bitmap_ranks(bitmap, Kw, bits, wrank, wsum);
+        gather_wo_rows<DT>(b * 64, K, nO, [&](int32_t t) { return outlier_column(t, Kw, bits, wrank); }, Wq, N, WO,
+                           xo_pitch);
+        return;
+    }
+    const int64_t ry = (int64_t)blockIdx.y - ny_wo;  // this workgroup's group of 4 rows
+    const int64_t c = sl * 64 + lane, r = ry * 4 + w;  // this thread's chunk and row
     const bool live = c < C, row = r < M;
     // every load first (rows past M, slabs past nslab and chunks past K read 0): the chunk,
     // row r's slab partials (nslab <= 64 kParts), and in wave 0 the bitmap (Kw <= 64 kWords)
@@ -695,14 +748,14 @@ __global__ __launch_bounds__(256) void code_slab_kernel(const uint16_t* __restri
         if (lane < 16) {
             wr[lane] = before + incl - cnt;
             wb[lane] = wd;
-            if (blockIdx.y == 0) {
+            if (ry == 0) {
                 int32_t t = before + incl - cnt;
                 for (uint32_t b = wd; b; b &= b - 1) O[t++] = (int32_t)(32 * wi + __ffs(b) - 1);
             }
         }
         if (lane == 0) {
             tot = all;
-            if (sl == 0 && blockIdx.y == 0) *n_out = all;
+            if (sl == 0 && ry == 0) *n_out = all;
         }
     }
     __syncthreads();
@@ -777,10 +830,10 @@ hipError_t launch_code_rows(const XPassArgs& a, const uint32_t* bitmap, int32_t*
 // slab detection and the slab coding.  K = 0 takes the coding launch alone (one slab
 // workgroup per 4 rows), which writes s_x = 0 and n_O = 0.
 hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, uint32_t* bitmap, uint32_t* pmax,
-                              hipStream_t stream) {
+                              bool with_wo, int32_t* zero, int64_t n_zero, hipStream_t stream) {
     const uint16_t* x = (const uint16_t*)a.X;
     const int64_t nsteps = ceil_div(a.K, 64);  // blocks per row group of the blocked copy
-    if (a.K > 0 && a.M * a.K <= kOneMaxElems) {
+    if (!with_wo && a.K > 0 && a.M * a.K <= kOneMaxElems) {
         if (a.dt == F16)
             xpass_one_kernel<F16><<<1, 1024, 0, stream>>>(x, (int)a.M, (int)a.K, a.tau, bitmap, O, n_out, a.Xq,
                                                           (int)a.xq_pitch, a.Xqb, (int)nsteps, a.s_x,
@@ -808,14 +861,20 @@ hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, ui
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t gx = ceil_div(a.xq_pitch / 8, 64);
-    const dim3 g2((unsigned)(gx > 0 ? gx : 1), (unsigned)ceil_div(a.M, 4));
+    int64_t gx = ceil_div(a.xq_pitch / 8, 64);
+    gx = gx > 0 ? gx : 1;
+    // with_wo: rows of gather workgroups first (enough for ceil(N/64)), then the coding
+    const int64_t ny_wo = with_wo ? ceil_div(ceil_div(a.N, 64), gx) : 0;
+    const size_t lds = with_wo ? (size_t)ceil_div(a.K, 32) * 8 : 0;
+    const dim3 g2((unsigned)gx, (unsigned)(ny_wo + ceil_div(a.M, 4)));
     if (a.dt == F16)
-        code_slab_kernel<F16><<<g2, 256, 0, stream>>>(x, a.M, a.K, bitmap, pmax, nslab, O, n_out, a.Xq, a.xq_pitch,
-                                                      a.Xqb, nsteps, a.s_x, (uint16_t*)a.XO, a.xo_pitch);
+        code_slab_kernel<F16><<<g2, 256, lds, stream>>>(x, a.M, a.K, bitmap, pmax, nslab, O, n_out, a.Xq, a.xq_pitch,
+                                                        a.Xqb, nsteps, a.s_x, (uint16_t*)a.XO, a.xo_pitch, a.Wq, a.N,
+                                                        (uint16_t*)a.WO, ny_wo, zero, n_zero);
     else
-        code_slab_kernel<BF16><<<g2, 256, 0, stream>>>(x, a.M, a.K, bitmap, pmax, nslab, O, n_out, a.Xq, a.xq_pitch,
-                                                       a.Xqb, nsteps, a.s_x, (uint16_t*)a.XO, a.xo_pitch);
+        code_slab_kernel<BF16><<<g2, 256, lds, stream>>>(x, a.M, a.K, bitmap, pmax, nslab, O, n_out, a.Xq, a.xq_pitch,
+                                                         a.Xqb, nsteps, a.s_x, (uint16_t*)a.XO, a.xo_pitch, a.Wq, a.N,
+                                                         (uint16_t*)a.WO, ny_wo, zero, n_zero);
     return hipGetLastError();
 }
 

@@ -26,6 +26,8 @@ def _calls():
                          ["detect", "compact", "code_rows", "gemm"]),
         "matmul_small": (lambda: lib.int8_matmul(X, 16, 1024, 1, WQ, SW, 520, 6.0, Y, WS, BIG, None),
                          ["xpass_small", "gemm_small"]),
+        "matmul_mid": (lambda: lib.int8_matmul(X, 64, 1024, 0, WQ, SW, 65536, 6.0, Y, WS, BIG, None),
+                       ["xpass_small", "gemm"]),
         "matmul_long_rows": (lambda: lib.int8_matmul(X, 8192, 28672, 1, WQ, SW, 8192, 6.0, 8192 * MB, 4096 * MB,
                                                      BIG, None), ["detect", "compact", "code_rows", "gemm"]),
         "accumulators": (lambda: lib.int8_matmul_accumulators(X, 300, 1024, 0, WQ, 520, 6.0, Y, WO, WS, BIG, None),

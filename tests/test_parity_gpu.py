@@ -74,11 +74,29 @@ def test_ragged_medium(dt):
                                       (8, 4112, 72, "bf16"), (12, 2048, 40, "fp16"),
                                       # 128 rows on the small-batch path only because the stream-K
                                       # grid of the tiled path would fill under half the chip
-                                      (128, 2064, 7424, "fp16")])
+                                      (128, 2064, 7424, "fp16"),
+                                      # up to 128 rows on the tiled path: stream-K ragged in M, N and K;
+                                      # 256 tiles (no stream-K); stream-K over 64 tiles with the row
+                                      # coding (past 112 rows)
+                                      (100, 2064, 20000, "bf16"), (16, 2048, 65536, "fp16"),
+                                      (128, 1040, 16384, "bf16")])
 def test_edge_shapes(M, K, N, dt):
     _banner(f"edge {M}x{K}x{N} {dt}")
     x, w = _case(M, K, N, dt, n_out=2, seed=M + K + N)
     parity.run_case(x, w, 6.0)
+
+
+@pytest.mark.parametrize("M,K,N,n_out,dt", [(96, 2048, 20000, 40, "bf16"), (64, 1024, 65536, 300, "fp16"),
+                                             (112, 4112, 16400, 64, "fp16")])
+def test_mid_batches_tiled_many_outliers(M, K, N, n_out, dt):
+    # up to 112 rows on the tiled path (the slab X pass) with many outlier columns: the W_O
+    # gather looks each column up by its rank in the bitmap (several per bitmap word, up to
+    # ten rounds of 32)
+    _banner(f"mid tiled {M}x{K}x{N} {dt}, {n_out} outlier columns")
+    assert not lm.int8_matmul_workspace_layout(M, K, N)["small_batch"]
+    x, w = _case(M, K, N, dt, n_out=n_out, seed=M + N)
+    st = parity.run_case(x, w, 6.0)
+    assert st["n_outliers"] >= n_out
 
 
 @pytest.mark.parametrize("K,dt", [(128, "fp16"), (256, "bf16"), (400, "fp16"), (336, "bf16")])
@@ -106,6 +124,14 @@ def test_k_zero_on_the_tiled_path():
     C, F, _ = lm.int8_matmul_accumulators(X, Wq, 6.0)
     torch.cuda.synchronize()
     assert not Y.view(torch.int16).any() and not C.any() and not F.view(torch.int32).any()
+    # 64 rows, N wide enough for the tiled kernel
+    _banner("K=0, M=64, N=65536")
+    X = torch.zeros(64, 0, dtype=torch.bfloat16, device="cuda")
+    Wq = torch.zeros(65536, 0, dtype=torch.int8, device="cuda")
+    s_w = torch.zeros(65536, device="cuda")
+    Y = lm.int8_matmul(X, Wq, s_w, 6.0, Y=torch.full((64, 65536), 5.0, dtype=torch.bfloat16, device="cuda"))
+    torch.cuda.synchronize()
+    assert not Y.view(torch.int16).any()
 
 
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
