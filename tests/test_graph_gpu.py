@@ -19,7 +19,10 @@ def _inputs(M, K, N, dt, seed):
 
 
 @pytest.mark.parametrize("M,K,N,dt", [(300, 1040, 520, "fp16"), (16, 2048, 264, "bf16"),
-                                      (300, 4096, 264, "fp16")])
+                                      (300, 4096, 264, "fp16"),
+                                      # tiled stream-K after the slab X pass, whose coding launch
+                                      # zeroes the tile counters and gathers W_O
+                                      (64, 1024, 36864, "bf16")])
 def test_vectorwise_call_replays_from_a_graph(M, K, N, dt):
     print(f"\n[case] graph int8_matmul {dt} {M}x{K}x{N}", flush=True)
     X, W = _inputs(M, K, N, dt, seed=M)
