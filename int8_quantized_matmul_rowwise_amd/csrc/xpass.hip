@@ -597,7 +597,8 @@ __global__ __launch_bounds__(1024) void xpass_one_kernel(const uint16_t* __restr
 //     over the slabs' pmax), the slab's outlier ranks (popcounts of the words before it, a
 //     scan within it), its part of O, n_O (slab 0), then the codes, X_O and the padding,
 //     and (Xqb not NULL, 8 rows or more) the codes again in the product kernel's 1 KB
-//     blocks (xqb_offset), zero from K up to the block edge.
+//     blocks (xqb_offset), zero from K up to the block edge.  When the tiled product kernel
+//     follows (up to 112 rows), rows of W_O gather workgroups come first in this launch.
 // Both read X (the second time mostly from the cache); together they replace a detection
 // launch with too few threads to hide its latency and a one-workgroup-per-row coding.
 
