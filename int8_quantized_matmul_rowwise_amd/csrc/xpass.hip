@@ -787,7 +787,7 @@ template <int DT, int HOLD>
 static hipError_t code_rows_launch1(const XPassArgs& a, const uint32_t* bitmap, int32_t* O, int32_t* n_out,
                                     int64_t n_wo, hipStream_t stream) {
     // persistent row workgroups: as many as fit on the device at once (at most M).  Rows of
-    // more than 16384 elements (HOLD 16) take one workgroup each instead, which measured
+    // more than 16384 elements (HOLD 12 or 16) take one workgroup each instead, which measured
     // faster at every batch tried (K = 28672: 246 -> 237 us at M = 8192, 136 -> 132 us at
     // M = 4096), while at K = 12288 the persistent form stays about 1 us ahead.
     const size_t lds = (size_t)ceil_div(a.K, 32) * 8;
@@ -797,7 +797,7 @@ static hipError_t code_rows_launch1(const XPassArgs& a, const uint32_t* bitmap, 
     if (e == hipSuccess)
         e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, code_rows_kernel<DT, HOLD>, 256, lds);
     if (e != hipSuccess) return e;
-    int64_t groups = HOLD == 16 ? a.M : (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    int64_t groups = HOLD > 8 ? a.M : (int64_t)cus * (per_cu > 0 ? per_cu : 1);
     groups = groups < a.M ? groups : a.M;
     const unsigned grid = (unsigned)(n_wo + groups);
     if (grid == 0) return hipSuccess;
@@ -808,12 +808,18 @@ static hipError_t code_rows_launch1(const XPassArgs& a, const uint32_t* bitmap, 
 }
 
 // The register hold is sized to the row (16-byte chunks per thread of 256): fewer
-// registers per thread leave room for more workgroups per CU.
+// registers per thread leave room for more workgroups per CU.  Holds of 6 chunks for rows
+// of 12288 elements (74 registers, six workgroups per CU, against 84 and five with 8) and
+// of 2 for 4096: X pass 62.0 -> 58.9 us on 4096 x 12288, 23.2 -> 22.3 us on 2048 x 4096
+// (cold, interleaved on one box, three rounds).
 template <int DT>
 static hipError_t code_rows_launch(const XPassArgs& a, const uint32_t* bitmap, int32_t* O, int32_t* n_out,
                                    int64_t n_wo, hipStream_t stream) {
+    if (a.K <= 2048 * 2) return code_rows_launch1<DT, 2>(a, bitmap, O, n_out, n_wo, stream);
     if (a.K <= 2048 * 4) return code_rows_launch1<DT, 4>(a, bitmap, O, n_out, n_wo, stream);
+    if (a.K <= 2048 * 6) return code_rows_launch1<DT, 6>(a, bitmap, O, n_out, n_wo, stream);
     if (a.K <= 2048 * 8) return code_rows_launch1<DT, 8>(a, bitmap, O, n_out, n_wo, stream);
+    if (a.K <= 2048 * 12) return code_rows_launch1<DT, 12>(a, bitmap, O, n_out, n_wo, stream);
     if (a.K <= 2048 * 16) return code_rows_launch1<DT, 16>(a, bitmap, O, n_out, n_wo, stream);
     return code_rows_launch1<DT, 0>(a, bitmap, O, n_out, n_wo, stream);
 }

@@ -79,7 +79,9 @@ def test_ragged_medium(dt):
                                       # 256 tiles (no stream-K); stream-K over 64 tiles with the row
                                       # coding (past 112 rows)
                                       (100, 2064, 20000, "bf16"), (16, 2048, 65536, "fp16"),
-                                      (128, 1040, 16384, "bf16")])
+                                      (128, 1040, 16384, "bf16"),
+                                      # row coding holding 12 chunks per thread (one workgroup per row)
+                                      (300, 20496, 264, "fp16")])
 def test_edge_shapes(M, K, N, dt):
     _banner(f"edge {M}x{K}x{N} {dt}")
     x, w = _case(M, K, N, dt, n_out=2, seed=M + K + N)
