@@ -101,10 +101,11 @@ def test_mid_size_batches_on_the_qkv_weight(M, capfd, monkeypatch):
     assert st["n_outliers"] >= len(cols)
 
 
-def test_repeated_products_on_one_workspace():
+@pytest.mark.parametrize("M,K,N", [(130, 4096, 9000),   # the row coding zeroes the counters
+                                   (64, 2048, 36864)])  # the slab X pass zeroes them
+def test_repeated_products_on_one_workspace(M, K, N):
     # the tile counters are left at zero by every call: the products run three times on one
     # prepared workspace and give the same bits each time
-    M, K, N = 130, 4096, 9000
     x, w = _case(M, K, N, "fp16", seed=11)
     Xd = x.cuda()
     Wq, s_w = lm.int8_quantize_weight(w.cuda())
