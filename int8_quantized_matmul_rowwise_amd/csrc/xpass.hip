@@ -677,17 +677,19 @@ __global__ __launch_bounds__(256) void code_slab_kernel(const uint16_t* __restri
     if ((int64_t)blockIdx.y < ny_wo) {
         // the W_O gather (tiled product): 64 rows of Wq per workgroup, O[t] found from the
         // bitmap (the coding workgroups write O meanwhile); workgroup 0 zeroes the counters
+        // (a very wide weight: each takes every nb-th group of 64 rows)
         extern __shared__ uint32_t dyn_lds[];
         __shared__ int32_t wsum[4];
-        const int64_t b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+        const int64_t b = (int64_t)blockIdx.y * gridDim.x + blockIdx.x, nb = ny_wo * (int64_t)gridDim.x;
         if (b == 0)
             for (int64_t i = tid; i < n_zero; i += 256) zero[i] = 0;
         if (b * 64 >= N) return;
         uint32_t* bits = dyn_lds;
         int32_t* wrank = (int32_t*)(dyn_lds + Kw);
         const int32_t nO = bitmap_ranks(bitmap, Kw, bits, wrank, wsum);
-        gather_wo_rows<DT>(b * 64, K, nO, [&](int32_t t) { return outlier_column(t, Kw, bits, wrank); }, Wq, N, WO,
-                           xo_pitch);
+        for (int64_t n0 = b * 64; n0 < N; n0 += nb * 64)
+            gather_wo_rows<DT>(n0, K, nO, [&](int32_t t) { return outlier_column(t, Kw, bits, wrank); }, Wq, N, WO,
+                               xo_pitch);
         return;
     }
     const int64_t ry = (int64_t)blockIdx.y - ny_wo;  // this workgroup's group of 4 rows
@@ -870,8 +872,11 @@ hipError_t launch_xpass_small(const XPassArgs& a, int32_t* O, int32_t* n_out, ui
     }
     int64_t gx = ceil_div(a.xq_pitch / 8, 64);
     gx = gx > 0 ? gx : 1;
-    // with_wo: rows of gather workgroups first (enough for ceil(N/64)), then the coding
-    const int64_t ny_wo = with_wo ? ceil_div(ceil_div(a.N, 64), gx) : 0;
+    // with_wo: rows of gather workgroups first (one per 64 weight rows, at most kMaxGatherRows
+    // rows of them: the grid's y extent is limited), then the coding
+    constexpr int64_t kMaxGatherRows = 4096;
+    int64_t ny_wo = with_wo ? ceil_div(ceil_div(a.N, 64), gx) : 0;
+    ny_wo = ny_wo < kMaxGatherRows ? ny_wo : kMaxGatherRows;
     const size_t lds = with_wo ? (size_t)ceil_div(a.K, 32) * 8 : 0;
     const dim3 g2((unsigned)gx, (unsigned)(ny_wo + ceil_div(a.M, 4)));
     if (a.dt == F16)

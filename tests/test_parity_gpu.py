@@ -89,7 +89,10 @@ def test_edge_shapes(M, K, N, dt):
 
 
 @pytest.mark.parametrize("M,K,N,n_out,dt", [(96, 2048, 20000, 40, "bf16"), (64, 1024, 65536, 300, "fp16"),
-                                             (112, 4112, 16400, 64, "fp16")])
+                                             (112, 4112, 16400, 64, "fp16"),
+                                             # more groups of 64 weight rows than gather workgroups:
+                                             # each takes every 4096th group
+                                             (16, 256, 300000, 40, "bf16")])
 def test_mid_batches_tiled_many_outliers(M, K, N, n_out, dt):
     # up to 112 rows on the tiled path (the slab X pass) with many outlier columns: the W_O
     # gather looks each column up by its rank in the bitmap (several per bitmap word, up to
