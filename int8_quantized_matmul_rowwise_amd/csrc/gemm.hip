@@ -504,20 +504,30 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(Params p) {
                         for (int j = 0; j < NJ; ++j) F[j] = mfma16<DT>(xa, wa[j], F[j]);
                     }
                 }
+                // the columns' factors, and the slice's row factors four at a time (one table
+                // read for both column tiles): read between the staging stores one by one,
+                // each would be read again and waited for before every element, since the
+                // compiler cannot tell the table from the staging area
+                float c[NJ], cf[NJ];
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
-                    const float c = csc[wn * (32 * NJ) + 32 * j + rl];
+                    c[j] = csc[wn * (32 * NJ) + 32 * j + rl];
                     // the outlier term's factor: c_n, or 1 (an exact product) when W_O holds
                     // 16-bit rows of W
-                    const float cf = p.f_scaled ? c : 1.0f;
+                    cf[j] = p.f_scaled ? c[j] : 1.0f;
+                }
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) {
-                        // row factors: four at a time from the table, for each column tile
-                        const float re = ((const v4f*)(rsc + rb + 8 * (e >> 2)))[0][e & 3];
-                        const float yi = __fmul_rn(__fmul_rn((float)acc[i][j][e], re), c);
-                        const float y = __fadd_rn(yi, __fmul_rn(cf, F[j][e]));
-                        ys[(8 * (e >> 2) + 4 * h + (e & 3)) * kYPitch + 32 * j + rl] = from_f32<DT>(y);
-                    }
+                for (int q = 0; q < 4; ++q) {
+                    const v4f rf = *(const v4f*)(rsc + rb + 8 * q);
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int e = 4 * q + r;
+                            const float yi = __fmul_rn(__fmul_rn((float)acc[i][j][e], rf[r]), c[j]);
+                            const float y = __fadd_rn(yi, __fmul_rn(cf[j], F[j][e]));
+                            ys[(8 * q + 4 * h + r) * kYPitch + 32 * j + rl] = from_f32<DT>(y);
+                        }
                 }
                 // all the prefetched outlier operands are in before the first stores (else
                 // the compiler's wait for a later slice's would also wait for the stores)
