@@ -597,13 +597,29 @@ def trace_summary(trace_dir: str, bench_json: str, wl, cmd: str, group: int = 0)
         lines += ["", f"bench line of the same run: step {line['ms_per_step'] * 1e3:.1f} us, {kernel} "
                   f"{ms * 1e3:.1f} us per launch inside the step (HIP events), value {line['value']:.1f} "
                   f"{line['unit']}, roofline achieved {roof['achieved']:.1f} {roof['unit']} (frac {roof['frac']:.4f})"]
+        # the timed steps' dispatches: the last `steps` of the product kernel in the per-dispatch
+        # trace (the warmup steps before them include the part's clock settling under load)
+        timed = None
+        traces = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True))
+        if traces:
+            with open(traces[0], newline="") as fh:
+                durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in csv.DictReader(fh)
+                        if f"::{kernel}<" in r["Kernel_Name"]]
+            if len(durs) >= line["steps"]:
+                timed = durs[-line["steps"]:]
+                lines.append(f"trace of {kernel}, the {len(durs)} dispatches in order (us): "
+                             + ", ".join(f"{d:.1f}" for d in durs))
         if avg_prod:
-            if roof["bound"] == "mfma":
-                frac = 2.0 * wl.M * wl.N * wl.K / (avg_prod * 1e-6) / 1e12 / roof["peak"]
-            else:
-                frac = algorithmic_bytes(wl, group) / (avg_prod * 1e-6) / 1e9 / roof["peak"]
-            lines.append(f"trace average of {kernel}: {avg_prod:.1f} us ({(avg_prod / (ms * 1e3) - 1) * 100:+.1f} % "
-                         f"vs the events): roofline frac from the trace {frac:.4f}")
+            def frac_of(us):
+                if roof["bound"] == "mfma":
+                    return 2.0 * wl.M * wl.N * wl.K / (us * 1e-6) / 1e12 / roof["peak"]
+                return algorithmic_bytes(wl, group) / (us * 1e-6) / 1e9 / roof["peak"]
+            lines.append(f"trace average of {kernel} over all its dispatches: {avg_prod:.1f} us "
+                         f"({(avg_prod / (ms * 1e3) - 1) * 100:+.1f} % vs the events): roofline frac {frac_of(avg_prod):.4f}")
+            if timed:
+                avg_t = sum(timed) / len(timed)
+                lines.append(f"trace average of {kernel} over the {len(timed)} timed steps' dispatches: {avg_t:.1f} us "
+                             f"({(avg_t / (ms * 1e3) - 1) * 100:+.1f} % vs the events): roofline frac {frac_of(avg_t):.4f}")
             if avg_prod < 0.95 * ms * 1e3:
                 lines.append("(the events bracket the product stage from the end of the X pass: under the profiler "
                              "the dispatch gap before the kernel, which lands inside that bracket, grows by a few "
