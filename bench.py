@@ -866,8 +866,9 @@ def vector_bench(args, wl) -> int:
     tops = ops / (ms_step * 1e-3) / 1e12
     roof = roofline(kernel, wl, wl.name, ms_gemm)
     roof["xpass_ms"] = ms_xpass
-    log(f"cold step {ms_step * 1e3:.1f} us = {tops:.0f} TOPS; {kernel} {ms_gemm * 1e3:.1f} us in the step = "
-        f"{roof['achieved']:.0f} {roof['unit']}; X pass {ms_xpass * 1e3:.1f} us; n_outliers {n_out}")
+    where, rest = ("back to back", "the rest of the step") if args.fixed else ("in the step", "X pass")
+    log(f"cold step {ms_step * 1e3:.1f} us = {tops:.0f} TOPS; {kernel} {ms_gemm * 1e3:.1f} us {where} = "
+        f"{roof['achieved']:.0f} {roof['unit']}; {rest} {ms_xpass * 1e3:.1f} us; n_outliers {n_out}")
 
     warm = None
     if not args.no_warm:
