@@ -598,7 +598,8 @@ def trace_summary(trace_dir: str, bench_json: str, wl, cmd: str, group: int = 0)
                   f"{ms * 1e3:.1f} us per launch inside the step (HIP events), value {line['value']:.1f} "
                   f"{line['unit']}, roofline achieved {roof['achieved']:.1f} {roof['unit']} (frac {roof['frac']:.4f})"]
         # the timed steps' dispatches: the last `steps` of the product kernel in the per-dispatch
-        # trace (the warmup steps before them include the part's clock settling under load)
+        # trace of a --no-warm run (the warmup steps before them include the part's clock
+        # settling under load; with warm steps the last dispatches would be theirs)
         timed = None
         traces = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True))
         if traces:
