@@ -906,6 +906,10 @@ def vector_bench(args, wl) -> int:
     if ceilings and roof["bound"] == "hbm" and ceilings.get("cold_read_gbs"):
         # the product kernel's byte rate against a plain read of the weight in the same state
         roof["frac_of_cold_read"] = roof["achieved"] / ceilings["cold_read_gbs"]
+    if ceilings and roof["bound"] == "mfma" and ceilings.get("i8_mfma_tops_random_operands"):
+        # the product kernel's rate against this part's own int8 MFMA rate on changing
+        # operands (its power limit), measured in the same run: boxes differ in that ceiling
+        roof["frac_of_random_operand_mfma"] = roof["achieved"] / ceilings["i8_mfma_tops_random_operands"]
 
     line = {
         "metric": "effective TOPS of int8 outlier-decomposed matmul; % i8 MFMA peak",
