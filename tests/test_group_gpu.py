@@ -154,3 +154,26 @@ def test_group_two_stage_calls_equal_the_one_call():
     Yb = lm.int8_matmul_group_products(300, 2048, Xd.dtype, 256, Wq2, s2, ws)
     assert torch.equal(Ya.view(torch.int16), lm.int8_matmul_group(Xd, Wq, s, 256).view(torch.int16))
     assert torch.equal(Yb.view(torch.int16), lm.int8_matmul_group(Xd, Wq2, s2, 256).view(torch.int16))
+
+
+def _group_draw(i):
+    # seeded: G a power of two in [128, 4096], K a multiple of it, ragged M and N (N % 8 = 0)
+    rng = np.random.default_rng(2000 + i)
+    while True:
+        G = int(2 ** rng.integers(7, 13))
+        K = G * int(rng.integers(1, max(2, 16384 // G) + 1))
+        M = int(rng.integers(1, 65)) if i % 2 == 0 else int(rng.integers(65, 600))
+        N = 8 * int(rng.integers(1, 400))
+        if M * N * K <= 3e9 and K <= 16384:
+            return M, K, N, G, ("fp16" if rng.integers(2) else "bf16"), int(rng.integers(0, 6))
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_group_seeded_shape_sweep(i):
+    """Seeded shapes over both group-wise product kernels (small batches on even draws),
+    Y compared bit for bit with the oracle."""
+    M, K, N, G, dt, n_out = _group_draw(i)
+    route = "small-batch" if lm.int8_matmul_group_small_batch(M, K, N, G) else "tiled"
+    print(f"\n[case] group sweep {i}: {M}x{K}x{N} G={G} {dt} injected={n_out} -> {route}", flush=True)
+    x, w = _case(M, K, N, dt, seed=100 + i, n_outliers=n_out)
+    _run(x, w, dt, G)
