@@ -103,3 +103,26 @@ def test_fixed_set_larger_than_one_launch_dimension():
     cols = np.arange(0, 65600, dtype=np.int32)
     print(f"\n[case] fixed {M}x{K}x{N} with {cols.size} outlier columns", flush=True)
     _run(x, w, cols, "fp16")
+
+
+def _fixed_draw(i):
+    # seeded: ragged M, K (% 16), N (% 8); a random ascending set of 0..80 columns, which need
+    # not hold the injected large columns (those are then quantized like any other)
+    rng = np.random.default_rng(3000 + i)
+    while True:
+        M = int(rng.integers(1, 129)) if i % 2 == 0 else int(rng.integers(129, 600))
+        K = 16 * int(rng.integers(1, 500))
+        N = 8 * int(rng.integers(1, 250))
+        if M * K * N <= 3e9:
+            break
+    O = np.sort(rng.choice(K, size=int(rng.integers(0, min(K, 80) + 1)), replace=False)).astype(np.int32)
+    return M, K, N, ("fp16" if rng.integers(2) else "bf16"), O
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_fixed_seeded_shape_sweep(i):
+    M, K, N, dt, O = _fixed_draw(i)
+    route = "small-batch" if lm.int8_matmul_workspace_layout(M, K, N)["small_batch"] else "tiled"
+    print(f"\n[case] fixed sweep {i}: {M}x{K}x{N} {dt} |O|={O.size} -> {route}", flush=True)
+    x, w, _ = _case(M, K, N, dt, seed=200 + i)
+    _run(x, w, O, dt)
